@@ -1,0 +1,151 @@
+"""CPU fp64 oracle for the attention forward (ctypes wrapper over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline leg
+are the only callers.  The product path (the HIP library and its binding) never imports
+this package, and this package imports nothing from the product path.
+
+All functions take and return float64 numpy arrays in a canonical layout:
+dense tensors (B, N, S, D), packed tensors (T, N, D), stats (B, N, S) or (N, T).
+Layout conversions are the caller's (they are views, not arithmetic).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MASKS = {"none": 0, "causal": 1, "band": 2}
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.oracle_attn.argtypes = [P] * 7 + [I64] * 6 + [D, I, I64, I64, I]
+    lib.oracle_attn_varlen.argtypes = [P] * 8 + [I64] * 6 + [D, I, I64, I64, I]
+    lib.oracle_merge.argtypes = [P] * 9 + [I64] * 4 + [I]
+    lib.oracle_sparse.argtypes = [P] * 8 + [I64] * 5 + [D, I]
+    for f in (lib.oracle_attn, lib.oracle_attn_varlen, lib.oracle_merge, lib.oracle_sparse):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _clamp_tokens(x: int) -> int:
+    # Positions are < 2**40 in any workload here; clamping keeps pre/next in int64
+    # without changing which keys are visible.
+    lim = 1 << 62
+    return int(max(-lim, min(lim, int(x))))
+
+
+def attn(q, k, v, scale: float, mask: str = "none", pre: int = 0, next: int = 0,
+         threads: int = 0, return_probs: bool = False):
+    """Dense attention.  q (B,Nq,Sq,D), k/v (B,Nkv,Skv,D) -> out (B,Nq,Sq,D),
+    softmax_max (B,Nq,Sq), softmax_sum (B,Nq,Sq) [, probs (B,Nq,Sq,Skv)]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, Sq, D = q.shape
+    Bk, Nkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty_like(q)
+    m = np.empty((B, Nq, Sq))
+    l = np.empty((B, Nq, Sq))
+    probs = np.empty((B, Nq, Sq, Skv)) if return_probs else None
+    rc = _load().oracle_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(m), _ptr(l),
+                             _ptr(probs) if probs is not None else None,
+                             B, Nq, Nkv, Sq, Skv, D, float(scale), MASKS[mask],
+                             _clamp_tokens(pre), _clamp_tokens(next), threads)
+    if rc != 0:
+        raise ValueError("oracle_attn: invalid arguments")
+    return (out, m, l, probs) if return_probs else (out, m, l)
+
+
+def attn_varlen(q, k, v, cu_q, cu_kv, scale: float, mask: str = "none", pre: int = 0,
+                next: int = 0, threads: int = 0):
+    """Packed attention.  q (Tq,Nq,D), k/v (Tkv,Nkv,D), cu_* END offsets (B,) ->
+    out (Tq,Nq,D), softmax_max (Nq,Tq), softmax_sum (Nq,Tq)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu_q = np.ascontiguousarray(cu_q, dtype=np.int64)
+    cu_kv = np.ascontiguousarray(cu_kv, dtype=np.int64)
+    Tq, Nq, D = q.shape
+    Tkv, Nkv, _ = k.shape
+    out = np.empty_like(q)
+    m = np.empty((Nq, Tq))
+    l = np.empty((Nq, Tq))
+    rc = _load().oracle_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(m), _ptr(l),
+                                    _ptr(cu_q), _ptr(cu_kv), len(cu_q), Tq, Tkv, Nq, Nkv, D,
+                                    float(scale), MASKS[mask], _clamp_tokens(pre),
+                                    _clamp_tokens(next), threads)
+    if rc != 0:
+        raise ValueError("oracle_attn_varlen: invalid arguments")
+    return out, m, l
+
+
+def merge(o1, m1, l1, o2, m2, l2, threads: int = 0):
+    """Merge two partials.  o* (B,N,S,D), m*/l* (B,N,S) -> out, softmax_max, softmax_sum."""
+    o1, o2 = _f64(o1), _f64(o2)
+    m1, l1, m2, l2 = _f64(m1), _f64(l1), _f64(m2), _f64(l2)
+    B, N, S, D = o1.shape
+    out = np.empty_like(o1)
+    mo = np.empty((B, N, S))
+    lo = np.empty((B, N, S))
+    rc = _load().oracle_merge(_ptr(o1), _ptr(m1), _ptr(l1), _ptr(o2), _ptr(m2), _ptr(l2),
+                              _ptr(out), _ptr(mo), _ptr(lo), B, N, S, D, threads)
+    if rc != 0:
+        raise ValueError("oracle_merge: invalid arguments")
+    return out, mo, lo
+
+
+def sparse(q, k, v, offset, columns, scale: float, threads: int = 0):
+    """CSR-sparse attention.  q/k/v (B,N,S,D), offset int32 (B,N,S+1), columns int32
+    (B,N,nnz) -> out (B,N,S,D), softmax_max (B,N,S), softmax_sum (B,N,S)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    offset = np.ascontiguousarray(offset, dtype=np.int32)
+    columns = np.ascontiguousarray(columns, dtype=np.int32)
+    B, N, S, D = q.shape
+    nnz = columns.shape[-1]
+    out = np.empty_like(q)
+    m = np.empty((B, N, S))
+    l = np.empty((B, N, S))
+    rc = _load().oracle_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(m), _ptr(l),
+                               _ptr(offset), _ptr(columns), nnz, B, N, S, D, float(scale),
+                               threads)
+    if rc != 0:
+        raise ValueError("oracle_sparse: invalid arguments")
+    return out, m, l
+
+
+def max_threads() -> int:
+    """Threads the oracle uses when threads=0 (the OpenMP default of this process)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
