@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X attention forward (one JSON line on stdout).
+
+A step is one attn_fwd_varlen call over the packed causal GQA workload: 16 sequences with
+seed-0 lengths (T = 33,064 tokens, longest 3,977), Nq 32, Nkv 8, head_dim 128, bf16 inputs,
+fp32 accumulation, causal per sequence, all inputs resident in HBM before timing.
+The metric counts 4 * D * Nq * (visible (query, key) pairs) flops per step.
+
+Also measured in the same run (reported under "secondary"):
+  * attn_lse_merge on the ring-merge workload (S 8192, N 32, D 128, SBH bf16), timed over
+    rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
+  * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, fp32, band 128 + 64 random).
+
+cpu_baseline: the CPU fp64 oracle (untuned) on a bounded sample of the same workload
+(all sequences, the first --cpu-heads query heads), timed on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_varlen_causal_gqa_t33064_pmc.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("fa_fwd_bf16.hip", "fa_common.h", "fa_params.h"):
+        with open(os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the
+    kernel source changed since they were taken."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per launch
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="query heads in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the metric kernel (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding across GPUs is design only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import scaled_dot_product_02_amd as mi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def up(arr, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    # ---------------- metric: packed causal GQA forward ----------------
+    name = synthetic.METRIC_WORKLOAD
+    w = synthetic.make(name)
+    Nq, Nkv, D, B, T = w["Nq"], w["Nkv"], w["D"], w["B"], w["Tq"]
+    lengths = [int(x) for x in w["lengths_q"]]
+    pairs = sum(L * (L + 1) // 2 for L in lengths)
+    flops = 4.0 * D * Nq * pairs
+    alg_bytes = 2 * (T * Nq * D * 2 + T * Nkv * D * 2) + 2 * 4 * Nq * T  # q,k,v,out + stats
+    q, k, v = up(w["q"], "bf16"), up(w["k"], "bf16"), up(w["v"], "bf16")
+    cu = torch.from_numpy(w["cu_q"]).to(dev)
+    out = torch.empty_like(q)
+    smax = torch.empty((Nq, T), dtype=torch.float32, device=dev)
+    ssum = torch.empty((Nq, T), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    maxlen = max(lengths)
+
+    def step():
+        mi.attn_fwd_varlen(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen, Nq, Nkv, D,
+                           "bf16", scale, "causal", 0, 0, stream.cuda_stream)
+
+    ms = time_launches(step, args.steps, args.warmup, stream)
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16 causal varlen GQA D=128) + % MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch_sequences": B, "total_tokens": T,
+                   "max_seqlen": maxlen, "nq": Nq, "nkv": Nkv, "head_dim": D, "mask": "causal",
+                   "layout": "TND", "visible_pairs_per_head": pairs, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes,
+                     "kernel": "fa_fwd_bf16_kernel<128>"},
+    }
+
+    # ---------------- secondary: merge and sparse ----------------
+    if not args.no_secondary:
+        sec = {}
+        S, N, Dm = 8192, 32, 128
+        rng = np.random.default_rng(0)
+        sets = []
+        for _ in range(4):
+            o1 = torch.randn((S, 1, N * Dm), device=dev).to(torch.bfloat16)
+            o2 = torch.randn((S, 1, N * Dm), device=dev).to(torch.bfloat16)
+            st = [torch.from_numpy(x).to(dev) for x in
+                  (rng.standard_normal((1, N, S), dtype=np.float32),
+                   rng.uniform(1, 100, (1, N, S)).astype(np.float32),
+                   rng.standard_normal((1, N, S), dtype=np.float32),
+                   rng.uniform(1, 100, (1, N, S)).astype(np.float32))]
+            res = [torch.empty_like(o1), torch.empty((1, N, S), device=dev),
+                   torch.empty((1, N, S), device=dev)]
+            sets.append((o1, st[0], st[1], o2, st[2], st[3], *res))
+        it = [0]
+
+        def merge_step():
+            s_ = sets[it[0] % len(sets)]
+            it[0] += 1
+            mi.attn_lse_merge(*s_, 1, N, S, Dm, "bf16", "SBH", stream.cuda_stream)
+
+        mms = time_launches(merge_step, 4 * 25, 8, stream)
+        mbytes = 3 * S * N * Dm * 2 + 6 * N * S * 4
+        mgbs = mbytes / (mms * 1e-3) / 1e9
+        sec["attn_lse_merge"] = {
+            "workload": "ring_merge_sbh_bf16_s8192_n32_d128", "us_per_launch": round(mms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(mgbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": mbytes, "rotating_sets": len(sets)}}
+        del sets
+
+        ws = synthetic.make("csr_sparse_f32_b2n8s4096d64")
+        sq, sk, sv = (up(ws[x], "f32") for x in ("q", "k", "v"))
+        so = torch.empty_like(sq)
+        soff = torch.from_numpy(ws["offset"]).to(dev)
+        scol = torch.from_numpy(ws["columns"]).to(dev)
+        sB, sN, sS, sD, nnz = ws["B"], ws["N"], ws["S"], ws["D"], ws["nnz"]
+
+        def sparse_step():
+            mi.sparse_csr_attn(sq, sk, sv, so, soff, scol, nnz, sB, sN, sS, sD, "f32",
+                               1 / math.sqrt(sD), stream.cuda_stream)
+
+        sms = time_launches(sparse_step, 20, 3, stream)
+        sflops = 4.0 * sB * sN * nnz * sD
+        sbytes = 4 * 4 * sB * sN * sS * sD + 4 * sB * sN * (nnz + sS + 1)
+        stf = sflops / (sms * 1e-3) / 1e12
+        sec["sparse_csr_attn"] = {
+            "workload": "csr_sparse_f32_b2n8s4096d64", "us_per_launch": round(sms * 1e3, 2),
+            "tflops": round(stf, 3), "gbs_algorithmic": round(sbytes / (sms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "alu", "achieved": round(stf, 3), "peak": PEAK_F32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(stf / PEAK_F32_TFLOPS, 4)}}
+        result["secondary"] = sec
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    if args.cpu_heads > 0:
+        import oracle
+        hs = min(args.cpu_heads, Nq)
+        G = Nq // Nkv
+        kvh = (hs + G - 1) // G
+        qs = synthetic.storage_values(w["q"][:, :hs], "bf16")
+        ks = synthetic.storage_values(w["k"][:, :kvh], "bf16")
+        vs = synthetic.storage_values(w["v"][:, :kvh], "bf16")
+        # keep the head -> kv-head map: kv head of query head h is h // G
+        if hs % G:
+            raise SystemExit("--cpu-heads must be a multiple of the GQA group")
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        oracle.attn_varlen(qs, ks, vs, w["cu_q"], w["cu_kv"], scale, "causal", threads=threads)
+        dt = time.perf_counter() - t0
+        sflops = 4.0 * D * hs * pairs
+        result["cpu_baseline"] = {
+            "value": round(sflops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"all {B} sequences x query heads 0..{hs - 1} of {Nq} "
+                      f"({sflops / 1e9:.1f} GFLOP fp64, {dt:.1f} s wall)"}
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * miattn.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention forward.
+ *
+ * The library computes  out = softmax(scale * Q K^T) V  FlashAttention-style: score tiles
+ * live in registers and the S x S score matrix never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named q, k, v, out, prev_*, cur_*, softmax_*, cu_seqlens_*, csr_* are DEVICE
+ *    pointers.  The caller owns every buffer; the library never allocates, frees or
+ *    synchronizes, and keeps no state between calls besides its loaded code objects.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.  Every call
+ *    only enqueues work on that stream and returns; results are ready when the stream is.
+ *  - Every host-checkable condition is validated before any HIP call; on failure nothing
+ *    is enqueued and a status other than MIATTN_OK is returned.  A failed launch returns
+ *    MIATTN_ERR_LAUNCH.  No exception crosses the ABI.
+ *  - Device-resident metadata (cumulative lengths, CSR offsets/columns) is a caller
+ *    contract: monotone non-decreasing, last entry = total rows, columns in [0, S).
+ *    Contents violating it give undefined results (the library cannot read device
+ *    memory without a synchronization).
+ *  - Outputs are fully overwritten.  Inputs must not alias outputs except where noted.
+ *  - Results are bitwise reproducible run to run: no atomics, fixed reduction orders
+ *    (the determinism the aclnnFlashAttentionVarLenScore constraints ask for by default).
+ *  - Element (b, n, s, d) of a 4-D tensor sits at:
+ *      BNSD: ((b*N + n)*S + s)*D + d          (batch, heads, seq, head_dim)
+ *      BSND: ((b*S + s)*N + n)*D + d
+ *      BSH : same memory as BSND with H = N*D
+ *      SBH : ((s*B + b)*N + n)*D + d          (H = N*D; head n owns columns n*D..n*D+D-1)
+ *  - Masks act on sequence-local positions i (query) and j (key), top-left aligned:
+ *      MIATTN_MASK_NONE   : every key is visible;
+ *      MIATTN_MASK_CAUSAL : j <= i;
+ *      MIATTN_MASK_BAND   : -pre_tokens <= j - i <= next_tokens  (pre/next signed; the band
+ *                           must be non-empty: pre_tokens + next_tokens >= 0, following the
+ *                           band rule in the aclnnFlashAttentionVarLenScore constraints).
+ *    Tiles that no visible pair touches are never loaded.
+ *  - Softmax statistics (fp32, optional, each may be NULL):
+ *      softmax_max[row] = max over visible keys of scale * q.k   (natural-log units);
+ *      softmax_sum[row] = sum over visible keys of exp(scale * q.k - softmax_max[row]).
+ *    A row with no visible key yields out = 0, softmax_max = -inf, softmax_sum = 0.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MIATTN_OK = 0,
+    MIATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    MIATTN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    MIATTN_ERR_DTYPE = 3,       /* unknown dtype, or one this entry point does not take */
+    MIATTN_ERR_LAYOUT = 4,      /* unknown layout */
+    MIATTN_ERR_GQA_RATIO = 5,   /* Nq is not a non-zero integer multiple of Nkv */
+    MIATTN_ERR_MASK = 6,        /* unknown mask, or an empty band (pre + next < 0) */
+    MIATTN_ERR_UNSUPPORTED = 7, /* valid per the operator spec but not built (e.g. head_dim) */
+    MIATTN_ERR_LAUNCH = 8,      /* the HIP launch failed */
+    MIATTN_ERR_SCALE = 9        /* scale is not a finite positive number */
+} miattn_status_t;
+
+typedef enum { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2 } miattn_dtype_t;
+typedef enum { MIATTN_BNSD = 0, MIATTN_BSND = 1, MIATTN_BSH = 2, MIATTN_SBH = 3 } miattn_layout_t;
+typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 2 } miattn_mask_t;
+
+/*
+ * attn_fwd - dense attention forward over a batch of equal-length sequences.
+ *
+ * Defines: out = softmax(scale * Q K^T) V per (batch, query head), the formula of the
+ * Paddle "sparse_attention" page and of manual_attention in the blog "高效 AI 模型开发：
+ * PyTorch torch.nn.attention 报错排查与高效替代方法"; the (batch, heads, seq, head_dim)
+ * layout that blog requires; GQA/MQA (query head h reads kv head h / (Nq/Nkv)) and the
+ * band mask from the aclnnFlashAttentionVarLenScore constraints.
+ *
+ *   q    [B, Nq,  Sq,  D] in `layout`;   k, v [B, Nkv, Skv, D] in `layout`;
+ *   out  [B, Nq,  Sq,  D] in `layout` (same dtype as q);
+ *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
+ *   dtype: MIATTN_BF16 (MFMA path, fp32 accumulation, RNE output) or MIATTN_F32.
+ *   D: 64 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
+ *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
+ *   scale: finite and > 0 (callers pass 1/sqrt(D)).
+ *   Pass pre_tokens/next_tokens for MIATTN_MASK_BAND; they are ignored otherwise.
+ *   Returns MIATTN_OK or an error status; nothing is enqueued on error.
+ */
+miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
+                         float* softmax_max, float* softmax_sum,
+                         int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                         miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                         miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                         void* stream);
+
+/*
+ * attn_fwd_varlen - attention forward over a packed batch of variable-length sequences.
+ *
+ * Defines: the TND packing and per-sequence computation of aclnnFlashAttentionVarLenScore
+ * (功能说明 and 约束说明): all sequences are stacked along T with no padding; sequence b
+ * owns query rows [cu_seqlens_q[b-1], cu_seqlens_q[b]) and key rows
+ * [cu_seqlens_kv[b-1], cu_seqlens_kv[b]) (cu[-1] = 0: the vectors are END offsets with no
+ * leading zero, so lengths [2,2,0,2,2] are passed as [2,4,4,6,8]); zero-length sequences
+ * are allowed; mask positions are local to each sequence.
+ *
+ *   q   [Tq,  Nq,  D];  k, v [Tkv, Nkv, D];  out [Tq, Nq, D]   (row-major, dtype `dtype`);
+ *   softmax_max, softmax_sum: fp32 [Nq, Tq] contiguous, or NULL;
+ *   cu_seqlens_q, cu_seqlens_kv: DEVICE int64 [B], monotone, last = Tq / Tkv;
+ *   max_seqlen_q, max_seqlen_kv: host upper bounds of the sequence lengths (the grid is
+ *   sized from max_seqlen_q; rows of a longer sequence are NOT computed).
+ *   Ranges: 1 <= B <= 2048, 1 <= Tq, Tkv <= 2^20, 1 <= Nq, Nkv <= 256, D in {64, 128}.
+ *   dtype, scale, mask, pre/next: as for attn_fwd.
+ */
+miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                float* softmax_max, float* softmax_sum,
+                                const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                int64_t B, int64_t Tq, int64_t Tkv,
+                                int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                int64_t Nq, int64_t Nkv, int64_t D,
+                                miattn_dtype_t dtype, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                void* stream);
+
+/*
+ * attn_lse_merge - merge two partial attention results of the same queries over disjoint
+ * key sets into one (the ring-attention update of "npu_ring_attention_update对外接口",
+ * equivalent small-operator logic): with m = max(prev_max, cur_max),
+ *   a = prev_sum * exp(prev_max - m),  c = cur_sum * exp(cur_max - m),  l = a + c,
+ *   out = prev_out * (a / l) + cur_out * (c / l),  out_max = m,  out_sum = l,
+ * computed in fp32 and rounded (RNE) to the output dtype.  If both partials are empty
+ * (m = -inf) the row becomes out = 0, out_max = -inf, out_sum = 0.
+ *
+ *   prev_out, cur_out, out: [B, N, S, D] in `layout`, dtype `dtype` (BF16, F32);
+ *   prev_max, prev_sum, cur_max, cur_sum, out_max, out_sum: fp32 [B, N, S] contiguous
+ *   (a packed TND batch is B = 1, S = T with layout BSND; its stats are then [N, T]).
+ *   out may alias prev_out or cur_out; out_max/out_sum may alias the matching input stats
+ *   (the update is elementwise and each element is read before it is written by the same
+ *   thread).  Any D >= 1.
+ */
+miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,
+                               const void* cur_out, const float* cur_max, const float* cur_sum,
+                               void* out, float* out_max, float* out_sum,
+                               int64_t B, int64_t N, int64_t S, int64_t D,
+                               miattn_dtype_t dtype, miattn_layout_t layout, void* stream);
+
+/*
+ * sparse_csr_attn - CSR-sparse attention (Paddle "sparse_attention": formula, parameters
+ * and code example): row i of slice (b, n) attends only to the key rows listed in
+ * csr_columns[b][n][csr_offset[b][n][i] .. csr_offset[b][n][i+1]) of the same slice,
+ * softmax(scale * q_i . k_c) over those entries, times v_c.  `csr_offset` is a row pointer
+ * (offset[0] = 0, offset[S] = entries used).  Every stored entry counts once (a repeated
+ * column counts as often as it is stored); an empty row gives 0.
+ *
+ *   q, k, v, out: fp32 [B, N, S, D] (BNSD) contiguous;
+ *   csr_offset: DEVICE int32 [B, N, S+1];  csr_columns: DEVICE int32 [B, N, nnz];
+ *   dtype: MIATTN_F32 only.  D in {64, 128}.  nnz >= 0.
+ */
+miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, void* out,
+                                const int32_t* csr_offset, const int32_t* csr_columns,
+                                int64_t nnz, int64_t B, int64_t N, int64_t S, int64_t D,
+                                miattn_dtype_t dtype, float scale, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* miattn_status_str(miattn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

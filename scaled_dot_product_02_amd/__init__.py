@@ -1,0 +1,114 @@
+"""Python binding of libmiattn (the MI355X attention-forward C ABI in include/miattn.h).
+
+Argument marshalling only: every function has the name and the positional arguments of
+the C entry point; pointer arguments accept torch tensors (their data_ptr()), plain
+integers or None; enum arguments accept the C values or their names ("bf16", "SBH",
+"causal").  `stream` defaults to torch's current HIP stream.  A non-OK status raises
+MiattnError.  All computation runs in the HIP kernels of libmiattn.so; there is no
+fallback: importing this package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmiattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m scaled_dot_product_02_amd.build` "
+        "(or __graft_entry__.build()); there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATTN_ERR_DTYPE",
+          4: "MIATTN_ERR_LAYOUT", 5: "MIATTN_ERR_GQA_RATIO", 6: "MIATTN_ERR_MASK",
+          7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE"}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
+MASKS = {"none": 0, "causal": 1, "band": 2}
+
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_lse_merge", "sparse_csr_attn", "miattn_status_str")
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+_P, _I64, _E, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+_lib.attn_fwd.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
+_lib.attn_fwd_varlen.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
+_lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
+_lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
+for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_lse_merge, _lib.sparse_csr_attn):
+    _f.restype = ctypes.c_int
+_lib.miattn_status_str.argtypes = [ctypes.c_int]
+_lib.miattn_status_str.restype = ctypes.c_char_p
+
+
+def status_str(status: int) -> str:
+    return _lib.miattn_status_str(int(status)).decode()
+
+
+def miattn_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _enum(x, table):
+    return table[x] if isinstance(x, str) else int(x)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise MiattnError(rc, where)
+
+
+def attn_fwd(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D,
+             dtype, layout, scale, mask, pre_tokens=0, next_tokens=0, stream=None):
+    _check(_lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                         _ptr(softmax_sum), B, Nq, Nkv, Sq, Skv, D, _enum(dtype, DTYPES),
+                         _enum(layout, LAYOUTS), scale, _enum(mask, MASKS), pre_tokens,
+                         next_tokens, _stream(stream)), "attn_fwd")
+
+
+def attn_fwd_varlen(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                    B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask,
+                    pre_tokens=0, next_tokens=0, stream=None):
+    _check(_lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                                _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+                                B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
+                                _enum(dtype, DTYPES), scale, _enum(mask, MASKS), pre_tokens,
+                                next_tokens, _stream(stream)), "attn_fwd_varlen")
+
+
+def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, out_max,
+                   out_sum, B, N, S, D, dtype, layout, stream=None):
+    _check(_lib.attn_lse_merge(_ptr(prev_out), _ptr(prev_max), _ptr(prev_sum), _ptr(cur_out),
+                               _ptr(cur_max), _ptr(cur_sum), _ptr(out), _ptr(out_max),
+                               _ptr(out_sum), B, N, S, D, _enum(dtype, DTYPES),
+                               _enum(layout, LAYOUTS), _stream(stream)), "attn_lse_merge")
+
+
+def sparse_csr_attn(q, k, v, out, csr_offset, csr_columns, nnz, B, N, S, D, dtype, scale,
+                    stream=None):
+    _check(_lib.sparse_csr_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(csr_offset),
+                                _ptr(csr_columns), nnz, B, N, S, D, _enum(dtype, DTYPES),
+                                scale, _stream(stream)), "sparse_csr_attn")

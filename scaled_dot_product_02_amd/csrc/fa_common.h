@@ -1,0 +1,62 @@
+// Device helpers shared by the attention-forward kernels (product path only).
+#pragma once
+#include "fa_params.h"
+
+namespace miattn {
+
+// Where a workgroup's tile lives.
+struct TileCoord {
+    int b, h, kvh;          // sequence, query head, kv head
+    int t;                  // q-tile index inside the sequence
+    int64_t q0, kv0;        // first packed row of the sequence (0 for dense batches)
+    int len_q, len_kv;      // sequence lengths
+    bool live;
+};
+
+// Decode the linear workgroup id.
+//
+// Work items are ordered (level, b, kv head, member of the GQA group), where level 0 holds
+// the LAST q tile of every sequence: under a causal mask later tiles see more keys, so the
+// heaviest tiles are dispatched first.  Workgroups are handed to the 8 XCDs round-robin
+// (id mod 8), so the `group` query heads that share one kv head are given ids congruent
+// mod 8: they run on the same XCD, back to back, and re-read that head's K/V tiles from
+// the XCD's own L2.
+__device__ inline TileCoord decode_tile(const FaParams& p, int L, int tile_m)
+{
+    TileCoord c;
+    const int G = p.group;
+    const int xcd = L & 7;
+    const int s = L >> 3;
+    const int gi = (s / G) * 8 + xcd;
+    const int g = s - (s / G) * G;
+    c.kvh = gi % p.Nkv;
+    const int rest = gi / p.Nkv;
+    c.b = rest % p.B;
+    const int level = rest / p.B;
+    c.live = level < p.n_levels;
+    c.h = c.kvh * G + g;
+    c.t = p.n_levels - 1 - level;
+    c.q0 = 0;
+    c.kv0 = 0;
+    c.len_q = p.Sq;
+    c.len_kv = p.Skv;
+    if (c.live && p.cu_q) {
+        c.q0 = c.b ? p.cu_q[c.b - 1] : 0;
+        c.kv0 = c.b ? p.cu_kv[c.b - 1] : 0;
+        c.len_q = (int)(p.cu_q[c.b] - c.q0);
+        c.len_kv = (int)(p.cu_kv[c.b] - c.kv0);
+    }
+    if (c.live && (int64_t)c.t * tile_m >= c.len_q) c.live = false;
+    return c;
+}
+
+// Visible key range [lo, hi) of query rows [r0, r1) under the band -pre <= j - i <= next.
+__device__ inline void key_range(const FaParams& p, int r0, int r1, int len_kv, int& lo, int& hi)
+{
+    int64_t a = (int64_t)r0 - p.pre;
+    int64_t z = (int64_t)(r1 - 1) + p.next + 1;
+    lo = a < 0 ? 0 : (a > len_kv ? len_kv : (int)a);
+    hi = z < 0 ? 0 : (z > len_kv ? len_kv : (int)z);
+}
+
+}  // namespace miattn

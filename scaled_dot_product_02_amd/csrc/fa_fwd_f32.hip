@@ -1,0 +1,122 @@
+// Attention forward for fp32 inputs (fp32 arithmetic on the vector ALUs).
+//
+// Same operation, batches, masks and statistics as the bf16 MFMA kernel; fp32 is the
+// slower path the SDPA-pitfalls blog describes for FlashAttention backends, and it is
+// kept exact to fp32 rounding rather than rounded through bf16.
+//
+// One workgroup = one wave = 64 query rows, one row per lane; K/V tiles of 32 keys are
+// staged in LDS and read as broadcasts.  Keys are consumed in chunks of 16 with one
+// online-softmax rescale per chunk.
+#include "fa_common.h"
+
+namespace miattn {
+namespace {
+
+constexpr int BM = kF32TileM;  // query rows per workgroup (one per lane)
+constexpr int BN = 32;         // keys per LDS tile
+constexpr int CH = 16;         // keys per softmax chunk
+
+template <int D>
+__global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
+{
+    __shared__ __attribute__((aligned(16))) float Ks[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+
+    const TileCoord tc = decode_tile(p, blockIdx.x, BM);
+    if (!tc.live) return;
+    const int lane = threadIdx.x;
+    const int i0 = tc.t * BM;
+    const int i1 = min(i0 + BM, tc.len_q);
+    const int qi = i0 + lane;
+
+    const float* qg = (const float*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
+    const float* kg = (const float*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
+    const float* vg = (const float*)p.v + (int64_t)tc.b * p.v_sb + tc.kv0 * p.v_ss + (int64_t)tc.kvh * p.v_sh;
+    float* og = (float*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
+    const int64_t st_base = (int64_t)tc.b * p.st_sb + (int64_t)tc.h * p.st_sh + tc.q0;
+
+    int kv_lo, kv_hi;
+    key_range(p, i0, i1, tc.len_kv, kv_lo, kv_hi);
+
+    float q[D], o[D];
+    #pragma unroll
+    for (int d = 0; d < D; d += 4) {
+        float4 x = qi < tc.len_q ? *(const float4*)(qg + (int64_t)qi * p.q_ss + d) : float4{0, 0, 0, 0};
+        q[d] = x.x; q[d + 1] = x.y; q[d + 2] = x.z; q[d + 3] = x.w;
+        o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int j0 = (kv_lo / BN) * BN; j0 < kv_hi; j0 += BN) {
+        __syncthreads();
+        for (int c = lane; c < BN * D / 4; c += 64) {
+            const int row = c / (D / 4), col = 4 * (c % (D / 4));
+            float4 kx{0, 0, 0, 0}, vx{0, 0, 0, 0};
+            if (j0 + row < tc.len_kv) {
+                kx = *(const float4*)(kg + (int64_t)(j0 + row) * p.k_ss + col);
+                vx = *(const float4*)(vg + (int64_t)(j0 + row) * p.v_ss + col);
+            }
+            *(float4*)(Ks + row * D + col) = kx;
+            *(float4*)(Vs + row * D + col) = vx;
+        }
+        __syncthreads();
+
+        for (int c0 = 0; c0 < BN; c0 += CH) {
+            float s[CH];
+            float mx = -INFINITY;
+            #pragma unroll
+            for (int jj = 0; jj < CH; ++jj) {
+                const float* kr = Ks + (c0 + jj) * D;
+                float acc = 0.f;
+                #pragma unroll
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], kr[d], acc);
+                const int j = j0 + c0 + jj;
+                const int64_t dj = (int64_t)j - qi;
+                const bool vis = j < tc.len_kv && dj <= p.next && -dj <= p.pre;
+                s[jj] = vis ? acc * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, s[jj]);
+            }
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
+            #pragma unroll
+            for (int d = 0; d < D; ++d) o[d] *= alpha;
+            #pragma unroll
+            for (int jj = 0; jj < CH; ++jj) {
+                const float e = __builtin_amdgcn_exp2f(s[jj] - m_use);
+                l_run += e;
+                const float* vr = Vs + (c0 + jj) * D;
+                #pragma unroll
+                for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(e, vr[d], o[d]);
+            }
+            m_run = m_new;
+        }
+    }
+
+    if (qi < i1) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float* orow = og + (int64_t)qi * p.o_ss;
+        #pragma unroll
+        for (int d = 0; d < D; d += 4)
+            *(float4*)(orow + d) = float4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+        if (p.smax) p.smax[st_base + qi] = l_run > 0.f ? m_run * 0.69314718055994530942f : -INFINITY;
+        if (p.ssum) p.ssum[st_base + qi] = l_run;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream)
+{
+    dim3 grid(p.n_slots), block(64);
+    if (D == 64)
+        hipLaunchKernelGGL(fa_fwd_f32_kernel<64>, grid, block, 0, stream, p);
+    else if (D == 128)
+        hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace miattn

@@ -1,0 +1,70 @@
+// Internal launch parameters shared by the C-ABI layer and the kernels (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+// One attention forward launch.  Dense batches use stride_b and implicit sequence
+// starts of 0; packed (TND) batches read the sequence bounds from cu_q / cu_kv
+// (END offsets, no leading zero) and use stride_b = 0.
+struct FaParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* smax;            // may be null
+    float* ssum;            // may be null
+    const int64_t* cu_q;    // null for dense batches
+    const int64_t* cu_kv;
+    int64_t q_sb, q_ss, q_sh;   // element strides: batch, sequence position, head
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_ss, o_sh;
+    int64_t st_sb, st_sh;       // stats element index = b*st_sb + h*st_sh + (seq start + i)
+    int32_t B, Nq, Nkv, group;  // group = Nq / Nkv
+    int32_t Sq, Skv;            // dense: lengths; packed: upper bounds (max_seqlen)
+    int32_t n_levels;           // q tiles per sequence at the longest length
+    int32_t n_slots;            // workgroups in the grid (multiple of 8 * group)
+    int64_t pre, next;          // visible band: -pre <= j - i <= next (clamped)
+    float scale;                // softmax scale
+    float scale_log2;           // scale * log2(e)
+};
+
+struct MergeParams {
+    const void* o1;
+    const float* m1;
+    const float* l1;
+    const void* o2;
+    const float* m2;
+    const float* l2;
+    void* out;
+    float* mo;
+    float* lo;
+    int64_t sb, sh, ss;         // element strides of the outputs (head_dim contiguous)
+    int32_t B, N, S, D;
+};
+
+struct SparseParams {
+    const float* q;
+    const float* k;
+    const float* v;
+    float* out;
+    const int32_t* offset;
+    const int32_t* columns;
+    int64_t nnz;
+    int32_t B, N, S;
+    float scale_log2;
+};
+
+// Launchers (defined next to their kernels).  Each returns the launch status.
+hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, hipStream_t stream);
+hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_sparse_csr(const SparseParams& p, int D, hipStream_t stream);
+
+// Row tile heights, used by the C-ABI layer to size the grids.
+constexpr int kBf16TileM = 128;
+constexpr int kF32TileM = 64;
+
+}  // namespace miattn

@@ -1,0 +1,145 @@
+// Merge of two partial attention results (ring-attention update).
+//
+// For each (b, n, s), in the order of "npu_ring_attention_update对外接口" (equivalent
+// small-operator logic): m = max(m1, m2); a = l1 exp(m1 - m); c = l2 exp(m2 - m);
+// l = a + c; out = o1 (a/l) + o2 (c/l); statistics (m, l) are written out, and the
+// output is rounded (RNE) to its storage type.  Both partials empty (m = -inf) gives
+// (0, -inf, 0).
+//
+// HBM-bound elementwise work.  One workgroup takes SB = 16 consecutive positions s of one
+// batch entry b for all heads: it first reads the 4 statistics of those N x 16 rows
+// (16 consecutive floats per head, coalesced), forms the two weights per row in LDS and
+// writes the merged statistics, then streams the outputs in 16-byte vectors (8 bf16 or
+// 4 fp32) with no further global reads of the statistics.
+#include "fa_params.h"
+
+namespace miattn {
+namespace {
+
+constexpr int SB = 16;     // positions per workgroup
+constexpr int NT = 256;    // threads per workgroup
+constexpr int NMAX = 256;  // largest head count
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Vec;
+template <> struct Vec<__bf16> { static constexpr int W = 8; };
+template <> struct Vec<float> { static constexpr int W = 4; };
+
+__device__ inline void unpack(const u32x4& x, float* f, __bf16*)
+{
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(x[e] << 16);
+        f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+    }
+}
+__device__ inline void unpack(const u32x4& x, float* f, float*)
+{
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(x[e]);
+}
+__device__ inline u32x4 pack(const float* f, __bf16*)
+{
+    u32x4 r;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 a = (__bf16)f[2 * e], b = (__bf16)f[2 * e + 1];
+        r[e] = (unsigned)__builtin_bit_cast(unsigned short, a) |
+               ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    }
+    return r;
+}
+__device__ inline u32x4 pack(const float* f, float*)
+{
+    u32x4 r;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(f[e]);
+    return r;
+}
+
+// VEC = true: 16-byte vectors (D a multiple of the vector width, aligned pointers and
+// strides); VEC = false: one element per thread step, any D.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(NT) void lse_merge_kernel(MergeParams p)
+{
+    __shared__ float w1s[NMAX * SB];
+    __shared__ float w2s[NMAX * SB];
+    const int s0 = blockIdx.x * SB;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int nrow = min(SB, p.S - s0);
+
+    // weights and merged statistics of the N x SB rows
+    for (int e = tid; e < p.N * SB; e += NT) {
+        const int n = e / SB, ds = e % SB;
+        if (ds >= nrow) continue;
+        const int64_t idx = ((int64_t)b * p.N + n) * p.S + s0 + ds;
+        const float m1 = p.m1[idx], l1 = p.l1[idx], m2 = p.m2[idx], l2 = p.l2[idx];
+        const float m = fmaxf(m1, m2);
+        float w1 = 0.f, w2 = 0.f, l = 0.f;
+        if (m != -INFINITY) {
+            const float a = l1 * expf(m1 - m);
+            const float c = l2 * expf(m2 - m);
+            l = a + c;
+            w1 = a / l;
+            w2 = c / l;
+        }
+        w1s[e] = w1;
+        w2s[e] = w2;
+        p.mo[idx] = m;
+        p.lo[idx] = l;
+    }
+    __syncthreads();
+
+    const int W = VEC ? Vec<T>::W : 1;
+    const int per_row = p.N * p.D / W;   // vectors (or elements) per position
+    for (int ds = 0; ds < nrow; ++ds) {
+        const int64_t rbase = (int64_t)b * p.sb + (int64_t)(s0 + ds) * p.ss;
+        for (int c = tid; c < per_row; c += NT) {
+            const int n = (c * W) / p.D;
+            const int d = (c * W) - n * p.D;
+            const int64_t off = rbase + (int64_t)n * p.sh + d;
+            const float w1 = w1s[n * SB + ds], w2 = w2s[n * SB + ds];
+            if constexpr (VEC) {
+                float x1[Vec<T>::W], x2[Vec<T>::W], y[Vec<T>::W];
+                unpack(*(const u32x4*)((const T*)p.o1 + off), x1, (T*)nullptr);
+                unpack(*(const u32x4*)((const T*)p.o2 + off), x2, (T*)nullptr);
+                #pragma unroll
+                for (int e = 0; e < Vec<T>::W; ++e) y[e] = __builtin_fmaf(x1[e], w1, x2[e] * w2);
+                *(u32x4*)((T*)p.out + off) = pack(y, (T*)nullptr);
+            } else {
+                const float x1 = (float)((const T*)p.o1)[off];
+                const float x2 = (float)((const T*)p.o2)[off];
+                ((T*)p.out)[off] = (T)__builtin_fmaf(x1, w1, x2 * w2);
+            }
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_t(const MergeParams& p, hipStream_t stream)
+{
+    constexpr int W = Vec<T>::W;
+    const bool vec = p.D % W == 0 && p.sb % W == 0 && p.sh % W == 0 && p.ss % W == 0 &&
+                     ((uintptr_t)p.o1 % 16 == 0) && ((uintptr_t)p.o2 % 16 == 0) &&
+                     ((uintptr_t)p.out % 16 == 0);
+    dim3 grid((p.S + SB - 1) / SB, p.B), block(NT);
+    if (vec)
+        hipLaunchKernelGGL((lse_merge_kernel<T, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((lse_merge_kernel<T, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// dtype: 0 = fp32, 1 = bf16 (the C-ABI enum values)
+hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream)
+{
+    if (dtype == 1) return launch_t<__bf16>(p, stream);
+    if (dtype == 0) return launch_t<float>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace miattn

@@ -1,0 +1,224 @@
+// C ABI of the attention-forward library: argument validation, layout strides, grid
+// sizing and launches on the caller's stream.  Declared in include/miattn.h.
+#include <math.h>
+
+#include "../../include/miattn.h"
+#include "fa_params.h"
+
+using namespace miattn;
+
+namespace {
+
+constexpr int64_t kTokensClamp = int64_t(1) << 40;  // |pre|, |next| beyond this change nothing
+
+struct Strides { int64_t sb, ss, sh; };
+
+bool layout_ok(int layout) { return layout >= MIATTN_BNSD && layout <= MIATTN_SBH; }
+
+Strides strides_of(int layout, int64_t B, int64_t N, int64_t S, int64_t D)
+{
+    switch (layout) {
+    case MIATTN_BNSD: return {N * S * D, D, S * D};
+    case MIATTN_BSND:
+    case MIATTN_BSH: return {S * N * D, N * D, D};
+    default: /* SBH */ return {N * D, B * N * D, D};
+    }
+}
+
+miattn_status_t check_mask(int mask, int64_t pre, int64_t next, int64_t& pre_c, int64_t& next_c)
+{
+    auto clamp = [](int64_t x) { return x > kTokensClamp ? kTokensClamp : (x < -kTokensClamp ? -kTokensClamp : x); };
+    if (mask == MIATTN_MASK_NONE) {
+        pre_c = next_c = kTokensClamp;
+    } else if (mask == MIATTN_MASK_CAUSAL) {
+        pre_c = kTokensClamp;
+        next_c = 0;
+    } else if (mask == MIATTN_MASK_BAND) {
+        // the band must be non-empty: pre + next >= 0 (evaluated without overflow)
+        if ((__int128)pre + (__int128)next < 0) return MIATTN_ERR_MASK;
+        pre_c = clamp(pre);
+        next_c = clamp(next);
+    } else {
+        return MIATTN_ERR_MASK;
+    }
+    return MIATTN_OK;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+miattn_status_t check_dtype_fa(int dtype)
+{
+    if (dtype == MIATTN_F32 || dtype == MIATTN_BF16) return MIATTN_OK;
+    if (dtype == MIATTN_F16) return MIATTN_ERR_UNSUPPORTED;
+    return MIATTN_ERR_DTYPE;
+}
+
+// Grid of the attention kernels: levels x batch x kv heads groups, padded to a
+// multiple of 8 groups, times the GQA group size.
+miattn_status_t size_grid(FaParams& p, int64_t max_len_q, int tile_m)
+{
+    const int64_t levels = (max_len_q + tile_m - 1) / tile_m;
+    const int64_t groups = levels * p.B * p.Nkv;
+    const int64_t slots = ((groups + 7) / 8) * 8 * p.group;
+    if (slots >= (int64_t(1) << 31)) return MIATTN_ERR_UNSUPPORTED;
+    p.n_levels = (int32_t)levels;
+    p.n_slots = (int32_t)slots;
+    return MIATTN_OK;
+}
+
+miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
+{
+    const int tile_m = dtype == MIATTN_BF16 ? kBf16TileM : kF32TileM;
+    miattn_status_t st = size_grid(p, max_len_q, tile_m);
+    if (st != MIATTN_OK) return st;
+    hipError_t e = dtype == MIATTN_BF16 ? launch_fa_fwd_bf16(p, (int)D, stream)
+                                        : launch_fa_fwd_f32(p, (int)D, stream);
+    return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* miattn_status_str(miattn_status_t s)
+{
+    switch (s) {
+    case MIATTN_OK: return "ok";
+    case MIATTN_ERR_NULL: return "a required pointer is null";
+    case MIATTN_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MIATTN_ERR_DTYPE: return "unknown or unsupported dtype for this entry point";
+    case MIATTN_ERR_LAYOUT: return "unknown layout";
+    case MIATTN_ERR_GQA_RATIO: return "Nq must be a non-zero integer multiple of Nkv";
+    case MIATTN_ERR_MASK: return "unknown mask or empty band (pre_tokens + next_tokens < 0)";
+    case MIATTN_ERR_UNSUPPORTED: return "valid but not built (head_dim, dtype or grid size)";
+    case MIATTN_ERR_LAUNCH: return "kernel launch failed";
+    case MIATTN_ERR_SCALE: return "scale must be finite and positive";
+    }
+    return "unknown status";
+}
+
+miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
+                         float* softmax_max, float* softmax_sum,
+                         int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                         miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                         miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+{
+    if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
+    miattn_status_t st = check_dtype_fa(dtype);
+    if (st == MIATTN_ERR_DTYPE) return st;
+    if (!layout_ok(layout)) return MIATTN_ERR_LAYOUT;
+    if (B < 1 || Nq < 1 || Nkv < 1 || Sq < 1 || Skv < 1 || D < 1) return MIATTN_ERR_SHAPE;
+    if (Nq > 256 || Nkv > 256 || D > 768) return MIATTN_ERR_SHAPE;
+    if (B * Sq > (int64_t(1) << 31) || B * Skv > (int64_t(1) << 31)) return MIATTN_ERR_SHAPE;
+    if (Nq % Nkv != 0) return MIATTN_ERR_GQA_RATIO;
+    FaParams p{};
+    st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
+    if (st != MIATTN_OK) return st;
+    if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
+    if (check_dtype_fa(dtype) != MIATTN_OK) return MIATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+
+    const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.smax = softmax_max; p.ssum = softmax_sum;
+    p.cu_q = p.cu_kv = nullptr;
+    p.q_sb = sq.sb; p.q_ss = sq.ss; p.q_sh = sq.sh;
+    p.o_sb = sq.sb; p.o_ss = sq.ss; p.o_sh = sq.sh;
+    p.k_sb = skv.sb; p.k_ss = skv.ss; p.k_sh = skv.sh;
+    p.v_sb = skv.sb; p.v_ss = skv.ss; p.v_sh = skv.sh;
+    p.st_sb = Nq * Sq; p.st_sh = Sq;
+    p.B = (int32_t)B; p.Nq = (int32_t)Nq; p.Nkv = (int32_t)Nkv; p.group = (int32_t)(Nq / Nkv);
+    p.Sq = (int32_t)Sq; p.Skv = (int32_t)Skv;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launch_fa(p, dtype, D, (hipStream_t)stream, Sq);
+}
+
+miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                float* softmax_max, float* softmax_sum,
+                                const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                int64_t B, int64_t Tq, int64_t Tkv,
+                                int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                int64_t Nq, int64_t Nkv, int64_t D,
+                                miattn_dtype_t dtype, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+{
+    if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_kv) return MIATTN_ERR_NULL;
+    miattn_status_t st = check_dtype_fa(dtype);
+    if (st == MIATTN_ERR_DTYPE) return st;
+    if (B < 1 || B > 2048) return MIATTN_ERR_SHAPE;
+    if (Tq < 1 || Tkv < 1 || Tq > (int64_t(1) << 20) || Tkv > (int64_t(1) << 20)) return MIATTN_ERR_SHAPE;
+    if (max_seqlen_q < 1 || max_seqlen_q > Tq || max_seqlen_kv < 1 || max_seqlen_kv > Tkv)
+        return MIATTN_ERR_SHAPE;
+    if (Nq < 1 || Nkv < 1 || Nq > 256 || Nkv > 256 || D < 1 || D > 768) return MIATTN_ERR_SHAPE;
+    if (Nq % Nkv != 0) return MIATTN_ERR_GQA_RATIO;
+    FaParams p{};
+    st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
+    if (st != MIATTN_OK) return st;
+    if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
+    if (check_dtype_fa(dtype) != MIATTN_OK) return MIATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.smax = softmax_max; p.ssum = softmax_sum;
+    p.cu_q = cu_seqlens_q; p.cu_kv = cu_seqlens_kv;
+    p.q_sb = 0; p.q_ss = Nq * D; p.q_sh = D;
+    p.o_sb = 0; p.o_ss = Nq * D; p.o_sh = D;
+    p.k_sb = 0; p.k_ss = Nkv * D; p.k_sh = D;
+    p.v_sb = 0; p.v_ss = Nkv * D; p.v_sh = D;
+    p.st_sb = 0; p.st_sh = Tq;
+    p.B = (int32_t)B; p.Nq = (int32_t)Nq; p.Nkv = (int32_t)Nkv; p.group = (int32_t)(Nq / Nkv);
+    p.Sq = (int32_t)max_seqlen_q; p.Skv = (int32_t)max_seqlen_kv;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launch_fa(p, dtype, D, (hipStream_t)stream, max_seqlen_q);
+}
+
+miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,
+                               const void* cur_out, const float* cur_max, const float* cur_sum,
+                               void* out, float* out_max, float* out_sum,
+                               int64_t B, int64_t N, int64_t S, int64_t D,
+                               miattn_dtype_t dtype, miattn_layout_t layout, void* stream)
+{
+    if (!prev_out || !prev_max || !prev_sum || !cur_out || !cur_max || !cur_sum || !out ||
+        !out_max || !out_sum)
+        return MIATTN_ERR_NULL;
+    if (dtype != MIATTN_F32 && dtype != MIATTN_BF16)
+        return dtype == MIATTN_F16 ? MIATTN_ERR_UNSUPPORTED : MIATTN_ERR_DTYPE;
+    if (!layout_ok(layout)) return MIATTN_ERR_LAYOUT;
+    if (B < 1 || N < 1 || S < 1 || D < 1 || N > 256 || B > 65535) return MIATTN_ERR_SHAPE;
+    if (B * N * S * D > (int64_t(1) << 40) || S > (int64_t(1) << 30) || N * D > (int64_t(1) << 30))
+        return MIATTN_ERR_SHAPE;
+    const Strides s = strides_of(layout, B, N, S, D);
+    MergeParams p{};
+    p.o1 = prev_out; p.m1 = prev_max; p.l1 = prev_sum;
+    p.o2 = cur_out; p.m2 = cur_max; p.l2 = cur_sum;
+    p.out = out; p.mo = out_max; p.lo = out_sum;
+    p.sb = s.sb; p.ss = s.ss; p.sh = s.sh;
+    p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S; p.D = (int32_t)D;
+    return launch_lse_merge(p, dtype, (hipStream_t)stream) == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
+}
+
+miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, void* out,
+                                const int32_t* csr_offset, const int32_t* csr_columns,
+                                int64_t nnz, int64_t B, int64_t N, int64_t S, int64_t D,
+                                miattn_dtype_t dtype, float scale, void* stream)
+{
+    if (!q || !k || !v || !out || !csr_offset) return MIATTN_ERR_NULL;
+    if (nnz > 0 && !csr_columns) return MIATTN_ERR_NULL;
+    if (dtype != MIATTN_F32)
+        return (dtype == MIATTN_BF16 || dtype == MIATTN_F16) ? MIATTN_ERR_UNSUPPORTED : MIATTN_ERR_DTYPE;
+    if (B < 1 || N < 1 || S < 1 || D < 1 || nnz < 0 || D > 768) return MIATTN_ERR_SHAPE;
+    if (S >= (int64_t(1) << 31) - 1 || nnz >= (int64_t(1) << 31) || B * N * S >= (int64_t(1) << 33))
+        return MIATTN_ERR_SHAPE;
+    if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
+    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+    SparseParams p{};
+    p.q = (const float*)q; p.k = (const float*)k; p.v = (const float*)v; p.out = (float*)out;
+    p.offset = csr_offset; p.columns = csr_columns; p.nnz = nnz;
+    p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launch_sparse_csr(p, (int)D, (hipStream_t)stream) == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/miattn.h
+declares, and rejects every invalid argument with the documented status before any HIP
+call (so none of these tests touches a GPU)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+LIB = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmiattn.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("attn_fwd", "attn_fwd_varlen", "attn_lse_merge", "sparse_csr_attn",
+                 "miattn_status_str"):
+        assert name in d, d
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+
+
+@pytest.fixture(scope="module")
+def mi():
+    import scaled_dot_product_02_amd as m
+    return m
+
+
+P = 256  # a fake, never-dereferenced device address: every call below fails validation
+
+
+def _fwd(mi, **kw):
+    a = dict(q=P, k=P, v=P, out=P, m=None, l=None, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64,
+             dtype="bf16", layout="BNSD", scale=0.125, mask="none", pre=0, nxt=0)
+    a.update(kw)
+    with pytest.raises(mi.MiattnError) as e:
+        mi.attn_fwd(a["q"], a["k"], a["v"], a["out"], a["m"], a["l"], a["B"], a["Nq"], a["Nkv"],
+                    a["Sq"], a["Skv"], a["D"], a["dtype"], a["layout"], a["scale"], a["mask"],
+                    a["pre"], a["nxt"], stream=0)
+    return mi.STATUS[e.value.status]
+
+
+def test_attn_fwd_validation(mi):
+    assert _fwd(mi, q=None) == "MIATTN_ERR_NULL"
+    assert _fwd(mi, out=None) == "MIATTN_ERR_NULL"
+    assert _fwd(mi, dtype=9) == "MIATTN_ERR_DTYPE"
+    assert _fwd(mi, dtype="f16") == "MIATTN_ERR_UNSUPPORTED"
+    assert _fwd(mi, layout=7) == "MIATTN_ERR_LAYOUT"
+    assert _fwd(mi, B=0) == "MIATTN_ERR_SHAPE"
+    assert _fwd(mi, Sq=0) == "MIATTN_ERR_SHAPE"
+    assert _fwd(mi, Skv=-3) == "MIATTN_ERR_SHAPE"
+    assert _fwd(mi, Nq=257, Nkv=1) == "MIATTN_ERR_SHAPE"        # N in 1..256
+    assert _fwd(mi, D=769) == "MIATTN_ERR_SHAPE"                # D in 1..768
+    assert _fwd(mi, Nq=6, Nkv=4) == "MIATTN_ERR_GQA_RATIO"      # Nq / Nkv not an integer
+    assert _fwd(mi, Nq=2, Nkv=4) == "MIATTN_ERR_GQA_RATIO"
+    assert _fwd(mi, mask=5) == "MIATTN_ERR_MASK"
+    assert _fwd(mi, mask="band", pre=3, nxt=-4) == "MIATTN_ERR_MASK"   # empty band
+    assert _fwd(mi, mask="band", pre=-(1 << 63), nxt=-(1 << 62)) == "MIATTN_ERR_MASK"
+    assert _fwd(mi, scale=0.0) == "MIATTN_ERR_SCALE"
+    assert _fwd(mi, scale=-0.1) == "MIATTN_ERR_SCALE"
+    assert _fwd(mi, scale=float("nan")) == "MIATTN_ERR_SCALE"
+    assert _fwd(mi, scale=float("inf")) == "MIATTN_ERR_SCALE"
+    assert _fwd(mi, D=96) == "MIATTN_ERR_UNSUPPORTED"           # in spec, not built
+    assert _fwd(mi, D=1) == "MIATTN_ERR_UNSUPPORTED"
+
+
+def _varlen(mi, **kw):
+    a = dict(q=P, k=P, v=P, out=P, cq=P, ck=P, B=3, Tq=100, Tkv=100, mq=50, mk=50, Nq=8, Nkv=2,
+             D=128, dtype="bf16", scale=0.1, mask="causal", pre=0, nxt=0)
+    a.update(kw)
+    with pytest.raises(mi.MiattnError) as e:
+        mi.attn_fwd_varlen(a["q"], a["k"], a["v"], a["out"], None, None, a["cq"], a["ck"], a["B"],
+                           a["Tq"], a["Tkv"], a["mq"], a["mk"], a["Nq"], a["Nkv"], a["D"],
+                           a["dtype"], a["scale"], a["mask"], a["pre"], a["nxt"], stream=0)
+    return mi.STATUS[e.value.status]
+
+
+def test_attn_fwd_varlen_validation(mi):
+    assert _varlen(mi, cq=None) == "MIATTN_ERR_NULL"
+    assert _varlen(mi, ck=None) == "MIATTN_ERR_NULL"
+    assert _varlen(mi, B=0) == "MIATTN_ERR_SHAPE"
+    assert _varlen(mi, B=2049) == "MIATTN_ERR_SHAPE"              # cumulative-length vector 1..2K
+    assert _varlen(mi, Tq=0) == "MIATTN_ERR_SHAPE"
+    assert _varlen(mi, Tkv=(1 << 20) + 1) == "MIATTN_ERR_SHAPE"   # T in 1..1M
+    assert _varlen(mi, mq=0) == "MIATTN_ERR_SHAPE"
+    assert _varlen(mi, mq=101) == "MIATTN_ERR_SHAPE"              # longer than T
+    assert _varlen(mi, Nq=8, Nkv=3) == "MIATTN_ERR_GQA_RATIO"
+    assert _varlen(mi, mask="band", pre=-5, nxt=4) == "MIATTN_ERR_MASK"
+    assert _varlen(mi, scale=0.0) == "MIATTN_ERR_SCALE"
+    assert _varlen(mi, D=32) == "MIATTN_ERR_UNSUPPORTED"
+    assert _varlen(mi, dtype=3) == "MIATTN_ERR_DTYPE"
+
+
+def test_attn_lse_merge_validation(mi):
+    def call(**kw):
+        a = dict(p=P, B=1, N=4, S=8, D=16, dtype="bf16", layout="SBH")
+        a.update(kw)
+        ptrs = [a["p"]] * 9
+        if "null" in kw:
+            ptrs[kw["null"]] = None
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_lse_merge(*ptrs, a["B"], a["N"], a["S"], a["D"], a["dtype"], a["layout"], stream=0)
+        return mi.STATUS[e.value.status]
+    for i in range(9):
+        assert call(null=i) == "MIATTN_ERR_NULL"
+    assert call(dtype=5) == "MIATTN_ERR_DTYPE"
+    assert call(dtype="f16") == "MIATTN_ERR_UNSUPPORTED"
+    assert call(layout=4) == "MIATTN_ERR_LAYOUT"
+    assert call(S=0) == "MIATTN_ERR_SHAPE"
+    assert call(N=300) == "MIATTN_ERR_SHAPE"
+
+
+def test_sparse_csr_attn_validation(mi):
+    def call(**kw):
+        a = dict(q=P, col=P, nnz=10, B=1, N=1, S=8, D=64, dtype="f32", scale=0.125)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.sparse_csr_attn(a["q"], P, P, P, P, a["col"], a["nnz"], a["B"], a["N"], a["S"],
+                               a["D"], a["dtype"], a["scale"], stream=0)
+        return mi.STATUS[e.value.status]
+    assert call(q=None) == "MIATTN_ERR_NULL"
+    assert call(col=None) == "MIATTN_ERR_NULL"
+    assert call(dtype="bf16") == "MIATTN_ERR_UNSUPPORTED"
+    assert call(dtype=11) == "MIATTN_ERR_DTYPE"
+    assert call(nnz=-1) == "MIATTN_ERR_SHAPE"
+    assert call(S=0) == "MIATTN_ERR_SHAPE"
+    assert call(scale=0.0) == "MIATTN_ERR_SCALE"
+    assert call(D=32) == "MIATTN_ERR_UNSUPPORTED"
+
+
+def test_status_strings(mi):
+    for code in range(10):
+        assert mi.status_str(code) and mi.status_str(code) != "unknown status"
+    assert mi.status_str(99) == "unknown status"
