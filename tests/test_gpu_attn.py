@@ -151,9 +151,10 @@ def test_varlen_full_workload_sampled(metric_run, seqs, heads):
 
 
 def test_varlen_full_workload_properties(metric_run):
-    """Every output row of the full workload: finite, and a convex combination of value
-    rows (so within the per-dimension min/max of the sequence's V); row 0 of each
-    sequence sees one key, so its softmax_sum is exactly 1 and its output is V[0]."""
+    """Every output row of the full workload is finite with softmax_sum >= 1; row 0 of each
+    sequence sees one key, so its softmax_sum is 1 (up to the rounding of the scaled
+    logit, which the exponent's fused multiply-add leaves as a residue of one ulp) and its
+    output is V[0]."""
     w, go, gm, gl = metric_run
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gm)) and np.all(np.isfinite(gl))
     assert np.all(gl >= 1.0 - 1e-6)
@@ -162,7 +163,7 @@ def test_varlen_full_workload_properties(metric_run):
     G = w["Nq"] // w["Nkv"]
     for b in range(w["B"]):
         r0 = int(cu[b])
-        assert np.all(gl[:, r0] == 1.0)
+        assert np.all(np.abs(gl[:, r0] - 1.0) <= 2.0 ** -22)
         for h in range(w["Nq"]):
             assert np.max(np.abs(go[r0, h] - v[r0, h // G])) <= 2 ** -8 * np.max(np.abs(v[r0, h // G]))
 
