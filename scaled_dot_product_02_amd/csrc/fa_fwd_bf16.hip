@@ -6,21 +6,32 @@
 // (aclnnFlashAttentionVarLenScore, 功能说明 / 约束说明), emitting the per-row softmax max
 // and sum that the ring-attention update consumes ("npu_ring_attention_update对外接口").
 //
-// How (one workgroup = 4 waves = 128 query rows of one head; 32 rows per wave):
-//   * Q rows stay in VGPRs for the whole kernel as MFMA B operands.
-//   * Per 64-key tile: K (row-major) and V (transposed, V^T[d][key]) are staged in LDS
-//     from 128-bit global loads that were issued one tile ahead (register double buffer).
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns ONE query column and 16 keys
-//     per 32x32 block, so the row max / row sum are in-lane reductions plus one exchange
-//     with the lane 32 apart.
-//   * Online softmax in the log2 domain (scale * log2(e) folded into one FMA before
-//     v_exp_f32); running max and sum stay in registers; the sum is accumulated from
-//     fp32 probabilities.
+// Design (one workgroup = 8 waves = 256 query rows of one head; two waves per SIMD):
+//   * Each wave owns one 32-row query block, held in VGPRs for the whole kernel as MFMA
+//     B operands.  A wave needs under 256 registers with every accumulator in ordinary
+//     VGPRs, so two waves share each SIMD and the hardware overlaps one wave's softmax
+//     (vector ALU) with the other's matrix-core work.  Waves w and w + 4 share a SIMD,
+//     which evens out the causal triangle across the four SIMDs.
+//   * Keys advance in tiles of 32.  K (row-major) and V (transposed, V^T[d][key]) tiles
+//     are staged from 128-bit global loads through registers into a 4-deep ring of LDS
+//     buffers, two tiles ahead, with one barrier per tile.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns ONE query column and 16 of the
+//     32 keys, so the row max / row sum are in-lane reductions plus one exchange with the
+//     lane 32 apart.
 //   * O^T += V^T P^T: the probabilities are rounded to bf16 (RNE) and used straight from
-//     the S^T accumulator registers as the B operand; the key order inside an MFMA is
-//     permuted consistently on the V^T side, so no shuffle is needed.
-//   * Tiles no visible pair touches are never loaded; the mask is evaluated only on
-//     tiles that straddle the band edge or the sequence end.
+//     the S^T accumulator registers as the B operand.  The order of keys inside each MFMA
+//     follows the S^T register layout; the V^T rows in LDS store their keys in that same
+//     order (bits 2 and 3 of the key index swapped), so each A operand is one 128-bit read.
+//   * Software pipeline: iteration t issues QK(t+1) and PV(t-1) on the matrix cores and
+//     then runs the softmax of tile t on the vector ALUs, which overlap.
+//   * Online softmax in the log2 domain (scale * log2(e) folded into one FMA before
+//     v_exp_f32).  The reference max m_ref moves only when a tile's max exceeds it by more
+//     than 2^8 (probabilities stay <= 256, safe in bf16 and fp32), so the O accumulator is
+//     almost never rescaled; the true running max is tracked separately and the emitted
+//     softmax_sum is re-referenced to it at the end.  The row sum is accumulated from the
+//     fp32 probabilities.
+//   * Tiles no visible pair touches are never loaded or computed; masks are evaluated
+//     only on tiles that straddle the band edge or the sequence end.
 #include "fa_common.h"
 
 namespace miattn {
@@ -32,44 +43,62 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = kBf16TileM;  // query rows per workgroup
-constexpr int BN = 64;          // keys per tile
-constexpr int NT = 256;         // threads per workgroup
+constexpr int BM = kBf16TileM;  // 256 query rows per workgroup
+constexpr int BN = 32;          // keys per tile
+constexpr int NT = 512;         // threads per workgroup (8 waves)
+constexpr int NBUF = 4;         // LDS ring depth (tiles)
+constexpr float kLazyThresh = 8.0f;  // log2 units
 
 template <int D>
 struct Cfg {
-    static constexpr int KS = D + 8;          // K row stride in LDS (bf16): 16 B pad
-    static constexpr int VS = BN + 4;         // V^T row stride in LDS (bf16): 8 B pad
-    static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-    static constexpr int KLOADS = BN * CPR / NT;   // K chunks per thread
-    static constexpr int VUNITS = (BN / 4) * CPR;  // (4 keys x 8 dims) V units per tile
-    static constexpr int KK = D / 16;         // MFMA k-steps over the head dim
-    static constexpr int RT = D / 32;         // 32-row output tiles over the head dim
+    static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
+    static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+    static constexpr int KCHUNKS = BN * CPR;          // K chunks per tile
+    static constexpr int KPER = KCHUNKS / 256;        // per K-loading thread (threads 0..255)
+    static constexpr int VUNITS = (BN / 4) * CPR;     // (4 keys x 8 dims) V units per tile
+    static constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
+    static constexpr int RT = D / 32;                 // 32-row output tiles over the head dim
+    static constexpr int KBUF = BN * KS;
+    static constexpr int VBUF = D * VS;
 };
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+// max / sum of x over the lane pair (l, l ^ 32); v_permlane32_swap(x, x) leaves
+// (x[l % 32], x[l % 32 + 32]) in every lane, so both lanes get the same result.
+__device__ inline float pair_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Position of key k (0..31 inside a tile) in a V^T row: bits 2 and 3 swapped, matching
+// the key order of the P operand taken from the S^T accumulator layout.
+__device__ inline int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <int D>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * C::KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[D * C::VS];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF * C::KBUF];
+    __shared__ __attribute__((aligned(16))) __bf16 Vt[NBUF * C::VBUF];
 
     const TileCoord tc = decode_tile(p, blockIdx.x, BM);
     if (!tc.live) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lq = lane & 31;     // query column owned by this lane
-    const int hf = lane >> 5;     // which half of the wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31;   // query column owned by this lane
+    const int hf = lane >> 5;   // half of the wave
 
+    const int len_q = tc.len_q, len_kv = tc.len_kv;
     const int i0 = tc.t * BM;
-    const int i1 = min(i0 + BM, tc.len_q);
-    const int wr0 = i0 + 32 * wave;              // first row of this wave
-    const int wr1 = min(wr0 + 32, i1);           // one past its last valid row
-    const int qi = wr0 + lq;                     // this lane's query row
+    const int i1 = min(i0 + BM, len_q);
 
     const __bf16* qg = (const __bf16*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
     const __bf16* kg = (const __bf16*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
@@ -77,166 +106,207 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     __bf16* og = (__bf16*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
     const int64_t st_base = (int64_t)tc.b * p.st_sb + (int64_t)tc.h * p.st_sh + tc.q0;
 
+    // ---- key tiles of the workgroup
     int kv_lo, kv_hi;
-    key_range(p, i0, i1, tc.len_kv, kv_lo, kv_hi);
+    key_range(p, i0, i1, len_kv, kv_lo, kv_hi);
+    const int T0 = kv_lo / BN;
+    const int T1 = kv_lo < kv_hi ? (kv_hi + BN - 1) / BN : T0;
+
+    // ---- this wave's rows [rb, re): active tiles, unmasked tiles, per-lane key bounds
+    const int rb = i0 + 32 * wave;
+    const int re = min(rb + 32, i1);
+    int w_lo = 0, w_hi = 0;   // tiles [w_lo, w_hi) hold a visible key of this wave
+    int full_lo = 0, full_hi = 0;   // tiles [full_lo, full_hi) need no mask
+    int jlo = 0, jhi = -1;          // keys [jlo, jhi] are visible from this lane's row
+    if (rb < re) {
+        int lo, hi;
+        key_range(p, rb, re, len_kv, lo, hi);
+        if (lo < hi) {
+            w_lo = lo / BN;
+            w_hi = (hi + BN - 1) / BN;
+        }
+        const int64_t flo = (int64_t)(re - 1) - p.pre;   // first key seen by every row
+        const int64_t fhi = (int64_t)rb + p.next;         // last key seen by every row
+        const int64_t fl = flo <= 0 ? 0 : (flo + BN - 1) / BN;
+        const int64_t fh = fhi < 0 ? 0 : (min(fhi, (int64_t)len_kv - 1) + 1) / BN;
+        full_lo = (int)min(fl, (int64_t)1 << 30);
+        full_hi = (int)fh;
+        const int qi = rb + lq;
+        const int64_t a = (int64_t)qi - p.pre, z = (int64_t)qi + p.next;
+        jlo = (int)max((int64_t)0, min(a, (int64_t)len_kv));
+        jhi = (int)max((int64_t)-1, min(z, (int64_t)len_kv - 1));
+    }
+    auto wave_active = [&](int t) { return t >= w_lo && t < w_hi; };
 
     // ---- Q fragment: B operand of S^T = K Q^T; lane (lq, hf) holds d = 16kk + 8hf + 0..7
     bf16x8 qf[C::KK];
-    #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-        if (qi < tc.len_q)
-            qf[kk] = *(const bf16x8*)(qg + (int64_t)qi * p.q_ss + 16 * kk + 8 * hf);
-        else
-            qf[kk] = bf16x8{};
+    {
+        const int qi = min(rb + lq, len_q - 1);
+        const __bf16* qrow = qg + (int64_t)qi * p.q_ss + 8 * hf;
+        #pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
     }
 
     f32x16 o[C::RT];
     #pragma unroll
     for (int r = 0; r < C::RT; ++r) o[r] = f32x16{};
-    float m_run = -INFINITY;   // running max of scale*log2(e)*s over visible keys
-    float l_run = 0.f;         // this lane's half of the running sum
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+    const float cl2 = p.scale_log2;
 
-    // ---- register staging of one K/V tile
-    u32x4 kreg[C::KLOADS];
-    u32x4 vreg[4];
-    const int vq = tid % (BN / 4);   // key quad of this thread's V unit
-    const int vc = tid / (BN / 4);   // 8-dim chunk of this thread's V unit
-    const bool v_active = tid < C::VUNITS;
+    // ---- global -> register -> LDS staging of one tile
+    //      threads 0..255 load K chunks, threads 256.. load V units (4 keys x 8 dims)
+    u32x4 stage[4];
+    const bool k_loader = tid < 256;
+    const int vuid = tid - 256;
+    const int vq = vuid % (BN / 4), vc = vuid / (BN / 4);
+    const bool v_loader = !k_loader && vuid < C::VUNITS;
 
-    auto load_tile = [&](int j0) {
-        #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) {
-            const int c = tid + NT * u;
-            const int row = j0 + c / C::CPR;
-            if (row < tc.len_kv)
-                kreg[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
-            else
-                kreg[u] = u32x4{};
-        }
-        if (v_active) {
+    auto load_tile = [&](int t) {
+        const int j0 = t * BN;
+        if (k_loader) {
+            #pragma unroll
+            for (int u = 0; u < C::KPER; ++u) {
+                const int c = tid + 256 * u;
+                const int row = min(j0 + c / C::CPR, len_kv - 1);
+                stage[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
+            }
+        } else if (v_loader) {
             #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = j0 + 4 * vq + r;
-                if (row < tc.len_kv)
-                    vreg[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
-                else
-                    vreg[r] = u32x4{};
+                const int row = min(j0 + 4 * vq + r, len_kv - 1);
+                stage[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
             }
         }
     };
-    auto store_tile = [&]() {
-        #pragma unroll
-        for (int u = 0; u < C::KLOADS; ++u) {
-            const int c = tid + NT * u;
-            *(u32x4*)(Ks + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = kreg[u];
-        }
-        if (v_active) {
-            // transpose 4 keys x 8 dims into 8 rows of V^T holding 4 keys each
+    auto store_tile = [&](int t) {
+        const int bf = t % NBUF;
+        __bf16* kb = Ks + bf * C::KBUF;
+        __bf16* vb = Vt + bf * C::VBUF;
+        if (k_loader) {
+            #pragma unroll
+            for (int u = 0; u < C::KPER; ++u) {
+                const int c = tid + 256 * u;
+                *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
+            }
+        } else if (v_loader) {
+            const int pos = vt_pos(4 * vq);
             #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 u32x2 lo, hi;
-                lo[0] = (vreg[0][e] & 0xffffu) | (vreg[1][e] << 16);
-                lo[1] = (vreg[2][e] & 0xffffu) | (vreg[3][e] << 16);
-                hi[0] = (vreg[0][e] >> 16) | (vreg[1][e] & 0xffff0000u);
-                hi[1] = (vreg[2][e] >> 16) | (vreg[3][e] & 0xffff0000u);
-                *(u32x2*)(Vt + (8 * vc + 2 * e) * C::VS + 4 * vq) = lo;
-                *(u32x2*)(Vt + (8 * vc + 2 * e + 1) * C::VS + 4 * vq) = hi;
+                lo[0] = (stage[0][e] & 0xffffu) | (stage[1][e] << 16);
+                lo[1] = (stage[2][e] & 0xffffu) | (stage[3][e] << 16);
+                hi[0] = (stage[0][e] >> 16) | (stage[1][e] & 0xffff0000u);
+                hi[1] = (stage[2][e] >> 16) | (stage[3][e] & 0xffff0000u);
+                *(u32x2*)(vb + (8 * vc + 2 * e) * C::VS + pos) = lo;
+                *(u32x2*)(vb + (8 * vc + 2 * e + 1) * C::VS + pos) = hi;
             }
         }
     };
 
-    const int j_start = (kv_lo / BN) * BN;
-    if (kv_lo < kv_hi) load_tile(j_start);
-
-    for (int j0 = j_start; j0 < kv_hi; j0 += BN) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (j0 + BN < kv_hi) load_tile(j0 + BN);
-
-        // does any pair of this wave's rows and this tile lie inside the band?
-        const bool wave_rows = wr0 < wr1;
-        const int64_t dmax = (int64_t)(j0 + BN - 1) - wr0;      // largest j - i
-        const int64_t dmin = (int64_t)j0 - (wr1 - 1);           // smallest j - i
-        const bool any_vis = wave_rows && j0 < tc.len_kv && dmin <= p.next && -dmax <= p.pre;
-        if (!any_vis) continue;
-        const bool full = (j0 + BN <= tc.len_kv) && dmax <= p.next && -dmin <= p.pre;
-
-        // ---- S^T = K Q^T : two 32(key) x 32(query) blocks
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+    // ---- S^T = K Q^T for tile t (32 keys x 32 queries)
+    auto qk = [&](int t, f32x16& s) {
+        const __bf16* kb = Ks + (t % NBUF) * C::KBUF + lq * C::KS + 8 * hf;
+        s = f32x16{};
         #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
-            #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *(const bf16x8*)(Ks + (32 * kb + lq) * C::KS + 16 * kk + 8 * hf);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-            }
+            const bf16x8 a = *(const bf16x8*)(kb + 16 * kk);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
         }
-        // key of accumulator element i of block kb: j0 + 32kb + 8(i/4) + 4hf + i%4
-        if (!full) {
-            #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = j0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                    const int64_t dj = (int64_t)j - qi;
-                    if (!(j < tc.len_kv && dj <= p.next && -dj <= p.pre)) s[kb][i] = -INFINITY;
-                }
-            }
-        }
+    };
 
-        // ---- online softmax (log2 domain)
-        float mx = -INFINITY;
-        #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx * p.scale_log2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float rs = 0.f;
-        #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], p.scale_log2, -m_use));
-                s[kb][i] = e;
-                rs += e;
-            }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        #pragma unroll
-        for (int r = 0; r < C::RT; ++r)
-            #pragma unroll
-            for (int i = 0; i < 16; ++i) o[r][i] *= alpha;
-
-        // ---- P (bf16) as B operand: slot t of MFMA j holds key 16j + 8(t/4) + 4hf + t%4
-        bf16x8 pf[4];
-        #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            #pragma unroll
-            for (int t = 0; t < 8; ++t) pf[j][t] = (__bf16)s[j >> 1][8 * (j & 1) + t];
-
-        // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T for tile t
+    bf16x8 pp[2];
+    auto pv = [&](int t) {
+        const __bf16* vb = Vt + (t % NBUF) * C::VBUF + lq * C::VS + 8 * hf;
         #pragma unroll
         for (int r = 0; r < C::RT; ++r) {
             #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const __bf16* vr = Vt + (32 * r + lq) * C::VS + 16 * j + 4 * hf;
-                const bf16x4 lo = *(const bf16x4*)vr;
-                const bf16x4 hi = *(const bf16x4*)(vr + 8);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], o[r], 0, 0, 0);
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 a = *(const bf16x8*)(vb + 32 * r * C::VS + 16 * j);
+                o[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[j], o[r], 0, 0, 0);
             }
         }
+    };
+
+    // ---- online softmax of tile t; leaves bf16 probabilities in pp
+    auto softmax = [&](int t, f32x16& s) {
+        const int jb = t * BN + 4 * hf;   // key of element i: jb + 8(i/4) + i%4
+        if (t < full_lo || t >= full_hi) {
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = jb + 8 * (i >> 2) + (i & 3);
+                if (j < jlo || j > jhi) s[i] = -INFINITY;
+            }
+        }
+        float mx = s[0];
+        #pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        mx = pair_max(mx);
+        const float mt = mx * cl2;
+        m_true = fmaxf(m_true, mt);
+        const bool need = mt > m_ref + kLazyThresh;
+        if (__any(need)) {
+            const float m_new = need ? mt : m_ref;
+            const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+            #pragma unroll
+            for (int r = 0; r < C::RT; ++r)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) o[r][i] *= alpha;
+            m_ref = m_new;
+        }
+        const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+        float rs = 0.f;
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, -mu));
+            s[i] = e;
+            rs += e;
+        }
+        l_run += rs;
+        // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8j + e
+        #pragma unroll
+        for (int j = 0; j < 2; ++j)
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) pp[j][e] = (__bf16)s[8 * j + e];
+    };
+
+    // iteration t: prefetch tile t+2, S(t+1) and O += P(t-1) V(t-1) on the matrix cores,
+    // softmax(t) on the vector ALUs, then land tile t+2 in LDS
+    auto step = [&](int t, f32x16& sc, f32x16& sn) {
+        if (t + 2 < T1) load_tile(t + 2);
+        if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
+        if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1);
+        if (wave_active(t)) softmax(t, sc);
+        if (t + 2 < T1) store_tile(t + 2);
+        __syncthreads();
+    };
+
+    f32x16 sa, sb;
+    if (T0 < T1) {
+        load_tile(T0);
+        store_tile(T0);
+        if (T0 + 1 < T1) {
+            load_tile(T0 + 1);
+            store_tile(T0 + 1);
+        }
+        __syncthreads();
+        if (wave_active(T0)) qk(T0, sa);
+        int t = T0;
+        for (; t + 1 < T1; t += 2) {
+            step(t, sa, sb);
+            step(t + 1, sb, sa);
+        }
+        if (t < T1) step(t, sa, sb);
+        if (wave_active(T1 - 1)) pv(T1 - 1);
     }
 
     // ---- epilogue: normalize, round to bf16, store; emit the row statistics
-    const float lt = l_run + xor32(l_run);
+    const float lt = pair_sum(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qi < wr1) {
-        __bf16* orow = og + (int64_t)qi * p.o_ss;
+    const int qi = rb + lq;
+    if (qi < re) {
+        __bf16* orow = og + (int64_t)qi * p.o_ss + 4 * hf;
         #pragma unroll
         for (int r = 0; r < C::RT; ++r)
             #pragma unroll
@@ -244,11 +314,12 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
                 bf16x4 w;
                 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][4 * g4 + e] * inv);
-                *(bf16x4*)(orow + 32 * r + 8 * g4 + 4 * hf) = w;
+                *(bf16x4*)(orow + 32 * r + 8 * g4) = w;
             }
         if (hf == 0) {
-            if (p.smax) p.smax[st_base + qi] = lt > 0.f ? m_run * 0.69314718055994530942f : -INFINITY;
-            if (p.ssum) p.ssum[st_base + qi] = lt;
+            const bool any = lt > 0.f;
+            if (p.smax) p.smax[st_base + qi] = any ? m_true * 0.69314718055994530942f : -INFINITY;
+            if (p.ssum) p.ssum[st_base + qi] = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
         }
     }
 }

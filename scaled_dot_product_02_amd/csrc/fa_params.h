@@ -64,7 +64,7 @@ hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream)
 hipError_t launch_sparse_csr(const SparseParams& p, int D, hipStream_t stream);
 
 // Row tile heights, used by the C-ABI layer to size the grids.
-constexpr int kBf16TileM = 128;
+constexpr int kBf16TileM = 256;
 constexpr int kF32TileM = 64;
 
 }  // namespace miattn
