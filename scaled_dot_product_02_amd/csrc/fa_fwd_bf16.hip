@@ -44,7 +44,15 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = kBf16TileM;  // 256 query rows per workgroup
-constexpr int BN = 32;          // keys per tile
+#ifndef FA_BN
+#define FA_BN 64
+#endif
+#ifndef FA_PREFETCH
+#define FA_PREFETCH 2
+#endif
+constexpr int BN = FA_BN;       // keys per tile
+constexpr int NKB = BN / 32;    // 32-key blocks per tile
+constexpr int PF = FA_PREFETCH; // tiles in flight ahead of the one in softmax (2 or 3)
 constexpr int NT = 512;         // threads per workgroup (8 waves)
 constexpr int NBUF = 4;         // LDS ring depth (tiles)
 constexpr float kLazyThresh = 8.0f;  // log2 units
@@ -53,9 +61,11 @@ template <int D>
 struct Cfg {
     static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
     static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
+    static constexpr int VPER = 4;                    // V units are 4 keys x 8 dims
     static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
     static constexpr int KCHUNKS = BN * CPR;          // K chunks per tile
     static constexpr int KPER = KCHUNKS / 256;        // per K-loading thread (threads 0..255)
+    static constexpr int SREG = KPER > 4 ? KPER : 4;  // staging registers (16 B each)
     static constexpr int VUNITS = (BN / 4) * CPR;     // (4 keys x 8 dims) V units per tile
     static constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
     static constexpr int RT = D / 32;                 // 32-row output tiles over the head dim
@@ -155,31 +165,52 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 
     // ---- global -> register -> LDS staging of one tile
     //      threads 0..255 load K chunks, threads 256.. load V units (4 keys x 8 dims)
-    u32x4 stage[4];
+    u32x4 stA[C::SREG], stB[C::SREG];
     const bool k_loader = tid < 256;
     const int vuid = tid - 256;
     const int vq = vuid % (BN / 4), vc = vuid / (BN / 4);
     const bool v_loader = !k_loader && vuid < C::VUNITS;
 
-    auto load_tile = [&](int t) {
+    // byte offsets of this thread's 16-byte chunks inside a tile whose first key is 0
+    uint32_t koff[C::KPER], voff = 0;
+    #pragma unroll
+    for (int u = 0; u < C::KPER; ++u) {
+        const int c = tid + 256 * u;
+        koff[u] = (uint32_t)(((c / C::CPR) * p.k_ss + 8 * (c % C::CPR)) * 2);
+    }
+    if (v_loader) voff = (uint32_t)((4 * vq * p.v_ss + 8 * vc) * 2);
+    const uint32_t vrow_bytes = (uint32_t)(p.v_ss * 2);
+
+    auto load_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
         const int j0 = t * BN;
+        const bool whole = j0 + BN <= len_kv;   // ragged last tile: clamp rows to the sequence
         if (k_loader) {
+            const char* kt = (const char*)(kg + (int64_t)j0 * p.k_ss);
             #pragma unroll
             for (int u = 0; u < C::KPER; ++u) {
-                const int c = tid + 256 * u;
-                const int row = min(j0 + c / C::CPR, len_kv - 1);
-                stage[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
+                if (whole) {
+                    stage[u] = *(const u32x4*)(kt + koff[u]);
+                } else {
+                    const int c = tid + 256 * u;
+                    const int row = min(j0 + c / C::CPR, len_kv - 1);
+                    stage[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
+                }
             }
         } else if (v_loader) {
+            const char* vt = (const char*)(vg + (int64_t)j0 * p.v_ss);
             #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = min(j0 + 4 * vq + r, len_kv - 1);
-                stage[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
+                if (whole) {
+                    stage[r] = *(const u32x4*)(vt + voff + r * vrow_bytes);
+                } else {
+                    const int row = min(j0 + 4 * vq + r, len_kv - 1);
+                    stage[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
+                }
             }
         }
     };
-    auto store_tile = [&](int t) {
-        const int bf = t % NBUF;
+    auto store_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
+        const int bf = t & (NBUF - 1);
         __bf16* kb = Ks + bf * C::KBUF;
         __bf16* vb = Vt + bf * C::VBUF;
         if (k_loader) {
@@ -203,25 +234,28 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         }
     };
 
-    // ---- S^T = K Q^T for tile t (32 keys x 32 queries)
-    auto qk = [&](int t, f32x16& s) {
-        const __bf16* kb = Ks + (t % NBUF) * C::KBUF + lq * C::KS + 8 * hf;
-        s = f32x16{};
+    // ---- S^T = K Q^T for tile t (NKB blocks of 32 keys x 32 queries)
+    auto qk = [&](int t, f32x16 (&s)[NKB]) {
+        const __bf16* kb = Ks + (t & (NBUF - 1)) * C::KBUF + lq * C::KS + 8 * hf;
+        #pragma unroll
+        for (int b = 0; b < NKB; ++b) s[b] = f32x16{};
         #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
-            const bf16x8 a = *(const bf16x8*)(kb + 16 * kk);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+            #pragma unroll
+            for (int b = 0; b < NKB; ++b) {
+                const bf16x8 a = *(const bf16x8*)(kb + 32 * b * C::KS + 16 * kk);
+                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[b], 0, 0, 0);
+            }
         }
     };
 
     // ---- O^T += V^T P^T for tile t
-    bf16x8 pp[2];
-    auto pv = [&](int t) {
-        const __bf16* vb = Vt + (t % NBUF) * C::VBUF + lq * C::VS + 8 * hf;
+    auto pv = [&](int t, const bf16x8 (&pp)[2 * NKB]) {
+        const __bf16* vb = Vt + (t & (NBUF - 1)) * C::VBUF + lq * C::VS + 8 * hf;
         #pragma unroll
         for (int r = 0; r < C::RT; ++r) {
             #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 2 * NKB; ++j) {
                 const bf16x8 a = *(const bf16x8*)(vb + 32 * r * C::VS + 16 * j);
                 o[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[j], o[r], 0, 0, 0);
             }
@@ -229,18 +263,22 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     };
 
     // ---- online softmax of tile t; leaves bf16 probabilities in pp
-    auto softmax = [&](int t, f32x16& s) {
-        const int jb = t * BN + 4 * hf;   // key of element i: jb + 8(i/4) + i%4
+    auto softmax = [&](int t, f32x16 (&s)[NKB], bf16x8 (&pp)[2 * NKB]) {
+        const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = jb + 8 * (i >> 2) + (i & 3);
-                if (j < jlo || j > jhi) s[i] = -INFINITY;
-            }
+            for (int b = 0; b < NKB; ++b)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = jb + 32 * b + 8 * (i >> 2) + (i & 3);
+                    if (j < jlo || j > jhi) s[b][i] = -INFINITY;
+                }
         }
-        float mx = s[0];
+        float mx = s[0][0];
         #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        for (int b = 0; b < NKB; ++b)
+            #pragma unroll
+            for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[b][i]);
         mx = pair_max(mx);
         const float mt = mx * cl2;
         m_true = fmaxf(m_true, mt);
@@ -258,47 +296,62 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         const float mu = m_ref == -INFINITY ? 0.f : m_ref;
         float rs = 0.f;
         #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, -mu));
-            s[i] = e;
-            rs += e;
-        }
-        l_run += rs;
-        // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8j + e
-        #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int b = 0; b < NKB; ++b)
             #pragma unroll
-            for (int e = 0; e < 8; ++e) pp[j][e] = (__bf16)s[8 * j + e];
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][i], cl2, -mu));
+                s[b][i] = e;
+                rs += e;
+            }
+        l_run += rs;
+        // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8(j%2) + e of block j/2
+        #pragma unroll
+        for (int j = 0; j < 2 * NKB; ++j)
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) pp[j][e] = (__bf16)s[j >> 1][8 * (j & 1) + e];
     };
 
-    // iteration t: prefetch tile t+2, S(t+1) and O += P(t-1) V(t-1) on the matrix cores,
-    // softmax(t) on the vector ALUs, then land tile t+2 in LDS
-    auto step = [&](int t, f32x16& sc, f32x16& sn) {
-        if (t + 2 < T1) load_tile(t + 2);
+    // Iteration t: prefetch tile t+PF into registers; S(t+1) = K Q^T and O += P(t-1) V(t-1)
+    // on the matrix cores; softmax(t) on the vector ALUs; land tile t+2 in LDS.  The two
+    // waves of a SIMD (w, w+4) run these phases in opposite orders, so one wave's softmax
+    // overlaps the other's MFMAs; P is double-buffered for that.
+    const bool late = (wave & 4) != 0;
+    auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], bf16x8 (&pc)[2 * NKB],
+                    bf16x8 (&pprev)[2 * NKB], u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
+        if (t + PF < T1) load_tile(t + PF, ld);
+        if (late && wave_active(t)) softmax(t, sc, pc);
         if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
-        if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1);
-        if (wave_active(t)) softmax(t, sc);
-        if (t + 2 < T1) store_tile(t + 2);
+        if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pprev);
+        if (!late && wave_active(t)) softmax(t, sc, pc);
+        if (t + 2 < T1) store_tile(t + 2, sto);
         __syncthreads();
     };
 
-    f32x16 sa, sb;
+    f32x16 sa[NKB], sb[NKB];
+    bf16x8 pa[2 * NKB], pb[2 * NKB];
     if (T0 < T1) {
-        load_tile(T0);
-        store_tile(T0);
+        load_tile(T0, stA);
+        store_tile(T0, stA);
         if (T0 + 1 < T1) {
-            load_tile(T0 + 1);
-            store_tile(T0 + 1);
+            load_tile(T0 + 1, stA);
+            store_tile(T0 + 1, stA);
         }
+        if (PF == 3 && T0 + 2 < T1) load_tile(T0 + 2, stB);
         __syncthreads();
         if (wave_active(T0)) qk(T0, sa);
         int t = T0;
+        // tile t+2 sits in the register set loaded one step earlier when PF == 3
+        u32x4 (&sB)[C::SREG] = PF == 3 ? stB : stA;
         for (; t + 1 < T1; t += 2) {
-            step(t, sa, sb);
-            step(t + 1, sb, sa);
+            step(t, sa, sb, pa, pb, stA, sB);
+            step(t + 1, sb, sa, pb, pa, sB, stA);
         }
-        if (t < T1) step(t, sa, sb);
-        if (wave_active(T1 - 1)) pv(T1 - 1);
+        if (t < T1) {
+            step(t, sa, sb, pa, pb, stA, sB);
+            if (wave_active(T1 - 1)) pv(T1 - 1, pa);
+        } else {
+            if (wave_active(T1 - 1)) pv(T1 - 1, pb);
+        }
     }
 
     // ---- epilogue: normalize, round to bf16, store; emit the row statistics

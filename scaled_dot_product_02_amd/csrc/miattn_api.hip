@@ -2,7 +2,7 @@
 // sizing and launches on the caller's stream.  Declared in include/miattn.h.
 #include <math.h>
 
-#include "../../include/miattn.h"
+#include "miattn.h"
 #include "fa_params.h"
 
 using namespace miattn;
