@@ -77,10 +77,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-heads", type=int, default=16,
+    ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads in the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="time only the metric kernel (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device-to-device copies of MIB MiB (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -97,6 +100,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     def up(arr, dtype):
         if dtype == "bf16":
