@@ -53,6 +53,13 @@ constexpr int BM = kBf16TileM;  // 256 query rows per workgroup
 constexpr int BN = FA_BN;       // keys per tile
 constexpr int NKB = BN / 32;    // 32-key blocks per tile
 constexpr int PF = FA_PREFETCH; // tiles in flight ahead of the one in softmax (2 or 3)
+#ifndef FA_LDSD
+#define FA_LDSD 4
+#endif
+#ifndef FA_SCHED
+#define FA_SCHED 1
+#endif
+constexpr int LDSD = FA_LDSD;   // LDS fragment reads kept in flight ahead of their MFMAs
 constexpr int NT = 512;         // threads per workgroup (8 waves)
 constexpr int NBUF = 4;         // LDS ring depth (tiles)
 constexpr float kLazyThresh = 8.0f;  // log2 units
@@ -156,6 +163,9 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
     }
+    // Drain the Q loads here, so that no wait on them is left for the key loop (where it
+    // would also wait for the tile prefetches issued in the same step).
+    __builtin_amdgcn_s_waitcnt(0);
 
     f32x16 o[C::RT];
     #pragma unroll
@@ -183,26 +193,27 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 
     auto load_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
         const int j0 = t * BN;
-        const bool whole = j0 + BN <= len_kv;   // ragged last tile: clamp rows to the sequence
-        if (k_loader) {
-            const char* kt = (const char*)(kg + (int64_t)j0 * p.k_ss);
-            #pragma unroll
-            for (int u = 0; u < C::KPER; ++u) {
-                if (whole) {
-                    stage[u] = *(const u32x4*)(kt + koff[u]);
-                } else {
+        if (j0 + BN <= len_kv) {
+            if (k_loader) {
+                const char* kt = (const char*)(kg + (int64_t)j0 * p.k_ss);
+                #pragma unroll
+                for (int u = 0; u < C::KPER; ++u) stage[u] = *(const u32x4*)(kt + koff[u]);
+            } else if (v_loader) {
+                const char* vt = (const char*)(vg + (int64_t)j0 * p.v_ss);
+                #pragma unroll
+                for (int r = 0; r < 4; ++r) stage[r] = *(const u32x4*)(vt + voff + r * vrow_bytes);
+            }
+        } else {   // ragged last tile: clamp rows to the sequence
+            if (k_loader) {
+                #pragma unroll
+                for (int u = 0; u < C::KPER; ++u) {
                     const int c = tid + 256 * u;
                     const int row = min(j0 + c / C::CPR, len_kv - 1);
                     stage[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
                 }
-            }
-        } else if (v_loader) {
-            const char* vt = (const char*)(vg + (int64_t)j0 * p.v_ss);
-            #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (whole) {
-                    stage[r] = *(const u32x4*)(vt + voff + r * vrow_bytes);
-                } else {
+            } else if (v_loader) {
+                #pragma unroll
+                for (int r = 0; r < 4; ++r) {
                     const int row = min(j0 + 4 * vq + r, len_kv - 1);
                     stage[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
                 }
@@ -237,29 +248,54 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     // ---- S^T = K Q^T for tile t (NKB blocks of 32 keys x 32 queries)
     auto qk = [&](int t, f32x16 (&s)[NKB]) {
         const __bf16* kb = Ks + (t & (NBUF - 1)) * C::KBUF + lq * C::KS + 8 * hf;
+        constexpr int NF = C::KK * NKB;   // fragments (= MFMAs), fragment f: kk = f / NKB, b = f % NKB
+        bf16x8 a[NF];
         #pragma unroll
         for (int b = 0; b < NKB; ++b) s[b] = f32x16{};
         #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-            #pragma unroll
-            for (int b = 0; b < NKB; ++b) {
-                const bf16x8 a = *(const bf16x8*)(kb + 32 * b * C::KS + 16 * kk);
-                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[b], 0, 0, 0);
-            }
+        for (int f = 0; f < LDSD && f < NF; ++f)
+            a[f] = *(const bf16x8*)(kb + 32 * (f % NKB) * C::KS + 16 * (f / NKB));
+        #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f + LDSD < NF)
+                a[f + LDSD] = *(const bf16x8*)(kb + 32 * ((f + LDSD) % NKB) * C::KS + 16 * ((f + LDSD) / NKB));
+            s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], qf[f / NKB], s[f % NKB], 0, 0, 0);
         }
+#if FA_SCHED
+        // keep LDSD reads in flight ahead of the MFMAs that consume them
+        __builtin_amdgcn_sched_group_barrier(0x100, LDSD, 0);
+        #pragma unroll
+        for (int f = 0; f < NF - LDSD; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LDSD, 0);
+#endif
     };
 
     // ---- O^T += V^T P^T for tile t
     auto pv = [&](int t, const bf16x8 (&pp)[2 * NKB]) {
         const __bf16* vb = Vt + (t & (NBUF - 1)) * C::VBUF + lq * C::VS + 8 * hf;
+        constexpr int NF = C::RT * 2 * NKB;   // fragment f: r = f / (2 NKB), j = f % (2 NKB)
+        bf16x8 a[NF];
         #pragma unroll
-        for (int r = 0; r < C::RT; ++r) {
-            #pragma unroll
-            for (int j = 0; j < 2 * NKB; ++j) {
-                const bf16x8 a = *(const bf16x8*)(vb + 32 * r * C::VS + 16 * j);
-                o[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[j], o[r], 0, 0, 0);
-            }
+        for (int f = 0; f < LDSD && f < NF; ++f)
+            a[f] = *(const bf16x8*)(vb + 32 * (f / (2 * NKB)) * C::VS + 16 * (f % (2 * NKB)));
+        #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f + LDSD < NF)
+                a[f + LDSD] = *(const bf16x8*)(vb + 32 * ((f + LDSD) / (2 * NKB)) * C::VS + 16 * ((f + LDSD) % (2 * NKB)));
+            o[f / (2 * NKB)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], pp[f % (2 * NKB)], o[f / (2 * NKB)], 0, 0, 0);
         }
+#if FA_SCHED
+        __builtin_amdgcn_sched_group_barrier(0x100, LDSD, 0);
+        #pragma unroll
+        for (int f = 0; f < NF - LDSD; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LDSD, 0);
+#endif
     };
 
     // ---- online softmax of tile t; leaves bf16 probabilities in pp
@@ -274,12 +310,18 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
                     if (j < jlo || j > jhi) s[b][i] = -INFINITY;
                 }
         }
-        float mx = s[0][0];
+        // tree reductions keep the dependent chains short
+        float mq[4];
         #pragma unroll
-        for (int b = 0; b < NKB; ++b)
+        for (int c = 0; c < 4; ++c) {
+            mq[c] = s[0][4 * c];
             #pragma unroll
-            for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-        mx = pair_max(mx);
+            for (int b = 0; b < NKB; ++b)
+                #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (b | i) mq[c] = fmaxf(mq[c], s[b][4 * c + i]);
+        }
+        float mx = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
         const float mt = mx * cl2;
         m_true = fmaxf(m_true, mt);
         const bool need = mt > m_ref + kLazyThresh;
@@ -294,16 +336,16 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
             m_ref = m_new;
         }
         const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-        float rs = 0.f;
+        float rq[4] = {0.f, 0.f, 0.f, 0.f};
         #pragma unroll
         for (int b = 0; b < NKB; ++b)
             #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][i], cl2, -mu));
                 s[b][i] = e;
-                rs += e;
+                rq[i & 3] += e;
             }
-        l_run += rs;
+        l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
         // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8(j%2) + e of block j/2
         #pragma unroll
         for (int j = 0; j < 2 * NKB; ++j)
@@ -312,23 +354,19 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     };
 
     // Iteration t: prefetch tile t+PF into registers; S(t+1) = K Q^T and O += P(t-1) V(t-1)
-    // on the matrix cores; softmax(t) on the vector ALUs; land tile t+2 in LDS.  The two
-    // waves of a SIMD (w, w+4) run these phases in opposite orders, so one wave's softmax
-    // overlaps the other's MFMAs; P is double-buffered for that.
-    const bool late = (wave & 4) != 0;
-    auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], bf16x8 (&pc)[2 * NKB],
-                    bf16x8 (&pprev)[2 * NKB], u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
+    // on the matrix cores; softmax(t) on the vector ALUs; land tile t+2 in LDS.
+    bf16x8 pp[2 * NKB];
+    auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], u32x4 (&ld)[C::SREG],
+                    u32x4 (&sto)[C::SREG]) {
         if (t + PF < T1) load_tile(t + PF, ld);
-        if (late && wave_active(t)) softmax(t, sc, pc);
         if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
-        if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pprev);
-        if (!late && wave_active(t)) softmax(t, sc, pc);
+        if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
+        if (wave_active(t)) softmax(t, sc, pp);
         if (t + 2 < T1) store_tile(t + 2, sto);
         __syncthreads();
     };
 
     f32x16 sa[NKB], sb[NKB];
-    bf16x8 pa[2 * NKB], pb[2 * NKB];
     if (T0 < T1) {
         load_tile(T0, stA);
         store_tile(T0, stA);
@@ -338,20 +376,16 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         }
         if (PF == 3 && T0 + 2 < T1) load_tile(T0 + 2, stB);
         __syncthreads();
-        if (wave_active(T0)) qk(T0, sa);
+        qk(T0, sa);
         int t = T0;
         // tile t+2 sits in the register set loaded one step earlier when PF == 3
         u32x4 (&sB)[C::SREG] = PF == 3 ? stB : stA;
         for (; t + 1 < T1; t += 2) {
-            step(t, sa, sb, pa, pb, stA, sB);
-            step(t + 1, sb, sa, pb, pa, sB, stA);
+            step(t, sa, sb, stA, sB);
+            step(t + 1, sb, sa, sB, stA);
         }
-        if (t < T1) {
-            step(t, sa, sb, pa, pb, stA, sB);
-            if (wave_active(T1 - 1)) pv(T1 - 1, pa);
-        } else {
-            if (wave_active(T1 - 1)) pv(T1 - 1, pb);
-        }
+        if (t < T1) step(t, sa, sb, stA, sB);
+        if (wave_active(T1 - 1)) pv(T1 - 1, pp);
     }
 
     // ---- epilogue: normalize, round to bf16, store; emit the row statistics
