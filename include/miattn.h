@@ -132,7 +132,8 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
  *   (a packed TND batch is B = 1, S = T with layout BSND; its stats are then [N, T]).
  *   out may alias prev_out or cur_out; out_max/out_sum may alias the matching input stats
  *   (the update is elementwise and each element is read before it is written by the same
- *   thread).  Any D >= 1.
+ *   thread).  Any D >= 1; limits: N <= 256, B <= 65535, N * D <= 2^27, S <= 2^30,
+ *   B * N * S * D <= 2^40 (else MIATTN_ERR_SHAPE).
  */
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,
                                const void* cur_out, const float* cur_max, const float* cur_sum,

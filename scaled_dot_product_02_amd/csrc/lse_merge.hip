@@ -6,17 +6,20 @@
 // output is rounded (RNE) to its storage type.  Both partials empty (m = -inf) gives
 // (0, -inf, 0).
 //
-// HBM-bound elementwise work.  One workgroup takes SB = 16 consecutive positions s of one
-// batch entry b for all heads: it first reads the 4 statistics of those N x 16 rows
-// (16 consecutive floats per head, coalesced), forms the two weights per row in LDS and
-// writes the merged statistics, then streams the outputs in 16-byte vectors (8 bf16 or
-// 4 fp32) with no further global reads of the statistics.
+// HBM-bound elementwise work.  One workgroup takes SB = 8 consecutive positions s of one
+// batch entry b for all heads.  Its N x 8 x D output elements are walked as one flat range
+// of 16-byte vectors (8 bf16 or 4 fp32), in passes of UV = 4 vectors per thread and array,
+// with non-temporal loads and stores (nothing reads them again).  The loads of the first
+// pass are issued before the statistics of the N x 8 rows are read (8 consecutive floats
+// per head), turned into two weights per row in LDS and written back merged; one barrier
+// then makes the weights visible, and every pass combines and stores its vectors.
 #include "fa_params.h"
 
 namespace miattn {
 namespace {
 
-constexpr int SB = 16;     // positions per workgroup
+constexpr int SB = 8;      // positions per workgroup
+constexpr int UV = 4;      // vectors (or elements) per thread and array in one pass
 constexpr int NT = 256;    // threads per workgroup
 constexpr int NMAX = 256;  // largest head count
 
@@ -70,48 +73,75 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeParams p)
     const int tid = threadIdx.x;
     const int nrow = min(SB, p.S - s0);
 
-    // weights and merged statistics of the N x SB rows
-    for (int e = tid; e < p.N * SB; e += NT) {
-        const int n = e / SB, ds = e % SB;
-        if (ds >= nrow) continue;
-        const int64_t idx = ((int64_t)b * p.N + n) * p.S + s0 + ds;
-        const float m1 = p.m1[idx], l1 = p.l1[idx], m2 = p.m2[idx], l2 = p.l2[idx];
-        const float m = fmaxf(m1, m2);
-        float w1 = 0.f, w2 = 0.f, l = 0.f;
-        if (m != -INFINITY) {
-            const float a = l1 * expf(m1 - m);
-            const float c = l2 * expf(m2 - m);
-            l = a + c;
-            w1 = a / l;
-            w2 = c / l;
-        }
-        w1s[e] = w1;
-        w2s[e] = w2;
-        p.mo[idx] = m;
-        p.lo[idx] = l;
-    }
-    __syncthreads();
-
     const int W = VEC ? Vec<T>::W : 1;
     const int per_row = p.N * p.D / W;   // vectors (or elements) per position
-    for (int ds = 0; ds < nrow; ++ds) {
-        const int64_t rbase = (int64_t)b * p.sb + (int64_t)(s0 + ds) * p.ss;
-        for (int c = tid; c < per_row; c += NT) {
-            const int n = (c * W) / p.D;
-            const int d = (c * W) - n * p.D;
-            const int64_t off = rbase + (int64_t)n * p.sh + d;
-            const float w1 = w1s[n * SB + ds], w2 = w2s[n * SB + ds];
-            if constexpr (VEC) {
-                float x1[Vec<T>::W], x2[Vec<T>::W], y[Vec<T>::W];
-                unpack(*(const u32x4*)((const T*)p.o1 + off), x1, (T*)nullptr);
-                unpack(*(const u32x4*)((const T*)p.o2 + off), x2, (T*)nullptr);
-                #pragma unroll
-                for (int e = 0; e < Vec<T>::W; ++e) y[e] = __builtin_fmaf(x1[e], w1, x2[e] * w2);
-                *(u32x4*)((T*)p.out + off) = pack(y, (T*)nullptr);
-            } else {
-                const float x1 = (float)((const T*)p.o1)[off];
-                const float x2 = (float)((const T*)p.o2)[off];
-                ((T*)p.out)[off] = (T)__builtin_fmaf(x1, w1, x2 * w2);
+    const int total = nrow * per_row;
+
+    for (int base = 0; base < total; base += NT * UV) {
+        u32x4 x1[UV], x2[UV];
+        float y1[UV], y2[UV];
+        int64_t off[UV];
+        int slot[UV];
+        #pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = base + tid + NT * u;
+            if (c < total) {
+                // vector c: position s0 + ds, head n, dims d .. d + W - 1
+                const int ds = c / per_row;
+                const int cr = (c - ds * per_row) * W;
+                const int n = cr / p.D;
+                const int d = cr - n * p.D;
+                slot[u] = n * SB + ds;
+                off[u] = (int64_t)b * p.sb + (int64_t)(s0 + ds) * p.ss + (int64_t)n * p.sh + d;
+                if constexpr (VEC) {
+                    x1[u] = __builtin_nontemporal_load((const u32x4*)((const T*)p.o1 + off[u]));
+                    x2[u] = __builtin_nontemporal_load((const u32x4*)((const T*)p.o2 + off[u]));
+                } else {
+                    y1[u] = (float)((const T*)p.o1)[off[u]];
+                    y2[u] = (float)((const T*)p.o2)[off[u]];
+                }
+            }
+        }
+        if (base == 0) {
+            // weights and merged statistics of the N x SB rows, while the first loads fly;
+            // each row's statistics are read and written by one thread, so outputs may
+            // alias the inputs
+            for (int e = tid; e < p.N * SB; e += NT) {
+                const int n = e / SB, ds = e % SB;
+                if (ds >= nrow) continue;
+                const int64_t idx = ((int64_t)b * p.N + n) * p.S + s0 + ds;
+                const float m1 = p.m1[idx], l1 = p.l1[idx], m2 = p.m2[idx], l2 = p.l2[idx];
+                const float m = fmaxf(m1, m2);
+                float w1 = 0.f, w2 = 0.f, l = 0.f;
+                if (m != -INFINITY) {
+                    const float a = l1 * expf(m1 - m);
+                    const float c = l2 * expf(m2 - m);
+                    l = a + c;
+                    w1 = a / l;
+                    w2 = c / l;
+                }
+                w1s[e] = w1;
+                w2s[e] = w2;
+                p.mo[idx] = m;
+                p.lo[idx] = l;
+            }
+            __syncthreads();
+        }
+        #pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = base + tid + NT * u;
+            if (c < total) {
+                const float w1 = w1s[slot[u]], w2 = w2s[slot[u]];
+                if constexpr (VEC) {
+                    float f1[Vec<T>::W], f2[Vec<T>::W], y[Vec<T>::W];
+                    unpack(x1[u], f1, (T*)nullptr);
+                    unpack(x2[u], f2, (T*)nullptr);
+                    #pragma unroll
+                    for (int e = 0; e < Vec<T>::W; ++e) y[e] = __builtin_fmaf(f1[e], w1, f2[e] * w2);
+                    __builtin_nontemporal_store(pack(y, (T*)nullptr), (u32x4*)((T*)p.out + off[u]));
+                } else {
+                    ((T*)p.out)[off[u]] = (T)__builtin_fmaf(y1[u], w1, y2[u] * w2);
+                }
             }
         }
     }

@@ -187,7 +187,7 @@ miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, cons
         return dtype == MIATTN_F16 ? MIATTN_ERR_UNSUPPORTED : MIATTN_ERR_DTYPE;
     if (!layout_ok(layout)) return MIATTN_ERR_LAYOUT;
     if (B < 1 || N < 1 || S < 1 || D < 1 || N > 256 || B > 65535) return MIATTN_ERR_SHAPE;
-    if (B * N * S * D > (int64_t(1) << 40) || S > (int64_t(1) << 30) || N * D > (int64_t(1) << 30))
+    if (B * N * S * D > (int64_t(1) << 40) || S > (int64_t(1) << 30) || N * D > (int64_t(1) << 27))
         return MIATTN_ERR_SHAPE;
     const Strides s = strides_of(layout, B, N, S, D);
     MergeParams p{};

@@ -123,6 +123,7 @@ def test_attn_lse_merge_validation(mi):
     assert call(layout=4) == "MIATTN_ERR_LAYOUT"
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(N=300) == "MIATTN_ERR_SHAPE"
+    assert call(N=8, D=(1 << 24) + 8) == "MIATTN_ERR_SHAPE"   # N * D > 2^27
 
 
 def test_sparse_csr_attn_validation(mi):
