@@ -12,9 +12,11 @@
 //     VGPRs, so two waves share each SIMD and the hardware overlaps one wave's softmax
 //     (vector ALU) with the other's matrix-core work.  Waves w and w + 4 share a SIMD,
 //     which evens out the causal triangle across the four SIMDs.
-//   * Keys advance in tiles of 32.  K (row-major) and V (transposed, V^T[d][key]) tiles
-//     are staged from 128-bit global loads through registers into a 4-deep ring of LDS
-//     buffers, two tiles ahead, with one barrier per tile.
+//   * Keys advance in tiles of 64.  K (row-major) and V (transposed, V^T[d][key]) tiles
+//     are staged from 128-bit buffer loads through registers into a 4-deep ring of LDS
+//     buffers with one barrier per tile; a tile's loads are issued two steps before its
+//     LDS stores (two register sets), which covers the memory latency under load.  Every
+//     thread stages the same share of each tile, with no branch.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns ONE query column and 16 of the
 //     32 keys, so the row max / row sum are in-lane reductions plus one exchange with the
 //     lane 32 apart.
@@ -48,7 +50,7 @@ constexpr int BM = kBf16TileM;  // 256 query rows per workgroup
 #define FA_BN 64
 #endif
 #ifndef FA_PREFETCH
-#define FA_PREFETCH 2
+#define FA_PREFETCH 3
 #endif
 constexpr int BN = FA_BN;       // keys per tile
 constexpr int NKB = BN / 32;    // 32-key blocks per tile
@@ -63,17 +65,16 @@ constexpr int LDSD = FA_LDSD;   // LDS fragment reads kept in flight ahead of th
 constexpr int NT = 512;         // threads per workgroup (8 waves)
 constexpr int NBUF = 4;         // LDS ring depth (tiles)
 constexpr float kLazyThresh = 8.0f;  // log2 units
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw
 
 template <int D>
 struct Cfg {
     static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
     static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
-    static constexpr int VPER = 4;                    // V units are 4 keys x 8 dims
     static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-    static constexpr int KCHUNKS = BN * CPR;          // K chunks per tile
-    static constexpr int KPER = KCHUNKS / 256;        // per K-loading thread (threads 0..255)
-    static constexpr int SREG = KPER > 4 ? KPER : 4;  // staging registers (16 B each)
-    static constexpr int VUNITS = (BN / 4) * CPR;     // (4 keys x 8 dims) V units per tile
+    static constexpr int KPT = BN * CPR / NT;         // K chunks per thread
+    static constexpr int VUNITS = (BN / 2) * CPR;     // V units (2 keys x 8 dims) per tile
+    static constexpr int SREG = KPT + 2;              // staging registers (16 B each)
     static constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
     static constexpr int RT = D / 32;                 // 32-row output tiles over the head dim
     static constexpr int KBUF = BN * KS;
@@ -163,9 +164,6 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
     }
-    // Drain the Q loads here, so that no wait on them is left for the key loop (where it
-    // would also wait for the tile prefetches issued in the same step).
-    __builtin_amdgcn_s_waitcnt(0);
 
     f32x16 o[C::RT];
     #pragma unroll
@@ -173,75 +171,63 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
     const float cl2 = p.scale_log2;
 
-    // ---- global -> register -> LDS staging of one tile
-    //      threads 0..255 load K chunks, threads 256.. load V units (4 keys x 8 dims)
+    // ---- global -> register -> LDS staging of one tile.  Every thread takes KPT K chunks
+    //      (16 B of one key row) and one V unit (2 keys x 8 dims), so the staging work is
+    //      the same in every wave and has no branch (a branch would also make the compiler
+    //      wait for the loads where the paths join).  The loads are buffer loads whose
+    //      descriptor spans only the tile's rows inside the sequence: rows past its end
+    //      (or a whole tile past the key range) read as zero, and each thread's byte offset
+    //      inside a tile is a constant.  With fewer V units than threads, threads repeat a
+    //      unit and store identical values.
     u32x4 stA[C::SREG], stB[C::SREG];
-    const bool k_loader = tid < 256;
-    const int vuid = tid - 256;
-    const int vq = vuid % (BN / 4), vc = vuid / (BN / 4);
-    const bool v_loader = !k_loader && vuid < C::VUNITS;
-
-    // byte offsets of this thread's 16-byte chunks inside a tile whose first key is 0
-    uint32_t koff[C::KPER], voff = 0;
+    const int vu = tid % C::VUNITS;
+    const int kp = vu % (BN / 2), vc = vu / (BN / 2);
+    const int64_t krb = 2 * p.k_ss, vrb = 2 * p.v_ss;   // row strides in bytes
+    uint32_t koff[C::KPT], voff[2];
     #pragma unroll
-    for (int u = 0; u < C::KPER; ++u) {
-        const int c = tid + 256 * u;
-        koff[u] = (uint32_t)(((c / C::CPR) * p.k_ss + 8 * (c % C::CPR)) * 2);
+    for (int u = 0; u < C::KPT; ++u) {
+        const int c = tid + NT * u;
+        koff[u] = (uint32_t)((c / C::CPR) * krb + 16 * (c % C::CPR));
     }
-    if (v_loader) voff = (uint32_t)((4 * vq * p.v_ss + 8 * vc) * 2);
-    const uint32_t vrow_bytes = (uint32_t)(p.v_ss * 2);
+    #pragma unroll
+    for (int r = 0; r < 2; ++r) voff[r] = (uint32_t)((2 * kp + r) * vrb + 16 * vc);
 
+    // descriptor inputs are workgroup-uniform; readfirstlane keeps them in scalar registers
+    // (a descriptor the compiler thinks divergent would be looped over lane by lane)
+    auto rsrc = [](const void* base, int64_t bytes) {
+        const uint64_t a = (uint64_t)base;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+        const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
+    };
     auto load_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
         const int j0 = t * BN;
-        if (j0 + BN <= len_kv) {
-            if (k_loader) {
-                const char* kt = (const char*)(kg + (int64_t)j0 * p.k_ss);
-                #pragma unroll
-                for (int u = 0; u < C::KPER; ++u) stage[u] = *(const u32x4*)(kt + koff[u]);
-            } else if (v_loader) {
-                const char* vt = (const char*)(vg + (int64_t)j0 * p.v_ss);
-                #pragma unroll
-                for (int r = 0; r < 4; ++r) stage[r] = *(const u32x4*)(vt + voff + r * vrow_bytes);
-            }
-        } else {   // ragged last tile: clamp rows to the sequence
-            if (k_loader) {
-                #pragma unroll
-                for (int u = 0; u < C::KPER; ++u) {
-                    const int c = tid + 256 * u;
-                    const int row = min(j0 + c / C::CPR, len_kv - 1);
-                    stage[u] = *(const u32x4*)(kg + (int64_t)row * p.k_ss + 8 * (c % C::CPR));
-                }
-            } else if (v_loader) {
-                #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = min(j0 + 4 * vq + r, len_kv - 1);
-                    stage[r] = *(const u32x4*)(vg + (int64_t)row * p.v_ss + 8 * vc);
-                }
-            }
-        }
+        const int rows = max(0, min(BN, len_kv - j0));
+        const __amdgpu_buffer_rsrc_t rk = rsrc((const char*)kg + (int64_t)j0 * krb, rows * krb);
+        const __amdgpu_buffer_rsrc_t rv = rsrc((const char*)vg + (int64_t)j0 * vrb, rows * vrb);
+        #pragma unroll
+        for (int u = 0; u < C::KPT; ++u) stage[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0);
+        #pragma unroll
+        for (int r = 0; r < 2; ++r) stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
     };
-    auto store_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
+    auto store_tile = [&](int t, const u32x4 (&stage)[C::SREG]) {
         const int bf = t & (NBUF - 1);
         __bf16* kb = Ks + bf * C::KBUF;
-        __bf16* vb = Vt + bf * C::VBUF;
-        if (k_loader) {
-            #pragma unroll
-            for (int u = 0; u < C::KPER; ++u) {
-                const int c = tid + 256 * u;
-                *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
-            }
-        } else if (v_loader) {
-            const int pos = vt_pos(4 * vq);
-            #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u32x2 lo, hi;
-                lo[0] = (stage[0][e] & 0xffffu) | (stage[1][e] << 16);
-                lo[1] = (stage[2][e] & 0xffffu) | (stage[3][e] << 16);
-                hi[0] = (stage[0][e] >> 16) | (stage[1][e] & 0xffff0000u);
-                hi[1] = (stage[2][e] >> 16) | (stage[3][e] & 0xffff0000u);
-                *(u32x2*)(vb + (8 * vc + 2 * e) * C::VS + pos) = lo;
-                *(u32x2*)(vb + (8 * vc + 2 * e + 1) * C::VS + pos) = hi;
-            }
+        #pragma unroll
+        for (int u = 0; u < C::KPT; ++u) {
+            const int c = tid + NT * u;
+            *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
+        }
+        // dims 8 vc + e of keys 2 kp, 2 kp + 1 -> one 32-bit word of V^T row 8 vc + e
+        __bf16* vb = Vt + bf * C::VBUF + 8 * vc * C::VS + vt_pos(2 * kp);
+        const u32x4 x0 = stage[C::KPT], x1 = stage[C::KPT + 1];
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // low halves (even e) or high halves (odd e) of the two keys' words: v_perm_b32
+            // takes bytes 0-3 from its second operand and 4-7 from its first
+            const unsigned w = __builtin_amdgcn_perm(x1[e >> 1], x0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+            *(unsigned*)(vb + e * C::VS) = w;
         }
     };
 
@@ -311,17 +297,20 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
                 }
         }
         // tree reductions keep the dependent chains short
+        // four independent chains, each folding two values per step (v_max3)
         float mq[4];
         #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            mq[c] = s[0][4 * c];
+            float m = s[0][4 * c];
             #pragma unroll
-            for (int b = 0; b < NKB; ++b)
-                #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (b | i) mq[c] = fmaxf(mq[c], s[b][4 * c + i]);
+            for (int k = 1; k < 4 * NKB; k += 2) {
+                const int b0 = k / 4, i0 = k % 4, b1 = (k + 1) / 4, i1 = (k + 1) % 4;
+                m = (k + 1 < 4 * NKB) ? fmaxf(fmaxf(m, s[b0][4 * c + i0]), s[b1][4 * c + i1])
+                                      : fmaxf(m, s[b0][4 * c + i0]);
+            }
+            mq[c] = m;
         }
-        float mx = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+        float mx = pair_max(fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]));
         const float mt = mx * cl2;
         m_true = fmaxf(m_true, mt);
         const bool need = mt > m_ref + kLazyThresh;
@@ -358,23 +347,24 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     bf16x8 pp[2 * NKB];
     auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], u32x4 (&ld)[C::SREG],
                     u32x4 (&sto)[C::SREG]) {
-        if (t + PF < T1) load_tile(t + PF, ld);
+        load_tile(t + PF, ld);
         if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
         if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
         if (wave_active(t)) softmax(t, sc, pp);
-        if (t + 2 < T1) store_tile(t + 2, sto);
+        store_tile(t + 2, sto);
         __syncthreads();
     };
 
     f32x16 sa[NKB], sb[NKB];
     if (T0 < T1) {
+        // Q and the first two tiles in one memory round trip; the wait also drains Q, so
+        // no wait on it is left for the key loop (where it would also wait for prefetches)
         load_tile(T0, stA);
+        load_tile(T0 + 1, stB);
+        __builtin_amdgcn_s_waitcnt(0);
         store_tile(T0, stA);
-        if (T0 + 1 < T1) {
-            load_tile(T0 + 1, stA);
-            store_tile(T0 + 1, stA);
-        }
-        if (PF == 3 && T0 + 2 < T1) load_tile(T0 + 2, stB);
+        store_tile(T0 + 1, stB);
+        if (PF == 3) load_tile(T0 + 2, stB);
         __syncthreads();
         qk(T0, sa);
         int t = T0;
