@@ -7,6 +7,7 @@ fp32 accumulation, causal per sequence, all inputs resident in HBM before timing
 The metric counts 4 * D * Nq * (visible (query, key) pairs) flops per step.
 
 Also measured in the same run (reported under "secondary"):
+  * the same forward with fp16 storage (same lengths and draws; 2.5 PFLOP/s fp16 peak);
   * attn_lse_merge on the ring-merge workload (S 8192, N 32, D 128, SBH bf16), timed over
     rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, fp32, band 128 + 64 random).
@@ -29,7 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
@@ -163,9 +164,25 @@ def main():
                      "kernel": "fa_fwd_bf16_kernel<128>"},
     }
 
-    # ---------------- secondary: merge and sparse ----------------
+    # ---------------- secondary: fp16 forward, merge and sparse ----------------
     if not args.no_secondary:
         sec = {}
+        wh = synthetic.varlen_inputs(0, Nq, Nkv, D, "f16", B=B)   # same lengths, fp16 storage
+        hq, hk, hv = (torch.from_numpy(np.ascontiguousarray(wh[x]).view(np.float16)).to(dev)
+                      for x in ("q", "k", "v"))
+        hout = torch.empty_like(hq)
+
+        def step_f16():
+            mi.attn_fwd_varlen(hq, hk, hv, hout, smax, ssum, cu, cu, B, T, T, maxlen, maxlen, Nq,
+                               Nkv, D, "f16", scale, "causal", 0, 0, stream.cuda_stream)
+
+        hms = time_launches(step_f16, args.steps, args.warmup, stream)
+        htf = flops / (hms * 1e-3) / 1e12
+        sec["attn_fwd_varlen_f16"] = {
+            "workload": name.replace("bf16", "f16"), "ms_per_launch": round(hms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(htf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(htf / PEAK_BF16_TFLOPS, 4)}}
+        del hq, hk, hv, hout
         S, N, Dm = 8192, 32, 128
         rng = np.random.default_rng(0)
         sets = []

@@ -76,7 +76,8 @@ typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 
  *   q    [B, Nq,  Sq,  D] in `layout`;   k, v [B, Nkv, Skv, D] in `layout`;
  *   out  [B, Nq,  Sq,  D] in `layout` (same dtype as q);
  *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
- *   dtype: MIATTN_BF16 (MFMA path, fp32 accumulation, RNE output) or MIATTN_F32.
+ *   dtype: MIATTN_BF16 or MIATTN_F16 (MFMA path: fp32 accumulation, the softmax weights
+ *   rounded to the input type for the P V product, RNE output) or MIATTN_F32.
  *   D: 64 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
  *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
@@ -127,7 +128,7 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
  * computed in fp32 and rounded (RNE) to the output dtype.  If both partials are empty
  * (m = -inf) the row becomes out = 0, out_max = -inf, out_sum = 0.
  *
- *   prev_out, cur_out, out: [B, N, S, D] in `layout`, dtype `dtype` (BF16, F32);
+ *   prev_out, cur_out, out: [B, N, S, D] in `layout`, dtype `dtype` (BF16, F16, F32);
  *   prev_max, prev_sum, cur_max, cur_sum, out_max, out_sum: fp32 [B, N, S] contiguous
  *   (a packed TND batch is B = 1, S = T with layout BSND; its stats are then [N, T]).
  *   out may alias prev_out or cur_out; out_max/out_sum may alias the matching input stats

@@ -41,6 +41,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -66,6 +68,26 @@ constexpr int NT = 512;         // threads per workgroup (8 waves)
 constexpr int NBUF = 4;         // LDS ring depth (tiles)
 constexpr float kLazyThresh = 8.0f;  // log2 units
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw
+
+// Element type of the MFMA path: bf16 or fp16 inputs, outputs and probabilities; fp32
+// accumulation either way.  Conversions from fp32 round to nearest even.
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    __device__ static f32x16 mfma(const v8& a, const v8& b, const f32x16& c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Elem<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    __device__ static f32x16 mfma(const v8& a, const v8& b, const f32x16& c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 template <int D>
 struct Cfg {
@@ -98,10 +120,12 @@ __device__ inline float pair_sum(float x)
 // the key order of the P operand taken from the S^T accumulator layout.
 __device__ inline int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D>;
+    using X8 = typename Elem<T>::v8;   // one MFMA operand: 8 elements
+    using X4 = typename Elem<T>::v4;
     __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF * C::KBUF];
     __shared__ __attribute__((aligned(16))) __bf16 Vt[NBUF * C::VBUF];
 
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     const __bf16* qg = (const __bf16*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
     const __bf16* kg = (const __bf16*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
     const __bf16* vg = (const __bf16*)p.v + (int64_t)tc.b * p.v_sb + tc.kv0 * p.v_ss + (int64_t)tc.kvh * p.v_sh;
-    __bf16* og = (__bf16*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
+    T* og = (T*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
     const int64_t st_base = (int64_t)tc.b * p.st_sb + (int64_t)tc.h * p.st_sh + tc.q0;
 
     // ---- key tiles of the workgroup
@@ -157,12 +181,12 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     auto wave_active = [&](int t) { return t >= w_lo && t < w_hi; };
 
     // ---- Q fragment: B operand of S^T = K Q^T; lane (lq, hf) holds d = 16kk + 8hf + 0..7
-    bf16x8 qf[C::KK];
+    X8 qf[C::KK];
     {
         const int qi = min(rb + lq, len_q - 1);
         const __bf16* qrow = qg + (int64_t)qi * p.q_ss + 8 * hf;
         #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
+        for (int kk = 0; kk < C::KK; ++kk) qf[kk] = *(const X8*)(qrow + 16 * kk);
     }
 
     f32x16 o[C::RT];
@@ -235,17 +259,17 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     auto qk = [&](int t, f32x16 (&s)[NKB]) {
         const __bf16* kb = Ks + (t & (NBUF - 1)) * C::KBUF + lq * C::KS + 8 * hf;
         constexpr int NF = C::KK * NKB;   // fragments (= MFMAs), fragment f: kk = f / NKB, b = f % NKB
-        bf16x8 a[NF];
+        X8 a[NF];
         #pragma unroll
         for (int b = 0; b < NKB; ++b) s[b] = f32x16{};
         #pragma unroll
         for (int f = 0; f < LDSD && f < NF; ++f)
-            a[f] = *(const bf16x8*)(kb + 32 * (f % NKB) * C::KS + 16 * (f / NKB));
+            a[f] = *(const X8*)(kb + 32 * (f % NKB) * C::KS + 16 * (f / NKB));
         #pragma unroll
         for (int f = 0; f < NF; ++f) {
             if (f + LDSD < NF)
-                a[f + LDSD] = *(const bf16x8*)(kb + 32 * ((f + LDSD) % NKB) * C::KS + 16 * ((f + LDSD) / NKB));
-            s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], qf[f / NKB], s[f % NKB], 0, 0, 0);
+                a[f + LDSD] = *(const X8*)(kb + 32 * ((f + LDSD) % NKB) * C::KS + 16 * ((f + LDSD) / NKB));
+            s[f % NKB] = Elem<T>::mfma(a[f], qf[f / NKB], s[f % NKB]);
         }
 #if FA_SCHED
         // keep LDSD reads in flight ahead of the MFMAs that consume them
@@ -260,18 +284,18 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     };
 
     // ---- O^T += V^T P^T for tile t
-    auto pv = [&](int t, const bf16x8 (&pp)[2 * NKB]) {
+    auto pv = [&](int t, const X8 (&pp)[2 * NKB]) {
         const __bf16* vb = Vt + (t & (NBUF - 1)) * C::VBUF + lq * C::VS + 8 * hf;
         constexpr int NF = C::RT * 2 * NKB;   // fragment f: r = f / (2 NKB), j = f % (2 NKB)
-        bf16x8 a[NF];
+        X8 a[NF];
         #pragma unroll
         for (int f = 0; f < LDSD && f < NF; ++f)
-            a[f] = *(const bf16x8*)(vb + 32 * (f / (2 * NKB)) * C::VS + 16 * (f % (2 * NKB)));
+            a[f] = *(const X8*)(vb + 32 * (f / (2 * NKB)) * C::VS + 16 * (f % (2 * NKB)));
         #pragma unroll
         for (int f = 0; f < NF; ++f) {
             if (f + LDSD < NF)
-                a[f + LDSD] = *(const bf16x8*)(vb + 32 * ((f + LDSD) / (2 * NKB)) * C::VS + 16 * ((f + LDSD) % (2 * NKB)));
-            o[f / (2 * NKB)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], pp[f % (2 * NKB)], o[f / (2 * NKB)], 0, 0, 0);
+                a[f + LDSD] = *(const X8*)(vb + 32 * ((f + LDSD) / (2 * NKB)) * C::VS + 16 * ((f + LDSD) % (2 * NKB)));
+            o[f / (2 * NKB)] = Elem<T>::mfma(a[f], pp[f % (2 * NKB)], o[f / (2 * NKB)]);
         }
 #if FA_SCHED
         __builtin_amdgcn_sched_group_barrier(0x100, LDSD, 0);
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     };
 
     // ---- online softmax of tile t; leaves bf16 probabilities in pp
-    auto softmax = [&](int t, f32x16 (&s)[NKB], bf16x8 (&pp)[2 * NKB]) {
+    auto softmax = [&](int t, f32x16 (&s)[NKB], X8 (&pp)[2 * NKB]) {
         const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
@@ -339,12 +363,12 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         #pragma unroll
         for (int j = 0; j < 2 * NKB; ++j)
             #pragma unroll
-            for (int e = 0; e < 8; ++e) pp[j][e] = (__bf16)s[j >> 1][8 * (j & 1) + e];
+            for (int e = 0; e < 8; ++e) pp[j][e] = (T)s[j >> 1][8 * (j & 1) + e];
     };
 
     // Iteration t: prefetch tile t+PF into registers; S(t+1) = K Q^T and O += P(t-1) V(t-1)
     // on the matrix cores; softmax(t) on the vector ALUs; land tile t+2 in LDS.
-    bf16x8 pp[2 * NKB];
+    X8 pp[2 * NKB];
     auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], u32x4 (&ld)[C::SREG],
                     u32x4 (&sto)[C::SREG]) {
         load_tile(t + PF, ld);
@@ -383,15 +407,15 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int qi = rb + lq;
     if (qi < re) {
-        __bf16* orow = og + (int64_t)qi * p.o_ss + 4 * hf;
+        T* orow = og + (int64_t)qi * p.o_ss + 4 * hf;
         #pragma unroll
         for (int r = 0; r < C::RT; ++r)
             #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 w;
+                X4 w;
                 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][4 * g4 + e] * inv);
-                *(bf16x4*)(orow + 32 * r + 8 * g4) = w;
+                for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * inv);
+                *(X4*)(orow + 32 * r + 8 * g4) = w;
             }
         if (hf == 0) {
             const bool any = lt > 0.f;
@@ -403,13 +427,17 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 
 }  // namespace
 
-hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, hipStream_t stream)
+hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(NT);
-    if (D == 64)
-        hipLaunchKernelGGL(fa_fwd_bf16_kernel<64>, grid, block, 0, stream, p);
+    if (D == 64 && !f16)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, __bf16>), grid, block, 0, stream, p);
+    else if (D == 128 && !f16)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, __bf16>), grid, block, 0, stream, p);
+    else if (D == 64)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, _Float16>), grid, block, 0, stream, p);
     else if (D == 128)
-        hipLaunchKernelGGL(fa_fwd_bf16_kernel<128>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, _Float16>), grid, block, 0, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -58,7 +58,8 @@ struct SparseParams {
 };
 
 // Launchers (defined next to their kernels).  Each returns the launch status.
-hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, hipStream_t stream);
+// the MFMA forward for bf16 (f16 = false) or fp16 (f16 = true) inputs
+hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
 hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_sparse_csr(const SparseParams& p, int D, hipStream_t stream);

@@ -27,6 +27,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T> struct Vec;
 template <> struct Vec<__bf16> { static constexpr int W = 8; };
+template <> struct Vec<_Float16> { static constexpr int W = 8; };
 template <> struct Vec<float> { static constexpr int W = 4; };
 
 __device__ inline void unpack(const u32x4& x, float* f, __bf16*)
@@ -35,6 +36,14 @@ __device__ inline void unpack(const u32x4& x, float* f, __bf16*)
     for (int e = 0; e < 4; ++e) {
         f[2 * e] = __uint_as_float(x[e] << 16);
         f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+    }
+}
+__device__ inline void unpack(const u32x4& x, float* f, _Float16*)
+{
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = (float)__builtin_bit_cast(_Float16, (unsigned short)(x[e] & 0xffffu));
+        f[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(x[e] >> 16));
     }
 }
 __device__ inline void unpack(const u32x4& x, float* f, float*)
@@ -48,6 +57,17 @@ __device__ inline u32x4 pack(const float* f, __bf16*)
     #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const __bf16 a = (__bf16)f[2 * e], b = (__bf16)f[2 * e + 1];
+        r[e] = (unsigned)__builtin_bit_cast(unsigned short, a) |
+               ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    }
+    return r;
+}
+__device__ inline u32x4 pack(const float* f, _Float16*)
+{
+    u32x4 r;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const _Float16 a = (_Float16)f[2 * e], b = (_Float16)f[2 * e + 1];
         r[e] = (unsigned)__builtin_bit_cast(unsigned short, a) |
                ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
     }
@@ -164,10 +184,11 @@ hipError_t launch_t(const MergeParams& p, hipStream_t stream)
 
 }  // namespace
 
-// dtype: 0 = fp32, 1 = bf16 (the C-ABI enum values)
+// dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the C-ABI enum values)
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream)
 {
     if (dtype == 1) return launch_t<__bf16>(p, stream);
+    if (dtype == 2) return launch_t<_Float16>(p, stream);
     if (dtype == 0) return launch_t<float>(p, stream);
     return hipErrorInvalidValue;
 }

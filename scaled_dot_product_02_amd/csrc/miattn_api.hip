@@ -48,8 +48,7 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 miattn_status_t check_dtype_fa(int dtype)
 {
-    if (dtype == MIATTN_F32 || dtype == MIATTN_BF16) return MIATTN_OK;
-    if (dtype == MIATTN_F16) return MIATTN_ERR_UNSUPPORTED;
+    if (dtype == MIATTN_F32 || dtype == MIATTN_BF16 || dtype == MIATTN_F16) return MIATTN_OK;
     return MIATTN_ERR_DTYPE;
 }
 
@@ -68,11 +67,12 @@ miattn_status_t size_grid(FaParams& p, int64_t max_len_q, int tile_m)
 
 miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
 {
-    const int tile_m = dtype == MIATTN_BF16 ? kBf16TileM : kF32TileM;
+    const bool mfma = dtype == MIATTN_BF16 || dtype == MIATTN_F16;
+    const int tile_m = mfma ? kBf16TileM : kF32TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
-    hipError_t e = dtype == MIATTN_BF16 ? launch_fa_fwd_bf16(p, (int)D, stream)
-                                        : launch_fa_fwd_f32(p, (int)D, stream);
+    hipError_t e = mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
+                        : launch_fa_fwd_f32(p, (int)D, stream);
     return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 
@@ -115,7 +115,6 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
     st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
     if (st != MIATTN_OK) return st;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (check_dtype_fa(dtype) != MIATTN_OK) return MIATTN_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
@@ -156,7 +155,6 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
     st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
     if (st != MIATTN_OK) return st;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (check_dtype_fa(dtype) != MIATTN_OK) return MIATTN_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
@@ -183,8 +181,7 @@ miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, cons
     if (!prev_out || !prev_max || !prev_sum || !cur_out || !cur_max || !cur_sum || !out ||
         !out_max || !out_sum)
         return MIATTN_ERR_NULL;
-    if (dtype != MIATTN_F32 && dtype != MIATTN_BF16)
-        return dtype == MIATTN_F16 ? MIATTN_ERR_UNSUPPORTED : MIATTN_ERR_DTYPE;
+    if (dtype != MIATTN_F32 && dtype != MIATTN_BF16 && dtype != MIATTN_F16) return MIATTN_ERR_DTYPE;
     if (!layout_ok(layout)) return MIATTN_ERR_LAYOUT;
     if (B < 1 || N < 1 || S < 1 || D < 1 || N > 256 || B > 65535) return MIATTN_ERR_SHAPE;
     if (B * N * S * D > (int64_t(1) << 40) || S > (int64_t(1) << 30) || N * D > (int64_t(1) << 27))

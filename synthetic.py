@@ -2,7 +2,7 @@
 
 This module draws random numbers and lays them out; it holds none of the attention
 arithmetic.  Both the HIP path and the CPU oracle receive exactly the values produced
-here (for bf16 the oracle receives the exact widening of the stored bf16 bytes).
+here (for bf16 and fp16 the oracle receives the exact widening of the stored 2-byte values).
 
 Recipe (one fresh ``numpy.random.default_rng(seed)`` per workload, seed 0 unless a test
 says otherwise; draws in this fixed order):
@@ -11,7 +11,7 @@ says otherwise; draws in this fixed order):
 2. Q, K, V: ``rng.standard_normal(shape, dtype=float32)`` each, in the storage layout;
 3. CSR columns (sparse workloads only), per (b, n) b-major, per row i ascending.
 
-bf16 storage is produced by round-to-nearest-even from those float32 draws.
+bf16 and fp16 storage are produced by round-to-nearest-even from those float32 draws.
 """
 from __future__ import annotations
 
@@ -37,20 +37,39 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's cast rounds to nearest, ties to even);
+    return uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f32_from_f16_bits(b: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 def storage_values(arr: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 values of a stored tensor (float32 array or bf16 bit patterns)."""
+    """float64 values of a stored tensor (float32 array, or bf16 / fp16 bit patterns)."""
     if dtype == "bf16":
         return f32_from_bf16_bits(arr).astype(np.float64)
+    if dtype == "f16":
+        return f32_from_f16_bits(arr).astype(np.float64)
     return np.asarray(arr, dtype=np.float64)
 
 
-def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in the storage form of `dtype` (bits for the 2-byte types)."""
     if dtype == "bf16":
         return bf16_bits_from_f32(x)
+    if dtype == "f16":
+        return f16_bits_from_f32(x)
     if dtype == "f32":
-        return x
+        return np.ascontiguousarray(x, dtype=np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
 
 
 # ----------------------------------------------------------------------------------------

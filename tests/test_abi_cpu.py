@@ -59,7 +59,7 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, q=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, out=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, dtype=9) == "MIATTN_ERR_DTYPE"
-    assert _fwd(mi, dtype="f16") == "MIATTN_ERR_UNSUPPORTED"
+    assert _fwd(mi, dtype="f16", D=96) == "MIATTN_ERR_UNSUPPORTED"   # fp16 takes D 64/128 too
     assert _fwd(mi, layout=7) == "MIATTN_ERR_LAYOUT"
     assert _fwd(mi, B=0) == "MIATTN_ERR_SHAPE"
     assert _fwd(mi, Sq=0) == "MIATTN_ERR_SHAPE"
@@ -119,7 +119,6 @@ def test_attn_lse_merge_validation(mi):
     for i in range(9):
         assert call(null=i) == "MIATTN_ERR_NULL"
     assert call(dtype=5) == "MIATTN_ERR_DTYPE"
-    assert call(dtype="f16") == "MIATTN_ERR_UNSUPPORTED"
     assert call(layout=4) == "MIATTN_ERR_LAYOUT"
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(N=300) == "MIATTN_ERR_SHAPE"

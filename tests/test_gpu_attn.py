@@ -63,7 +63,7 @@ def test_dense_bf16_b8n8s128d64(mi):
     _compare_dense(mi, w, 1 / math.sqrt(64), "none")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("layout", ["BNSD", "BSND", "BSH", "SBH"])
 @pytest.mark.parametrize("mask,pre,nxt", [("none", 0, 0), ("causal", 0, 0), ("band", 70, 33),
@@ -102,7 +102,7 @@ def _run_varlen(mi, w, scale, mask, pre=0, nxt=0):
 
 
 @pytest.mark.parametrize("mask,pre,nxt", [("causal", 0, 0), ("none", 0, 0), ("band", 200, 7)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_varlen_small(mi, mask, pre, nxt, dtype):
     lengths = [300, 0, 1, 129, 64, 517, 2]   # zero-length, single-row and ragged sequences
     w = synthetic.varlen_inputs(21, Nq=8, Nkv=2, D=128, dtype=dtype, lengths_q=lengths)
@@ -148,6 +148,22 @@ def test_varlen_full_workload_sampled(metric_run, seqs, heads):
             wo, wm, wl = oracle.attn(qh, kh, vh, 1 / math.sqrt(128), "causal")
             check_out(go[sl, h], wo[0, 0], "bf16", f"seq {b} head {h}")
             check_stats(gm[h, sl], gl[h, sl], wm[0, 0], wl[0, 0])
+
+
+def test_varlen_full_workload_f16_sampled(mi):
+    """The full packed workload's shape and lengths (same seed) with fp16 storage, sampled
+    whole sequences x heads against the oracle."""
+    w = synthetic.varlen_inputs(0, Nq=32, Nkv=8, D=128, dtype="f16", B=16)
+    assert w["Tq"] == synthetic.make(synthetic.METRIC_WORKLOAD)["Tq"]
+    go, gm, gl = _run_varlen(mi, w, 1 / math.sqrt(128), "causal")
+    cu = np.concatenate([[0], w["cu_q"]])
+    q, k, v = (synthetic.storage_values(w[x], "f16") for x in ("q", "k", "v"))
+    for b, h in [(14, 0), (14, 31), (0, 8), (9, 17)]:
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        wo, wm, wl = oracle.attn(q[sl, h][None, None], k[sl, h // 4][None, None],
+                                 v[sl, h // 4][None, None], 1 / math.sqrt(128), "causal")
+        check_out(go[sl, h], wo[0, 0], "f16", f"seq {b} head {h}")
+        check_stats(gm[h, sl], gl[h, sl], wm[0, 0], wl[0, 0])
 
 
 def test_varlen_full_workload_properties(metric_run):

@@ -44,8 +44,7 @@ def _partials(seed, B, N, S, D, dtype, layout, sums="positive", empty_frac=0.0):
         e2 = rng.random((B, N, S)) < empty_frac
         m1[e1], l1[e1] = -np.inf, 0.0
         m2[e2], l2[e2] = -np.inf, 0.0
-    if dtype == "bf16":
-        o1, o2 = synthetic.bf16_bits_from_f32(o1), synthetic.bf16_bits_from_f32(o2)
+    o1, o2 = synthetic.to_storage(o1, dtype), synthetic.to_storage(o2, dtype)
     return o1, m1, l1, o2, m2, l2
 
 
@@ -69,7 +68,7 @@ def _merge_oracle(parts, N, dtype, layout):
 
 
 @pytest.mark.parametrize("layout", ["SBH", "BNSD", "BSND"])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [128, 64, 1, 12])
 def test_merge_random_partials(mi, layout, dtype, D):
     B, N, S = 2, 4, 333

@@ -24,6 +24,21 @@ def test_bf16_round_to_nearest_even():
     assert np.array_equal(synthetic.bf16_bits_from_f32(back), b)
 
 
+def test_f16_round_to_nearest_even():
+    ulp = 2.0 ** -10                      # binary16 spacing at 1.0
+    x = np.array([1.0 + 2.0 ** -11,       # tie -> even (1.0)
+                  1.0 + 3 * 2.0 ** -11,   # tie between 1+ulp (odd) and 1+2ulp (even) -> up
+                  1.0 + 2.0 ** -11 + 2.0 ** -20,
+                  -2.5, 65504.0, 2.0 ** -24], dtype=np.float32)
+    b = synthetic.f16_bits_from_f32(x)
+    assert b.dtype == np.uint16
+    assert b[3] == 0xC100 and b[4] == 0x7BFF and b[5] == 0x0001   # -2.5, max normal, min subnormal
+    back = synthetic.f32_from_f16_bits(b)
+    assert back.tolist() == [1.0, 1.0 + 2 * ulp, 1.0 + ulp, -2.5, 65504.0, 2.0 ** -24]
+    assert np.array_equal(synthetic.storage_values(b, "f16"), back.astype(np.float64))
+    assert np.array_equal(synthetic.f16_bits_from_f32(back), b)
+
+
 def test_seeded_lengths_of_the_packed_workload():
     w = synthetic.WORKLOADS[synthetic.METRIC_WORKLOAD]
     rng = np.random.default_rng(0)
