@@ -10,6 +10,8 @@ Also measured in the same run (reported under "secondary"):
   * the same forward with fp16 storage (same lengths and draws; 2.5 PFLOP/s fp16 peak);
   * attn_lse_merge on the ring-merge workload (S 8192, N 32, D 128, SBH bf16), timed over
     rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
+  * causal attention over that workload's 4 key chunks of 2048 (a ring on one GPU): the
+    fused attn_fwd_update chain vs attn_fwd + attn_lse_merge, and one full forward;
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, fp32, band 128 + 64 random).
 
 cpu_baseline: the CPU fp64 oracle (untuned) on a bounded sample of the same workload
@@ -76,8 +78,8 @@ def time_launches(fn, steps: int, warmup: int, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads in the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-secondary", action="store_true",
@@ -205,6 +207,51 @@ def main():
             mi.attn_lse_merge(*s_, 1, N, S, Dm, "bf16", "SBH", stream.cuda_stream)
 
         mms = time_launches(merge_step, 4 * 25, 8, stream)
+
+        # causal ring over 4 key chunks of the same workload: fused update vs
+        # forward + merge kernel, and the single full forward for reference
+        qr, kr, vr = sets[0][0], sets[1][0], sets[2][0]
+        C, nch = S // 4, 4
+        run_o, run_m, run_l = sets[3][6], sets[3][7], sets[3][8]
+        part_o, part_m, part_l = sets[3][0], sets[3][1], sets[3][2]
+        sc = 1.0 / math.sqrt(Dm)
+
+        def ring_fused():
+            for j in range(nch):
+                kj, vj = kr[j * C:(j + 1) * C], vr[j * C:(j + 1) * C]
+                if j == 0:
+                    mi.attn_fwd(qr, kj, vj, run_o, run_m, run_l, 1, N, N, S, C, Dm, "bf16", "SBH",
+                                sc, "causal", 0, 0, stream.cuda_stream)
+                else:
+                    mi.attn_fwd_update(qr, kj, vj, run_o, run_m, run_l, run_o, run_m, run_l, 1, N, N,
+                                       S, C, Dm, "bf16", "SBH", sc, "band", 1 << 40, -j * C,
+                                       stream.cuda_stream)
+
+        def ring_unfused():
+            for j in range(nch):
+                kj, vj = kr[j * C:(j + 1) * C], vr[j * C:(j + 1) * C]
+                if j == 0:
+                    mi.attn_fwd(qr, kj, vj, run_o, run_m, run_l, 1, N, N, S, C, Dm, "bf16", "SBH",
+                                sc, "causal", 0, 0, stream.cuda_stream)
+                else:
+                    mi.attn_fwd(qr, kj, vj, part_o, part_m, part_l, 1, N, N, S, C, Dm, "bf16",
+                                "SBH", sc, "band", 1 << 40, -j * C, stream.cuda_stream)
+                    mi.attn_lse_merge(run_o, run_m, run_l, part_o, part_m, part_l, run_o, run_m,
+                                      run_l, 1, N, S, Dm, "bf16", "SBH", stream.cuda_stream)
+
+        def full_causal():
+            mi.attn_fwd(qr, kr, vr, run_o, run_m, run_l, 1, N, N, S, S, Dm, "bf16", "SBH", sc,
+                        "causal", 0, 0, stream.cuda_stream)
+
+        ring_flops = 4.0 * Dm * N * (S * (S + 1) // 2)
+        ring = {"workload": "causal_ring_4chunks_sbh_bf16_s8192_n32_d128",
+                "flop_per_pass": ring_flops}
+        for key, fn in (("fused_update", ring_fused), ("forward_plus_merge", ring_unfused),
+                        ("single_full_forward", full_causal)):
+            rms = time_launches(fn, 20, 3, stream)
+            ring[key] = {"ms_per_pass": round(rms, 4),
+                         "tflops": round(ring_flops / (rms * 1e-3) / 1e12, 2)}
+        sec["causal_ring_4_chunks"] = ring
         mbytes = 3 * S * N * Dm * 2 + 6 * N * S * 4
         mgbs = mbytes / (mms * 1e-3) / 1e9
         sec["attn_lse_merge"] = {

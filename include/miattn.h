@@ -143,6 +143,57 @@ miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, cons
                                miattn_dtype_t dtype, miattn_layout_t layout, void* stream);
 
 /*
+ * attn_fwd_update - attention of q over ONE chunk of keys, merged into a running result
+ * in the same launch: the forward of attn_fwd followed by the ring-attention update of
+ * attn_lse_merge ("npu_ring_attention_update对外接口"), with the chunk's partial result kept
+ * in fp32 registers instead of being stored, re-read and rounded in between.  With
+ * m_c, l_c, o_c the chunk's softmax max, sum and normalized output (attn_fwd's outputs):
+ *   m = max(prev_max, m_c),  a = prev_sum * exp(prev_max - m),  c = l_c * exp(m_c - m),
+ *   out = prev_out * a / (a + c) + o_c * c / (a + c),  out_max = m,  out_sum = a + c,
+ * rounded once (RNE) to the dtype.  Calling it once per key chunk, with the chunk's band
+ * offset in pre/next (e.g. causal over keys [j0, j0 + Skv): MIATTN_MASK_BAND with
+ * pre_tokens = 2^40, next_tokens = -j0), accumulates attention over all the chunks.
+ * A row that sees no key of this chunk keeps the prior bit for bit, given that a
+ * non-empty prior row has prev_sum > 0 (as every attention output has); an empty prior
+ * row (prev_max = -inf, prev_sum = 0) gives attn_fwd's result, and its prev_out is not
+ * read (it may hold anything, e.g. an uninitialized buffer before the first chunk).
+ *
+ *   q, k, v, layout, sizes, dtype, scale, mask, pre/next: as for attn_fwd;
+ *   prev_out, out: [B, Nq, Sq, D] in `layout`, dtype `dtype`;
+ *   prev_max, prev_sum, out_max, out_sum: fp32 [B, Nq, Sq] contiguous (none may be NULL).
+ *   out may alias prev_out and out_max / out_sum may alias prev_max / prev_sum (each
+ *   element is read and then written by the same thread), which is the usual in-place
+ *   accumulation.  Returns as attn_fwd (MIATTN_ERR_NULL for a NULL prior or statistics).
+ */
+miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
+                                const void* prev_out, const float* prev_max, const float* prev_sum,
+                                void* out, float* out_max, float* out_sum,
+                                int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                void* stream);
+
+/*
+ * attn_fwd_varlen_update - attn_fwd_update over a packed (TND) batch: the key chunk of
+ * sequence b is rows [cu_seqlens_kv[b-1], cu_seqlens_kv[b]) of k / v (a chunk packed
+ * with its own cumulative lengths, as one ring step holds it); the running result is
+ * [Tq, Nq, D] with statistics [Nq, Tq] (the TND form of the ring update, with
+ * actual_seq_qlen given by cu_seqlens_q).  Arguments and limits as attn_fwd_varlen, plus
+ * the prior and aliasing rules of attn_fwd_update.
+ */
+miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void* v,
+                                       const void* prev_out, const float* prev_max,
+                                       const float* prev_sum, void* out, float* out_max,
+                                       float* out_sum,
+                                       const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                       int64_t B, int64_t Tq, int64_t Tkv,
+                                       int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       miattn_dtype_t dtype, float scale,
+                                       miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                       void* stream);
+
+/*
  * sparse_csr_attn - CSR-sparse attention (Paddle "sparse_attention": formula, parameters
  * and code example): row i of slice (b, n) attends only to the key rows listed in
  * csr_columns[b][n][csr_offset[b][n][i] .. csr_offset[b][n][i+1]) of the same slice,

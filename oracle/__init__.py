@@ -124,6 +124,26 @@ def merge(o1, m1, l1, o2, m2, l2, threads: int = 0):
     return out, mo, lo
 
 
+def attn_update(q, k, v, prev_out, prev_max, prev_sum, scale: float, mask: str = "none",
+                pre: int = 0, next: int = 0, threads: int = 0):
+    """Attention of q over one key chunk, merged into a running result: the ring-attention
+    update ("npu_ring_attention_update对外接口", equivalent small-operator logic) of
+    (prev_out, prev_max, prev_sum) with attn(q, k, v).  Shapes as attn / merge."""
+    o, m, l = attn(q, k, v, scale, mask, pre, next, threads)
+    return merge(prev_out, prev_max, prev_sum, o, m, l, threads)
+
+
+def attn_varlen_update(q, k, v, prev_out, prev_max, prev_sum, cu_q, cu_kv, scale: float,
+                       mask: str = "none", pre: int = 0, next: int = 0, threads: int = 0):
+    """attn_update over a packed batch: out (Tq,Nq,D), stats (Nq,Tq) as attn_varlen."""
+    o, m, l = attn_varlen(q, k, v, cu_q, cu_kv, scale, mask, pre, next, threads)
+    # the packed result is the dense (1, Nq, Tq, D) view for the elementwise merge
+    bnsd = lambda x: np.ascontiguousarray(_f64(x).transpose(1, 0, 2))[None]
+    out, mo, lo = merge(bnsd(prev_out), _f64(prev_max)[None], _f64(prev_sum)[None],
+                        bnsd(o), m[None], l[None], threads)
+    return np.ascontiguousarray(out[0].transpose(1, 0, 2)), mo[0], lo[0]
+
+
 def sparse(q, k, v, offset, columns, scale: float, threads: int = 0):
     """CSR-sparse attention.  q/k/v (B,N,S,D), offset int32 (B,N,S+1), columns int32
     (B,N,nnz) -> out (B,N,S,D), softmax_max (B,N,S), softmax_sum (B,N,S)."""

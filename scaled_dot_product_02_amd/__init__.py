@@ -29,7 +29,8 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2}
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_lse_merge", "sparse_csr_attn", "miattn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
+           "attn_lse_merge", "sparse_csr_attn", "miattn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -41,9 +42,12 @@ class MiattnError(RuntimeError):
 _P, _I64, _E, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 _lib.attn_fwd.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_varlen.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
+_lib.attn_fwd_update.argtypes = [_P] * 9 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
+_lib.attn_fwd_varlen_update.argtypes = [_P] * 11 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
-for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_lse_merge, _lib.sparse_csr_attn):
+for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
+           _lib.attn_lse_merge, _lib.sparse_csr_attn):
     _f.restype = ctypes.c_int
 _lib.miattn_status_str.argtypes = [ctypes.c_int]
 _lib.miattn_status_str.restype = ctypes.c_char_p
@@ -97,6 +101,29 @@ def attn_fwd_varlen(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seq
                                 B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
                                 _enum(dtype, DTYPES), scale, _enum(mask, MASKS), pre_tokens,
                                 next_tokens, _stream(stream)), "attn_fwd_varlen")
+
+
+def attn_fwd_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
+                    B, Nq, Nkv, Sq, Skv, D, dtype, layout, scale, mask, pre_tokens=0,
+                    next_tokens=0, stream=None):
+    _check(_lib.attn_fwd_update(_ptr(q), _ptr(k), _ptr(v), _ptr(prev_out), _ptr(prev_max),
+                                _ptr(prev_sum), _ptr(out), _ptr(out_max), _ptr(out_sum),
+                                B, Nq, Nkv, Sq, Skv, D, _enum(dtype, DTYPES),
+                                _enum(layout, LAYOUTS), scale, _enum(mask, MASKS), pre_tokens,
+                                next_tokens, _stream(stream)), "attn_fwd_update")
+
+
+def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
+                           cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q,
+                           max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask, pre_tokens=0,
+                           next_tokens=0, stream=None):
+    _check(_lib.attn_fwd_varlen_update(_ptr(q), _ptr(k), _ptr(v), _ptr(prev_out),
+                                       _ptr(prev_max), _ptr(prev_sum), _ptr(out), _ptr(out_max),
+                                       _ptr(out_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+                                       B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
+                                       _enum(dtype, DTYPES), scale, _enum(mask, MASKS),
+                                       pre_tokens, next_tokens, _stream(stream)),
+           "attn_fwd_varlen_update")
 
 
 def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, out_max,

@@ -120,7 +120,8 @@ __device__ inline float pair_sum(float x)
 // the key order of the P operand taken from the S^T accumulator layout.
 __device__ inline int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <int D, typename T>
+// UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
+template <int D, typename T, bool UPDATE>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D>;
@@ -153,6 +154,22 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     key_range(p, i0, i1, len_kv, kv_lo, kv_hi);
     const int T0 = kv_lo / BN;
     const int T1 = kv_lo < kv_hi ? (kv_hi + BN - 1) / BN : T0;
+    if constexpr (UPDATE) {
+        if (T0 >= T1 && p.out == p.prev_out && p.smax == p.prev_max && p.ssum == p.prev_sum) {
+            // An in-place update by a key chunk that no row of this tile sees: every row
+            // keeps its value (the update leaves a non-empty prior unchanged), except that a
+            // row with an empty prior takes the empty result (out 0, sum 0).
+            for (int r = tid; r < i1 - i0; r += NT) {
+                const int64_t si = st_base + i0 + r;
+                if (p.prev_max[si] == -INFINITY) {
+                    p.ssum[si] = 0.f;
+                    T* orow = og + (int64_t)(i0 + r) * p.o_ss;
+                    for (int d = 0; d < D; d += 4) *(X4*)(orow + d) = X4{};
+                }
+            }
+            return;
+        }
+    }
 
     // ---- this wave's rows [rb, re): active tiles, unmasked tiles, per-lane key bounds
     const int rb = i0 + 32 * wave;
@@ -402,45 +419,81 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         if (wave_active(T1 - 1)) pv(T1 - 1, pp);
     }
 
-    // ---- epilogue: normalize, round to bf16, store; emit the row statistics
+    // ---- epilogue: normalize, round to the storage type, store; emit the row statistics.
+    //      This partial is O / lt with max mc = m_true ln 2 and sum l_c = lt 2^(m_ref - m_true).
+    //      With UPDATE it is merged into the prior (o_p, m_p, l_p) as the ring-attention
+    //      update does: m = max(m_p, mc), a = l_p e^(m_p - m), c = l_c e^(mc - m),
+    //      out = o_p a / (a + c) + (O / lt) c / (a + c), before the single rounding.
     const float lt = pair_sum(l_run);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int qi = rb + lq;
     if (qi < re) {
+        const bool any = lt > 0.f;
+        const float mc = any ? m_true * 0.69314718055994530942f : -INFINITY;
+        float m_out = mc;
+        float l_out = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
+        float wc = any ? 1.f / lt : 0.f;   // weight of the accumulator O
+        float wp = 0.f;                    // weight of the prior output
+        if constexpr (UPDATE) {
+            const float mp = p.prev_max[st_base + qi], lp = p.prev_sum[st_base + qi];
+            const float m = fmaxf(mp, mc);
+            wc = 0.f;
+            l_out = 0.f;
+            if (m != -INFINITY) {
+                const float a = lp * __builtin_amdgcn_exp2f((mp - m) * 1.4426950408889634f);
+                const float f = any ? __builtin_amdgcn_exp2f(m_ref - m * 1.4426950408889634f) : 0.f;
+                l_out = a + lt * f;
+                wp = a / l_out;
+                wc = f / l_out;
+            }
+            m_out = m;
+        }
         T* orow = og + (int64_t)qi * p.o_ss + 4 * hf;
         #pragma unroll
         for (int r = 0; r < C::RT; ++r)
             #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 X4 w;
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * inv);
+                if constexpr (UPDATE) {
+                    // an empty prior (weight 0) is not read: its buffer may hold anything
+                    const T* prow = (const T*)p.prev_out + (orow - (T*)p.out);
+                    X4 po{};
+                    if (wp != 0.f) po = *(const X4*)(prow + 32 * r + 8 * g4);
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (T)__builtin_fmaf((float)po[e], wp, o[r][4 * g4 + e] * wc);
+                } else {
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * wc);
+                }
                 *(X4*)(orow + 32 * r + 8 * g4) = w;
             }
         if (hf == 0) {
-            const bool any = lt > 0.f;
-            if (p.smax) p.smax[st_base + qi] = any ? m_true * 0.69314718055994530942f : -INFINITY;
-            if (p.ssum) p.ssum[st_base + qi] = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
+            if (p.smax) p.smax[st_base + qi] = m_out;
+            if (p.ssum) p.ssum[st_base + qi] = l_out;
         }
     }
+}
+
+template <typename T, bool UPDATE>
+hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
+{
+    dim3 grid(p.n_slots), block(NT);
+    if (D == 64)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE>), grid, block, 0, stream, p);
+    else if (D == 128)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE>), grid, block, 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream)
 {
-    dim3 grid(p.n_slots), block(NT);
-    if (D == 64 && !f16)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, __bf16>), grid, block, 0, stream, p);
-    else if (D == 128 && !f16)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, __bf16>), grid, block, 0, stream, p);
-    else if (D == 64)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, _Float16>), grid, block, 0, stream, p);
-    else if (D == 128)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, _Float16>), grid, block, 0, stream, p);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    const bool upd = p.prev_out != nullptr;
+    if (f16) return upd ? launch_t<_Float16, true>(p, D, stream) : launch_t<_Float16, false>(p, D, stream);
+    return upd ? launch_t<__bf16, true>(p, D, stream) : launch_t<__bf16, false>(p, D, stream);
 }
 
 }  // namespace miattn

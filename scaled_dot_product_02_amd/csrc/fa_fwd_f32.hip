@@ -16,7 +16,8 @@ constexpr int BM = kF32TileM;  // query rows per workgroup (one per lane)
 constexpr int BN = 32;         // keys per LDS tile
 constexpr int CH = 16;         // keys per softmax chunk
 
-template <int D>
+// UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
+template <int D, bool UPDATE>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
 {
     __shared__ __attribute__((aligned(16))) float Ks[BN * D];
@@ -95,28 +96,64 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
     }
 
     if (qi < i1) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        // partial: O / l_run with max mc = m_run ln 2 and sum l_run; with UPDATE it is merged
+        // into the prior (o_p, m_p, l_p): m = max(m_p, mc), a = l_p e^(m_p - m),
+        // c = l_run e^(mc - m), out = o_p a / (a + c) + (O / l_run) c / (a + c)
+        const bool any = l_run > 0.f;
+        const float mc = any ? m_run * 0.69314718055994530942f : -INFINITY;
+        float m_out = mc, l_out = l_run;
+        float wc = any ? 1.f / l_run : 0.f, wp = 0.f;
+        if constexpr (UPDATE) {
+            const float mp = p.prev_max[st_base + qi], lp = p.prev_sum[st_base + qi];
+            const float m = fmaxf(mp, mc);
+            wc = 0.f;
+            l_out = 0.f;
+            if (m != -INFINITY) {
+                const float a = lp * __builtin_amdgcn_exp2f((mp - m) * 1.4426950408889634f);
+                const float f = any ? __builtin_amdgcn_exp2f(m_run - m * 1.4426950408889634f) : 0.f;
+                l_out = a + l_run * f;
+                wp = a / l_out;
+                wc = f / l_out;
+            }
+            m_out = m;
+        }
         float* orow = og + (int64_t)qi * p.o_ss;
         #pragma unroll
-        for (int d = 0; d < D; d += 4)
-            *(float4*)(orow + d) = float4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
-        if (p.smax) p.smax[st_base + qi] = l_run > 0.f ? m_run * 0.69314718055994530942f : -INFINITY;
-        if (p.ssum) p.ssum[st_base + qi] = l_run;
+        for (int d = 0; d < D; d += 4) {
+            float4 y{o[d] * wc, o[d + 1] * wc, o[d + 2] * wc, o[d + 3] * wc};
+            if constexpr (UPDATE) {
+                // an empty prior (weight 0) is not read: its buffer may hold anything
+                if (wp != 0.f) {
+                    const float4 po = *(const float4*)((const float*)p.prev_out + (orow - (float*)p.out) + d);
+                    y = float4{__builtin_fmaf(po.x, wp, y.x), __builtin_fmaf(po.y, wp, y.y),
+                               __builtin_fmaf(po.z, wp, y.z), __builtin_fmaf(po.w, wp, y.w)};
+                }
+            }
+            *(float4*)(orow + d) = y;
+        }
+        if (p.smax) p.smax[st_base + qi] = m_out;
+        if (p.ssum) p.ssum[st_base + qi] = l_out;
     }
+}
+
+template <bool UPDATE>
+hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
+{
+    dim3 grid(p.n_slots), block(64);
+    if (D == 64)
+        hipLaunchKernelGGL((fa_fwd_f32_kernel<64, UPDATE>), grid, block, 0, stream, p);
+    else if (D == 128)
+        hipLaunchKernelGGL((fa_fwd_f32_kernel<128, UPDATE>), grid, block, 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream)
 {
-    dim3 grid(p.n_slots), block(64);
-    if (D == 64)
-        hipLaunchKernelGGL(fa_fwd_f32_kernel<64>, grid, block, 0, stream, p);
-    else if (D == 128)
-        hipLaunchKernelGGL(fa_fwd_f32_kernel<128>, grid, block, 0, stream, p);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    return p.prev_out ? launch_t<true>(p, D, stream) : launch_t<false>(p, D, stream);
 }
 
 }  // namespace miattn

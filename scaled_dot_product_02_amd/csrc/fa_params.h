@@ -13,8 +13,14 @@ struct FaParams {
     const void* k;
     const void* v;
     void* out;
-    float* smax;            // may be null
-    float* ssum;            // may be null
+    float* smax;            // may be null (never null when prev_out is set)
+    float* ssum;            // may be null (never null when prev_out is set)
+    // Running result that this launch's partial is merged into (ring-attention update in
+    // the epilogue); null for a plain forward.  prev_out has the strides of out, the
+    // statistics the indexing of smax / ssum; out / smax / ssum may alias them.
+    const void* prev_out;
+    const float* prev_max;
+    const float* prev_sum;
     const int64_t* cu_q;    // null for dense batches
     const int64_t* cu_kv;
     int64_t q_sb, q_ss, q_sh;   // element strides: batch, sequence position, head
@@ -58,7 +64,8 @@ struct SparseParams {
 };
 
 // Launchers (defined next to their kernels).  Each returns the launch status.
-// the MFMA forward for bf16 (f16 = false) or fp16 (f16 = true) inputs
+// the MFMA forward for bf16 (f16 = false) or fp16 (f16 = true) inputs; both forwards
+// merge into p.prev_* when p.prev_out is set
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
 hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);

@@ -97,11 +97,17 @@ const char* miattn_status_str(miattn_status_t s)
     return "unknown status";
 }
 
-miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
-                         float* softmax_max, float* softmax_sum,
-                         int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
-                         miattn_dtype_t dtype, miattn_layout_t layout, float scale,
-                         miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Dense forward; with prev_out set, the partial result is merged into the prior.
+miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
+                          const void* prev_out, const float* prev_max, const float* prev_sum,
+                          void* out, float* softmax_max, float* softmax_sum,
+                          int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                          int dtype, int layout, float scale,
+                          int mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
 {
     if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -120,6 +126,7 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;
+    p.prev_out = prev_out; p.prev_max = prev_max; p.prev_sum = prev_sum;
     p.cu_q = p.cu_kv = nullptr;
     p.q_sb = sq.sb; p.q_ss = sq.ss; p.q_sh = sq.sh;
     p.o_sb = sq.sb; p.o_ss = sq.ss; p.o_sh = sq.sh;
@@ -133,14 +140,16 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
     return launch_fa(p, dtype, D, (hipStream_t)stream, Sq);
 }
 
-miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
-                                float* softmax_max, float* softmax_sum,
-                                const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
-                                int64_t B, int64_t Tq, int64_t Tkv,
-                                int64_t max_seqlen_q, int64_t max_seqlen_kv,
-                                int64_t Nq, int64_t Nkv, int64_t D,
-                                miattn_dtype_t dtype, float scale,
-                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+// Packed (TND) forward; with prev_out set, the partial result is merged into the prior.
+miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
+                           const void* prev_out, const float* prev_max, const float* prev_sum,
+                           void* out, float* softmax_max, float* softmax_sum,
+                           const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                           int64_t B, int64_t Tq, int64_t Tkv,
+                           int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                           int64_t Nq, int64_t Nkv, int64_t D,
+                           int dtype, float scale,
+                           int mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
 {
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_kv) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -159,6 +168,7 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;
+    p.prev_out = prev_out; p.prev_max = prev_max; p.prev_sum = prev_sum;
     p.cu_q = cu_seqlens_q; p.cu_kv = cu_seqlens_kv;
     p.q_sb = 0; p.q_ss = Nq * D; p.q_sh = D;
     p.o_sb = 0; p.o_ss = Nq * D; p.o_sh = D;
@@ -170,6 +180,64 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
     return launch_fa(p, dtype, D, (hipStream_t)stream, max_seqlen_q);
+}
+
+}  // namespace
+
+extern "C" {
+
+miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
+                         float* softmax_max, float* softmax_sum,
+                         int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                         miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                         miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+{
+    return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
+                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, stream);
+}
+
+miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                float* softmax_max, float* softmax_sum,
+                                const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                int64_t B, int64_t Tq, int64_t Tkv,
+                                int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                int64_t Nq, int64_t Nkv, int64_t D,
+                                miattn_dtype_t dtype, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+{
+    return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
+                      cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
+                      D, dtype, scale, mask, pre_tokens, next_tokens, stream);
+}
+
+miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
+                                const void* prev_out, const float* prev_max, const float* prev_sum,
+                                void* out, float* out_max, float* out_sum,
+                                int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+{
+    if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
+    return fwd_dense(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum, B, Nq, Nkv,
+                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, stream);
+}
+
+miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void* v,
+                                       const void* prev_out, const float* prev_max,
+                                       const float* prev_sum, void* out, float* out_max,
+                                       float* out_sum,
+                                       const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                       int64_t B, int64_t Tq, int64_t Tkv,
+                                       int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       miattn_dtype_t dtype, float scale,
+                                       miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                       void* stream)
+{
+    if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
+    return fwd_varlen(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
+                      cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
+                      D, dtype, scale, mask, pre_tokens, next_tokens, stream);
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

@@ -20,10 +20,10 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", src, re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_every_entry_point():
     d = _declared()
-    for name in ("attn_fwd", "attn_fwd_varlen", "attn_lse_merge", "sparse_csr_attn",
-                 "miattn_status_str"):
+    for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
+                 "attn_lse_merge", "sparse_csr_attn", "miattn_status_str"):
         assert name in d, d
 
 
@@ -104,6 +104,44 @@ def test_attn_fwd_varlen_validation(mi):
     assert _varlen(mi, scale=0.0) == "MIATTN_ERR_SCALE"
     assert _varlen(mi, D=32) == "MIATTN_ERR_UNSUPPORTED"
     assert _varlen(mi, dtype=3) == "MIATTN_ERR_DTYPE"
+
+
+def test_attn_fwd_update_validation(mi):
+    def call(**kw):
+        a = dict(q=P, po=P, pm=P, pl=P, out=P, om=P, ol=P, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64,
+                 dtype="bf16", layout="BNSD", scale=0.125, mask="band", pre=1 << 40, nxt=-16)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_fwd_update(a["q"], P, P, a["po"], a["pm"], a["pl"], a["out"], a["om"], a["ol"],
+                               a["B"], a["Nq"], a["Nkv"], a["Sq"], a["Skv"], a["D"], a["dtype"],
+                               a["layout"], a["scale"], a["mask"], a["pre"], a["nxt"], stream=0)
+        return mi.STATUS[e.value.status]
+    for name in ("q", "po", "pm", "pl", "out", "om", "ol"):
+        assert call(**{name: None}) == "MIATTN_ERR_NULL", name   # prior and stats are required
+    assert call(dtype=7) == "MIATTN_ERR_DTYPE"
+    assert call(layout=9) == "MIATTN_ERR_LAYOUT"
+    assert call(Sq=0) == "MIATTN_ERR_SHAPE"
+    assert call(Nq=5) == "MIATTN_ERR_GQA_RATIO"
+    assert call(pre=3, nxt=-4) == "MIATTN_ERR_MASK"
+    assert call(scale=float("nan")) == "MIATTN_ERR_SCALE"
+    assert call(D=96) == "MIATTN_ERR_UNSUPPORTED"
+
+
+def test_attn_fwd_varlen_update_validation(mi):
+    def call(**kw):
+        a = dict(po=P, pm=P, pl=P, om=P, ol=P, cq=P, B=3, Tq=100, mq=50, D=128, mask="causal")
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_fwd_varlen_update(P, P, P, a["po"], a["pm"], a["pl"], P, a["om"], a["ol"],
+                                      a["cq"], P, a["B"], a["Tq"], 100, a["mq"], 50, 8, 2, a["D"],
+                                      "bf16", 0.1, a["mask"], 0, 0, stream=0)
+        return mi.STATUS[e.value.status]
+    for name in ("po", "pm", "pl", "om", "ol", "cq"):
+        assert call(**{name: None}) == "MIATTN_ERR_NULL", name
+    assert call(B=0) == "MIATTN_ERR_SHAPE"
+    assert call(mq=101) == "MIATTN_ERR_SHAPE"
+    assert call(mask=4) == "MIATTN_ERR_MASK"
+    assert call(D=64 + 32) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_attn_lse_merge_validation(mi):

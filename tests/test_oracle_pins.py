@@ -341,6 +341,74 @@ def test_merge_closed_forms_on_random_stats():
     assert np.all(o == 0) and np.all(mm == -np.inf) and np.all(ll == 0)
 
 
+@pytest.mark.parametrize("mask,pre,nxt,cuts", [("causal", 0, 0, [0, 5, 6, 13, 24]),
+                                                ("none", 0, 0, [0, 8, 16, 24]),
+                                                ("band", 7, 3, [0, 1, 11, 12, 24])])
+def test_update_over_key_chunks_equals_full_attention(mask, pre, nxt, cuts):
+    """Ring accumulation: starting from an empty result, attn_update over consecutive key
+    chunks [c0, c1), [c1, c2), ... with the band shifted by each chunk's start (keys
+    j0 + j' seen from query i iff -pre <= j0 + j' - i <= next) gives attention over all
+    keys.  Causal is band(inf, 0).  Empty chunks (13 -> 13) and one-key chunks included."""
+    rng = np.random.default_rng(11)
+    S, Skv = 20, 24
+    q, k, v = _rand(rng, 2, 4, S, 6), _rand(rng, 2, 2, Skv, 6), _rand(rng, 2, 2, Skv, 6)
+    full = oracle.attn(q, k, v, 0.4, mask, pre, nxt)
+    p_lo = (1 << 62) if mask in ("causal", "none") else pre
+    n_hi = 0 if mask == "causal" else ((1 << 62) if mask == "none" else nxt)
+    out = np.full(q.shape, 12345.0)     # an empty prior's output is never used
+    m = np.full((2, 4, S), -np.inf)
+    l = np.zeros((2, 4, S))
+    for c0, c1 in zip(cuts[:-1], cuts[1:]):
+        if c1 == c0:
+            continue
+        o_c = oracle.attn_update(q, k[:, :, c0:c1], v[:, :, c0:c1], np.where(l[..., None] > 0, out, 0.0),
+                                 m, l, 0.4, "band", p_lo + c0, n_hi - c0)
+        out, m, l = o_c
+    assert np.max(np.abs(out - full[0])) < TOL
+    assert np.array_equal(m == -np.inf, full[1] == -np.inf)
+    fin = full[1] > -np.inf
+    assert np.max(np.abs(m[fin] - full[1][fin])) < TOL
+    assert np.max(np.abs(l[fin] / full[2][fin] - 1)) < TOL
+    assert np.all(l[~fin] == 0)
+
+
+def test_varlen_update_over_key_chunks_equals_full_attention():
+    """The packed form: each sequence's keys split into chunks, each chunk packed with its
+    own cumulative lengths (one ring step's shard), accumulated with attn_varlen_update."""
+    rng = np.random.default_rng(12)
+    lq = np.array([9, 0, 1, 14])
+    cu = np.cumsum(lq)
+    T = int(cu[-1])
+    q, k, v = _rand(rng, T, 4, 5), _rand(rng, T, 2, 5), _rand(rng, T, 2, 5)
+    full = oracle.attn_varlen(q, k, v, cu, cu, 0.6, "causal")
+    starts = np.concatenate([[0], cu[:-1]])
+    out = np.zeros_like(q)
+    m = np.full((4, T), -np.inf)
+    l = np.zeros((4, T))
+    C = 4
+    for j in range(4):                     # chunk j holds keys [4j, 4j + 4) of each sequence
+        rows = [np.arange(s + min(C * j, n), s + min(C * (j + 1), n)) for s, n in zip(starts, lq)]
+        lk = np.array([len(r) for r in rows])
+        idx = np.concatenate(rows).astype(np.int64)
+        out, m, l = oracle.attn_varlen_update(q, k[idx], v[idx], out, m, l, cu, np.cumsum(lk),
+                                              0.6, "band", 1 << 62, -C * j)
+    assert np.max(np.abs(out - full[0])) < TOL
+    fin = full[1] > -np.inf
+    assert np.array_equal(m[~fin], full[1][~fin])
+    assert np.max(np.abs(m[fin] - full[1][fin])) < TOL
+    assert np.max(np.abs(l[fin] / full[2][fin] - 1)) < TOL
+
+
+def test_update_with_empty_prior_is_plain_attention():
+    rng = np.random.default_rng(13)
+    q, k, v = _rand(rng, 1, 2, 9, 4), _rand(rng, 1, 2, 11, 4), _rand(rng, 1, 2, 11, 4)
+    want = oracle.attn(q, k, v, 0.7, "band", 2, 1)
+    got = oracle.attn_update(q, k, v, np.zeros_like(q), np.full((1, 2, 9), -np.inf),
+                             np.zeros((1, 2, 9)), 0.7, "band", 2, 1)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+
+
 # ------------------------------------------------------------------------------------
 # CSR sparse attention
 # ------------------------------------------------------------------------------------
