@@ -14,6 +14,10 @@ Also measured in the same run (reported under "secondary"):
     fused attn_fwd_update chain vs attn_fwd + attn_lse_merge, and one full forward;
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, fp32, band 128 + 64 random).
 
+measured_peaks: the dense bf16 MFMA rate of the chip and the bandwidth of a plain 2-read /
+1-write stream at the merge's size, from the peak probes (libmiattn_probes.so); each
+roofline also states its fraction of the measured ceiling beside the datasheet one.
+
 cpu_baseline: the CPU fp64 oracle (untuned) on a bounded sample of the same workload
 (all sequences, the first --cpu-heads query heads), timed on this host's cores.
 
@@ -36,6 +40,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
+PROBES_LIB = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn_probes.so")
 PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_varlen_causal_gqa_t33064_pmc.json")
 
 
@@ -58,6 +63,20 @@ def measured_traffic():
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def load_probes():
+    """The peak probes (include/miattn_probes.h) through ctypes."""
+    import ctypes
+    if not os.path.exists(PROBES_LIB):
+        raise SystemExit(f"{PROBES_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PROBES_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.miattn_probe_mfma_bf16.argtypes = [P, I32, I32, P]
+    lib.miattn_probe_mfma_bf16_flops.argtypes = [I32, I32]
+    lib.miattn_probe_mfma_bf16_flops.restype = I64
+    lib.miattn_probe_stream_r2w1.argtypes = [P, P, P, I64, P]
+    return lib
 
 
 def time_launches(fn, steps: int, warmup: int, stream):
@@ -163,8 +182,29 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes": alg_bytes,
-                     "kernel": "fa_fwd_bf16_kernel<128>"},
+                     "kernel": "fa_fwd_bf16_kernel<128, __bf16, false>"},
     }
+
+    # ---------------- measured ceilings: dense bf16 MFMA rate of the chip ----------------
+    probes = load_probes()
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count   # 8 waves per CU
+    iters = 512
+    pout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def mfma_probe():
+        rc = probes.miattn_probe_mfma_bf16(pout.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(f"mfma probe launch failed ({rc})")
+
+    pms = time_launches(mfma_probe, 3, 1, stream)
+    mfma_meas = probes.miattn_probe_mfma_bf16_flops(blocks, iters) / (pms * 1e-3) / 1e12
+    result["measured_peaks"] = {
+        "mfma_bf16_tflops": round(mfma_meas, 1),
+        "mfma_method": f"{blocks} workgroups x 4 waves, back-to-back v_mfma_f32_32x32x16_bf16 "
+                       "on 8 independent accumulators"}
+    result["roofline"]["measured_peak"] = round(mfma_meas, 1)
+    result["roofline"]["frac_of_measured_peak"] = round(tflops / mfma_meas, 4)
+    del pout
 
     # ---------------- secondary: fp16 forward, merge and sparse ----------------
     if not args.no_secondary:
@@ -207,6 +247,23 @@ def main():
             mi.attn_lse_merge(*s_, 1, N, S, Dm, "bf16", "SBH", stream.cuda_stream)
 
         mms = time_launches(merge_step, 4 * 25, 8, stream)
+
+        # measured streaming ceiling at the same size: read two 64 MiB arrays, write one
+        sbytes_stream = sets[0][0].numel() * 2
+
+        def stream_step():
+            s_ = sets[it[0] % len(sets)]
+            it[0] += 1
+            rc = probes.miattn_probe_stream_r2w1(s_[0].data_ptr(), s_[3].data_ptr(),
+                                                 s_[6].data_ptr(), sbytes_stream, stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"stream probe launch failed ({rc})")
+
+        stms = time_launches(stream_step, 4 * 25, 8, stream)
+        stream_gbs = 3 * sbytes_stream / (stms * 1e-3) / 1e9
+        result["measured_peaks"]["stream_2r1w_gbs"] = round(stream_gbs, 1)
+        result["measured_peaks"]["stream_method"] = (
+            "o[i] = a[i] ^ b[i] over 3 x 64 MiB, non-temporal 16-byte accesses, 4 rotating sets")
 
         # causal ring over 4 key chunks of the same workload: fused update vs
         # forward + merge kernel, and the single full forward for reference
@@ -258,7 +315,9 @@ def main():
             "workload": "ring_merge_sbh_bf16_s8192_n32_d128", "us_per_launch": round(mms * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(mgbs / PEAK_HBM_GBS, 4),
-                         "algorithmic_bytes": mbytes, "rotating_sets": len(sets)}}
+                         "algorithmic_bytes": mbytes, "rotating_sets": len(sets),
+                         "measured_peak": round(stream_gbs, 1),
+                         "frac_of_measured_peak": round(mgbs / stream_gbs, 4)}}
         del sets
 
         ws = synthetic.make("csr_sparse_f32_b2n8s4096d64")

@@ -35,6 +35,26 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, name
 
 
+def test_probe_library_exports_its_declared_symbols():
+    lib = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn_probes.so")
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "miattn_probes.h")).read(), flags=re.S)
+    declared = set(re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", src, re.M))
+    assert declared == {"miattn_probe_mfma_bf16", "miattn_probe_mfma_bf16_flops",
+                        "miattn_probe_stream_r2w1"}
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert declared <= exported
+    import ctypes
+    probes = ctypes.CDLL(lib)
+    probes.miattn_probe_mfma_bf16_flops.restype = ctypes.c_int64
+    probes.miattn_probe_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert probes.miattn_probe_mfma_bf16_flops(3, 5) == 3 * 4 * 5 * 8 * 2 * 32 * 32 * 16
+    probes.miattn_probe_stream_r2w1.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_void_p]
+    assert probes.miattn_probe_stream_r2w1(256, 256, 256, 24, None) != 0   # not a multiple of 16
+    assert probes.miattn_probe_stream_r2w1(None, 256, 256, 32, None) != 0
+
+
 @pytest.fixture(scope="module")
 def mi():
     import scaled_dot_product_02_amd as m
