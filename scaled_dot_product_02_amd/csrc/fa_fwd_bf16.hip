@@ -94,7 +94,8 @@ struct Cfg {
     static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
     static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
     static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-    static constexpr int KPT = BN * CPR / NT;         // K chunks per thread
+    static constexpr int KCH = BN * CPR;              // K chunks per tile
+    static constexpr int KPT = (KCH + NT - 1) / NT;   // K chunks per thread (some repeat)
     static constexpr int VUNITS = (BN / 2) * CPR;     // V units (2 keys x 8 dims) per tile
     static constexpr int SREG = KPT + 2;              // staging registers (16 B each)
     static constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     uint32_t koff[C::KPT], voff[2];
     #pragma unroll
     for (int u = 0; u < C::KPT; ++u) {
-        const int c = tid + NT * u;
+        const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
         koff[u] = (uint32_t)((c / C::CPR) * krb + 16 * (c % C::CPR));
     }
     #pragma unroll
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         __bf16* kb = Ks + bf * C::KBUF;
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
-            const int c = tid + NT * u;
+            const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
             *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
         }
         // dims 8 vc + e of keys 2 kp, 2 kp + 1 -> one 32-bit word of V^T row 8 vc + e
@@ -290,13 +291,14 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         }
 #if FA_SCHED
         // keep LDSD reads in flight ahead of the MFMAs that consume them
-        __builtin_amdgcn_sched_group_barrier(0x100, LDSD, 0);
+        constexpr int AH = LDSD < NF ? LDSD : NF;
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
         #pragma unroll
-        for (int f = 0; f < NF - LDSD; ++f) {
+        for (int f = 0; f < NF - AH; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, LDSD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
 #endif
     };
 
@@ -315,13 +317,14 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
             o[f / (2 * NKB)] = Elem<T>::mfma(a[f], pp[f % (2 * NKB)], o[f / (2 * NKB)]);
         }
 #if FA_SCHED
-        __builtin_amdgcn_sched_group_barrier(0x100, LDSD, 0);
+        constexpr int AH = LDSD < NF ? LDSD : NF;
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
         #pragma unroll
-        for (int f = 0; f < NF - LDSD; ++f) {
+        for (int f = 0; f < NF - AH; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, LDSD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
 #endif
     };
 
@@ -478,12 +481,13 @@ template <typename T, bool UPDATE>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(NT);
-    if (D == 64)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE>), grid, block, 0, stream, p);
-    else if (D == 128)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE>), grid, block, 0, stream, p);
-    else
-        return hipErrorInvalidValue;
+    switch (D) {
+    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, T, UPDATE>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, T, UPDATE>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -140,12 +140,13 @@ template <bool UPDATE>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(64);
-    if (D == 64)
-        hipLaunchKernelGGL((fa_fwd_f32_kernel<64, UPDATE>), grid, block, 0, stream, p);
-    else if (D == 128)
-        hipLaunchKernelGGL((fa_fwd_f32_kernel<128, UPDATE>), grid, block, 0, stream, p);
-    else
-        return hipErrorInvalidValue;
+    switch (D) {
+    case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<32, UPDATE>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<64, UPDATE>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<96, UPDATE>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<128, UPDATE>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

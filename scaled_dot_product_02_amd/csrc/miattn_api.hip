@@ -46,6 +46,9 @@ miattn_status_t check_mask(int mask, int64_t pre, int64_t next, int64_t& pre_c, 
 
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
+// head dims with a built attention kernel (every dtype)
+bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
+
 miattn_status_t check_dtype_fa(int dtype)
 {
     if (dtype == MIATTN_F32 || dtype == MIATTN_BF16 || dtype == MIATTN_F16) return MIATTN_OK;
@@ -121,7 +124,7 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
     if (st != MIATTN_OK) return st;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     p.q = q; p.k = k; p.v = v; p.out = out;
@@ -164,7 +167,7 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
     if (st != MIATTN_OK) return st;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;

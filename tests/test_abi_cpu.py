@@ -79,7 +79,7 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, q=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, out=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, dtype=9) == "MIATTN_ERR_DTYPE"
-    assert _fwd(mi, dtype="f16", D=96) == "MIATTN_ERR_UNSUPPORTED"   # fp16 takes D 64/128 too
+    assert _fwd(mi, dtype="f16", D=80) == "MIATTN_ERR_UNSUPPORTED"   # fp16 takes the bf16 head dims
     assert _fwd(mi, layout=7) == "MIATTN_ERR_LAYOUT"
     assert _fwd(mi, B=0) == "MIATTN_ERR_SHAPE"
     assert _fwd(mi, Sq=0) == "MIATTN_ERR_SHAPE"
@@ -95,7 +95,7 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, scale=-0.1) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, scale=float("nan")) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, scale=float("inf")) == "MIATTN_ERR_SCALE"
-    assert _fwd(mi, D=96) == "MIATTN_ERR_UNSUPPORTED"           # in spec, not built
+    assert _fwd(mi, D=80) == "MIATTN_ERR_UNSUPPORTED"           # in spec, not built (32/64/96/128 are)
     assert _fwd(mi, D=1) == "MIATTN_ERR_UNSUPPORTED"
 
 
@@ -122,7 +122,7 @@ def test_attn_fwd_varlen_validation(mi):
     assert _varlen(mi, Nq=8, Nkv=3) == "MIATTN_ERR_GQA_RATIO"
     assert _varlen(mi, mask="band", pre=-5, nxt=4) == "MIATTN_ERR_MASK"
     assert _varlen(mi, scale=0.0) == "MIATTN_ERR_SCALE"
-    assert _varlen(mi, D=32) == "MIATTN_ERR_UNSUPPORTED"
+    assert _varlen(mi, D=48) == "MIATTN_ERR_UNSUPPORTED"
     assert _varlen(mi, dtype=3) == "MIATTN_ERR_DTYPE"
 
 
@@ -144,7 +144,7 @@ def test_attn_fwd_update_validation(mi):
     assert call(Nq=5) == "MIATTN_ERR_GQA_RATIO"
     assert call(pre=3, nxt=-4) == "MIATTN_ERR_MASK"
     assert call(scale=float("nan")) == "MIATTN_ERR_SCALE"
-    assert call(D=96) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=160) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_attn_fwd_varlen_update_validation(mi):
@@ -161,7 +161,7 @@ def test_attn_fwd_varlen_update_validation(mi):
     assert call(B=0) == "MIATTN_ERR_SHAPE"
     assert call(mq=101) == "MIATTN_ERR_SHAPE"
     assert call(mask=4) == "MIATTN_ERR_MASK"
-    assert call(D=64 + 32) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=100) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_attn_lse_merge_validation(mi):

@@ -64,7 +64,7 @@ def test_dense_bf16_b8n8s128d64(mi):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
 @pytest.mark.parametrize("layout", ["BNSD", "BSND", "BSH", "SBH"])
 @pytest.mark.parametrize("mask,pre,nxt", [("none", 0, 0), ("causal", 0, 0), ("band", 70, 33),
                                           ("band", 1 << 62, -150)])
@@ -109,6 +109,18 @@ def test_varlen_small(mi, mask, pre, nxt, dtype):
     go, gm, gl = _run_varlen(mi, w, 1 / math.sqrt(128), mask, pre, nxt)
     q, k, v = (synthetic.storage_values(w[x], dtype) for x in ("q", "k", "v"))
     wo, wm, wl = oracle.attn_varlen(q, k, v, w["cu_q"], w["cu_kv"], 1 / math.sqrt(128), mask, pre, nxt)
+    check_out(go, wo, dtype)
+    check_stats(gm, gl, wm, wl)
+
+
+@pytest.mark.parametrize("D", [32, 96])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_varlen_other_head_dims(mi, D, dtype):
+    lengths = [300, 0, 1, 129, 64, 517, 2]
+    w = synthetic.varlen_inputs(25 + D, Nq=8, Nkv=2, D=D, dtype=dtype, lengths_q=lengths)
+    go, gm, gl = _run_varlen(mi, w, 1 / math.sqrt(D), "causal")
+    q, k, v = (synthetic.storage_values(w[x], dtype) for x in ("q", "k", "v"))
+    wo, wm, wl = oracle.attn_varlen(q, k, v, w["cu_q"], w["cu_kv"], 1 / math.sqrt(D), "causal")
     check_out(go, wo, dtype)
     check_stats(gm, gl, wm, wl)
 

@@ -57,7 +57,7 @@ def _dense_case(seed, dtype, layout, D, B=2, Nq=4, Nkv=2, Sq=300, Skv=333):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
 @pytest.mark.parametrize("layout", ["BNSD", "SBH"])
 @pytest.mark.parametrize("mask,pre,nxt", [("none", 0, 0), ("causal", 0, 0), ("band", 70, 33),
                                           ("band", BIG, -150)])
