@@ -12,7 +12,8 @@ Also measured in the same run (reported under "secondary"):
     rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
   * causal attention over that workload's 4 key chunks of 2048 (a ring on one GPU): the
     fused attn_fwd_update chain vs attn_fwd + attn_lse_merge, and one full forward;
-  * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, fp32, band 128 + 64 random).
+  * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, band 128 + 64 random), in
+    fp32 and in fp64 (same pattern and draws).
 
 measured_peaks: the dense bf16 MFMA rate of the chip and the bandwidth of a plain 2-read /
 1-write stream at the merge's size, from the peak probes (libmiattn_probes.so); each
@@ -340,6 +341,22 @@ def main():
             "tflops": round(stf, 3), "gbs_algorithmic": round(sbytes / (sms * 1e-3) / 1e9, 1),
             "roofline": {"bound": "alu", "achieved": round(stf, 3), "peak": PEAK_F32_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(stf / PEAK_F32_TFLOPS, 4)}}
+        # the same CSR workload with fp64 inputs and arithmetic
+        wd = synthetic.sparse_inputs(0, sB, sN, sS, sD, band=128, n_random=64, dtype="f64")
+        dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(wd[x])).to(dev) for x in ("q", "k", "v"))
+        do_ = torch.empty_like(dq)
+
+        def sparse_step_f64():
+            mi.sparse_csr_attn(dq, dk, dv, do_, soff, scol, nnz, sB, sN, sS, sD, "f64",
+                               1 / math.sqrt(sD), stream.cuda_stream)
+
+        dms = time_launches(sparse_step_f64, 10, 2, stream)
+        dtf = sflops / (dms * 1e-3) / 1e12
+        sec["sparse_csr_attn_f64"] = {
+            "workload": "csr_sparse_f64_b2n8s4096d64", "us_per_launch": round(dms * 1e3, 2),
+            "tflops": round(dtf, 3),
+            "roofline": {"bound": "alu", "achieved": round(dtf, 3), "peak": 78.6,
+                         "unit": "TFLOP/s", "frac": round(dtf / 78.6, 4)}}
         result["secondary"] = sec
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------

@@ -60,7 +60,8 @@ typedef enum {
     MIATTN_ERR_SCALE = 9        /* scale is not a finite positive number */
 } miattn_status_t;
 
-typedef enum { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2 } miattn_dtype_t;
+/* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
+typedef enum { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2, MIATTN_F64 = 3 } miattn_dtype_t;
 typedef enum { MIATTN_BNSD = 0, MIATTN_BSND = 1, MIATTN_BSH = 2, MIATTN_SBH = 3 } miattn_layout_t;
 typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 2 } miattn_mask_t;
 
@@ -78,7 +79,7 @@ typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 
  *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
  *   dtype: MIATTN_BF16 or MIATTN_F16 (MFMA path: fp32 accumulation, the softmax weights
  *   rounded to the input type for the P V product, RNE output) or MIATTN_F32.
- *   D: 64 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
+ *   D: 32, 64, 96 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
  *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
  *   Pass pre_tokens/next_tokens for MIATTN_MASK_BAND; they are ignored otherwise.
@@ -106,7 +107,7 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
  *   cu_seqlens_q, cu_seqlens_kv: DEVICE int64 [B], monotone, last = Tq / Tkv;
  *   max_seqlen_q, max_seqlen_kv: host upper bounds of the sequence lengths (the grid is
  *   sized from max_seqlen_q; rows of a longer sequence are NOT computed).
- *   Ranges: 1 <= B <= 2048, 1 <= Tq, Tkv <= 2^20, 1 <= Nq, Nkv <= 256, D in {64, 128}.
+ *   Ranges: 1 <= B <= 2048, 1 <= Tq, Tkv <= 2^20, 1 <= Nq, Nkv <= 256, D in {32, 64, 96, 128}.
  *   dtype, scale, mask, pre/next: as for attn_fwd.
  */
 miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
@@ -201,9 +202,11 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
  * (offset[0] = 0, offset[S] = entries used).  Every stored entry counts once (a repeated
  * column counts as often as it is stored); an empty row gives 0.
  *
- *   q, k, v, out: fp32 [B, N, S, D] (BNSD) contiguous;
+ *   q, k, v, out: fp32 or fp64 [B, N, S, D] (BNSD) contiguous (all arithmetic in that type;
+ *   the fp64 path uses `scale` widened to double);
  *   csr_offset: DEVICE int32 [B, N, S+1];  csr_columns: DEVICE int32 [B, N, nnz];
- *   dtype: MIATTN_F32 only.  D in {64, 128}.  nnz >= 0.
+ *   dtype: MIATTN_F32 or MIATTN_F64 (bf16/fp16 -> UNSUPPORTED).  D in {32, 64, 96, 128}.
+ *   nnz >= 0.
  */
 miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, void* out,
                                 const int32_t* csr_offset, const int32_t* csr_columns,

@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATTN_ERR_DTYPE",
           4: "MIATTN_ERR_LAYOUT", 5: "MIATTN_ERR_GQA_RATIO", 6: "MIATTN_ERR_MASK",
           7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE"}
-DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2}
 

@@ -52,15 +52,16 @@ struct MergeParams {
 };
 
 struct SparseParams {
-    const float* q;
-    const float* k;
-    const float* v;
-    float* out;
+    const void* q;          // float or double, as `out`
+    const void* k;
+    const void* v;
+    void* out;
     const int32_t* offset;
     const int32_t* columns;
     int64_t nnz;
     int32_t B, N, S;
     float scale_log2;
+    double scale_log2_d;        // the same in double precision (fp64 inputs)
 };
 
 // Launchers (defined next to their kernels).  Each returns the launch status.
@@ -69,7 +70,7 @@ struct SparseParams {
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
 hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
-hipError_t launch_sparse_csr(const SparseParams& p, int D, hipStream_t stream);
+hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream);
 
 // Row tile heights, used by the C-ABI layer to size the grids.
 constexpr int kBf16TileM = 256;

@@ -274,19 +274,21 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
 {
     if (!q || !k || !v || !out || !csr_offset) return MIATTN_ERR_NULL;
     if (nnz > 0 && !csr_columns) return MIATTN_ERR_NULL;
-    if (dtype != MIATTN_F32)
+    if (dtype != MIATTN_F32 && dtype != MIATTN_F64)
         return (dtype == MIATTN_BF16 || dtype == MIATTN_F16) ? MIATTN_ERR_UNSUPPORTED : MIATTN_ERR_DTYPE;
     if (B < 1 || N < 1 || S < 1 || D < 1 || nnz < 0 || D > 768) return MIATTN_ERR_SHAPE;
     if (S >= (int64_t(1) << 31) - 1 || nnz >= (int64_t(1) << 31) || B * N * S >= (int64_t(1) << 33))
         return MIATTN_ERR_SHAPE;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (D != 64 && D != 128) return MIATTN_ERR_UNSUPPORTED;
+    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
     SparseParams p{};
-    p.q = (const float*)q; p.k = (const float*)k; p.v = (const float*)v; p.out = (float*)out;
+    p.q = q; p.k = k; p.v = v; p.out = out;
     p.offset = csr_offset; p.columns = csr_columns; p.nnz = nnz;
     p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return launch_sparse_csr(p, (int)D, (hipStream_t)stream) == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
+    p.scale_log2_d = (double)scale * 1.4426950408889634074;
+    return launch_sparse_csr(p, (int)D, dtype == MIATTN_F64, (hipStream_t)stream) == hipSuccess
+               ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

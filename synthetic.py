@@ -65,6 +65,8 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
         return f16_bits_from_f32(x)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f64":
+        return np.ascontiguousarray(x, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

@@ -6,6 +6,8 @@ Tolerances (stated once, used everywhere):
   fp16 outputs (fp32 accumulation): max |gpu - oracle| <= 5e-3  (derived: the softmax weights
     and the output are each rounded once to binary16, unit roundoff u = 2^-11, with |v|, |out|
     <= 5 for these normal draws, so the error is below 2 * 5 * u = 4.9e-3)
+  fp64 outputs (fp64 arithmetic):  max |gpu - oracle| <= 1e-10  (derived: score rounding
+    ~ D * 2^-53 * sum|q_d k_d| < 1e-12 for these draws, times |v| <= 5, with margin)
   softmax_max:  |gpu - oracle| <= 1e-4 * max(1, |oracle|)   (-inf must match exactly)
   softmax_sum:  |gpu - oracle| <= 1e-4 * oracle              (0 must match exactly)
 """
@@ -16,7 +18,7 @@ import torch
 
 import synthetic
 
-TOL_OUT = {"f32": 1e-5, "bf16": 2e-2, "f16": 5e-3}
+TOL_OUT = {"f32": 1e-5, "bf16": 2e-2, "f16": 5e-3, "f64": 1e-10}
 TOL_STAT = 1e-4
 
 
@@ -43,7 +45,8 @@ def host_values(t: torch.Tensor) -> np.ndarray:
 
 def empty_like_storage(shape, dtype: str) -> torch.Tensor:
     """Output buffer pre-filled with NaN so that an unwritten element fails the checks."""
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
+           "f64": torch.float64}[dtype]
     return torch.full(shape, float("nan"), dtype=tdt, device="cuda:0")
 
 

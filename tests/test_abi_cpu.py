@@ -79,6 +79,7 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, q=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, out=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, dtype=9) == "MIATTN_ERR_DTYPE"
+    assert _fwd(mi, dtype="f64") == "MIATTN_ERR_DTYPE"          # fp64 is the sparse op's only
     assert _fwd(mi, dtype="f16", D=80) == "MIATTN_ERR_UNSUPPORTED"   # fp16 takes the bf16 head dims
     assert _fwd(mi, layout=7) == "MIATTN_ERR_LAYOUT"
     assert _fwd(mi, B=0) == "MIATTN_ERR_SHAPE"
@@ -177,6 +178,7 @@ def test_attn_lse_merge_validation(mi):
     for i in range(9):
         assert call(null=i) == "MIATTN_ERR_NULL"
     assert call(dtype=5) == "MIATTN_ERR_DTYPE"
+    assert call(dtype="f64") == "MIATTN_ERR_DTYPE"
     assert call(layout=4) == "MIATTN_ERR_LAYOUT"
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(N=300) == "MIATTN_ERR_SHAPE"
@@ -198,7 +200,7 @@ def test_sparse_csr_attn_validation(mi):
     assert call(nnz=-1) == "MIATTN_ERR_SHAPE"
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(scale=0.0) == "MIATTN_ERR_SCALE"
-    assert call(D=32) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=48) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_status_strings(mi):

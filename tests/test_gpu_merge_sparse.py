@@ -145,25 +145,29 @@ def test_ring_halves_merge_equals_full_attention(mi):
                     wm[:, :, sel], wl[:, :, sel])
 
 
-def _sparse_gpu(mi, w, scale):
-    q, k, v = (dev(w[x], "f32") for x in ("q", "k", "v"))
+def _sparse_gpu(mi, w, scale, dtype="f32"):
+    q, k, v = (dev(w[x], dtype) for x in ("q", "k", "v"))
     off = torch.from_numpy(np.ascontiguousarray(w["offset"])).to("cuda:0")
     col = torch.from_numpy(np.ascontiguousarray(w["columns"])).to("cuda:0")
-    out = empty_like_storage(q.shape, "f32")
-    mi.sparse_csr_attn(q, k, v, out, off, col, w["nnz"], w["B"], w["N"], w["S"], w["D"], "f32", scale)
+    out = empty_like_storage(q.shape, dtype)
+    mi.sparse_csr_attn(q, k, v, out, off, col, w["nnz"], w["B"], w["N"], w["S"], w["D"], dtype, scale)
     torch.cuda.synchronize()
     return host_values(out)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_sparse_small(mi, D):
-    w = synthetic.sparse_inputs(51, 2, 3, 300, D, band=16, n_random=80)
-    go = _sparse_gpu(mi, w, 1 / math.sqrt(D))
-    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], 1 / math.sqrt(D))
-    check_out(go, wo, "f32")
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+def test_sparse_small(mi, D, dtype):
+    w = synthetic.sparse_inputs(51, 2, 3, 300, D, band=16, n_random=80, dtype=dtype)
+    # the entry point takes a float scale: the oracle gets the same float value
+    sc = float(np.float32(1 / math.sqrt(D)))
+    go = _sparse_gpu(mi, w, sc, dtype)
+    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], sc)
+    check_out(go, wo, dtype)
 
 
-def test_sparse_paddle_example(mi):
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_sparse_paddle_example(mi, dtype):
     """The Paddle sparse_attention worked example on the GPU (D = 2 is not built, so the
     example is embedded in D = 64 with zero padding, which leaves every dot product and
     every output column of the example unchanged)."""
@@ -172,10 +176,15 @@ def test_sparse_paddle_example(mi):
     x[0, 0, :, :2] = base
     w = dict(q=x, k=x, v=x, offset=np.array([[[0, 2, 4, 6, 8]]], np.int32),
              columns=np.array([[[0, 1, 0, 1, 2, 3, 2, 3]]], np.int32), nnz=8, B=1, N=1, S=4, D=64)
-    go = _sparse_gpu(mi, w, 1 / math.sqrt(2))
+    if dtype == "f64":
+        w = dict(w, q=x.astype(np.float64), k=x.astype(np.float64), v=x.astype(np.float64))
+    sc = float(np.float32(1 / math.sqrt(2)))
+    go = _sparse_gpu(mi, w, sc, dtype)
     printed = np.array([[1.60885942, 2.60885954], [1.99830270, 2.99830270]] * 2)
     assert np.max(np.abs(go[0, 0, :, :2] - printed)) < 1e-6
     assert np.all(go[0, 0, :, 2:] == 0)
+    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], sc)
+    check_out(go, wo, dtype)
 
 
 def test_sparse_empty_rows_and_duplicates(mi):
@@ -214,6 +223,15 @@ def test_sparse_full_workload(sparse_full):
     assert w["nnz"] == 768096
     wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], 1 / math.sqrt(64))
     check_out(go, wo, "f32")
+
+
+def test_sparse_full_workload_f64(mi):
+    """The full CSR workload (same seed and pattern) with fp64 inputs and arithmetic."""
+    w = synthetic.sparse_inputs(0, 2, 8, 4096, 64, band=128, n_random=64, dtype="f64")
+    assert w["nnz"] == 768096
+    go = _sparse_gpu(mi, w, 0.125, "f64")
+    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], 0.125)
+    check_out(go, wo, "f64")
 
 
 def test_sparse_deterministic(mi, sparse_full):
