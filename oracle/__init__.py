@@ -45,7 +45,9 @@ def _load():
     lib.oracle_attn_varlen.argtypes = [P] * 8 + [I64] * 6 + [D, I, I64, I64, I]
     lib.oracle_merge.argtypes = [P] * 9 + [I64] * 4 + [I]
     lib.oracle_sparse.argtypes = [P] * 8 + [I64] * 5 + [D, I]
-    for f in (lib.oracle_attn, lib.oracle_attn_varlen, lib.oracle_merge, lib.oracle_sparse):
+    lib.oracle_attn_keep.argtypes = [P] * 7 + [I64] * 7 + [D, I]
+    for f in (lib.oracle_attn, lib.oracle_attn_varlen, lib.oracle_merge, lib.oracle_sparse,
+              lib.oracle_attn_keep):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -106,6 +108,77 @@ def attn_varlen(q, k, v, cu_q, cu_kv, scale: float, mask: str = "none", pre: int
                                     _clamp_tokens(next), threads)
     if rc != 0:
         raise ValueError("oracle_attn_varlen: invalid arguments")
+    return out, m, l
+
+
+# ------------------------------------------------------------------------------------
+# explicit visibility matrices ("keep": True where key j is visible from query i), for the
+# mask modes of aclnnFlashAttentionVarLenScore (sparseMode, preTokens / nextTokens,
+# prefixOptional, attenMaskOptional), written from the readings stated with each.
+# ------------------------------------------------------------------------------------
+
+def keep_band(Sq: int, Skv: int, pre: int, next: int, align: str = "top_left") -> np.ndarray:
+    """Band -pre <= j - i <= next.  top_left: positions as they are; bottom_right: the
+    diagonal moved to the last query / last key pair, i.e. j - i - (Skv - Sq)."""
+    i = np.arange(Sq, dtype=np.int64)[:, None]
+    j = np.arange(Skv, dtype=np.int64)[None, :]
+    d = j - i - ((Skv - Sq) if align == "bottom_right" else 0)
+    return (d >= -int(pre)) & (d <= int(next))
+
+
+def keep_prefix_causal(Sq: int, Skv: int, prefix: int) -> np.ndarray:
+    """Bottom-right causal plus a prefix: key j is visible from query i when
+    j - i <= Skv - Sq, or when j < prefix (the first `prefix` keys are seen by every row)."""
+    i = np.arange(Sq, dtype=np.int64)[:, None]
+    j = np.arange(Skv, dtype=np.int64)[None, :]
+    return (j - i <= Skv - Sq) | (j < int(prefix))
+
+
+def attn_keep(q, k, v, keep, scale: float, threads: int = 0):
+    """Dense attention over an explicit visibility matrix.  q (B,Nq,Sq,D), k (B,Nkv,Skv,D),
+    v (B,Nkv,Skv,Dv), keep (Sq,Skv) or (B,Sq,Skv) bool -> out (B,Nq,Sq,Dv),
+    softmax_max (B,Nq,Sq), softmax_sum (B,Nq,Sq)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, Sq, D = q.shape
+    _, Nkv, Skv, Dv = v.shape
+    if k.shape != (B, Nkv, Skv, D) or v.shape[:3] != (B, Nkv, Skv):
+        raise ValueError("shape mismatch")
+    keep = np.broadcast_to(np.asarray(keep, dtype=bool), (B, Sq, Skv))
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    out = np.empty((B, Nq, Sq, Dv))
+    m = np.empty((B, Nq, Sq))
+    l = np.empty((B, Nq, Sq))
+    rc = _load().oracle_attn_keep(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(m), _ptr(l),
+                                  _ptr(keep), B, Nq, Nkv, Sq, Skv, D, Dv, float(scale), threads)
+    if rc != 0:
+        raise ValueError("oracle_attn_keep: invalid arguments")
+    return out, m, l
+
+
+def attn_varlen_keep(q, k, v, cu_q, cu_kv, keep_of, scale: float, threads: int = 0):
+    """Packed attention with a visibility matrix per sequence: keep_of(b, Sq_b, Skv_b) ->
+    bool (Sq_b, Skv_b).  q (Tq,Nq,D), k (Tkv,Nkv,D), v (Tkv,Nkv,Dv) -> out (Tq,Nq,Dv),
+    softmax_max (Nq,Tq), softmax_sum (Nq,Tq).  Each sequence is the dense definition on its
+    own rows (the packing of the varlen operator page)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Tq, Nq, _ = q.shape
+    Dv = v.shape[2]
+    out = np.zeros((Tq, Nq, Dv))
+    m = np.full((Nq, Tq), -np.inf)
+    l = np.zeros((Nq, Tq))
+    q0 = kv0 = 0
+    for b, (qe, ke) in enumerate(zip(np.asarray(cu_q), np.asarray(cu_kv))):
+        qe, ke = int(qe), int(ke)
+        if qe > q0:
+            qb = q[q0:qe].transpose(1, 0, 2)[None]
+            kb = k[kv0:ke].transpose(1, 0, 2)[None]
+            vb = v[kv0:ke].transpose(1, 0, 2)[None]
+            if ke > kv0:
+                o, mm, ll = attn_keep(qb, kb, vb, keep_of(b, qe - q0, ke - kv0), scale, threads)
+                out[q0:qe] = o[0].transpose(1, 0, 2)
+                m[:, q0:qe] = mm[0]
+                l[:, q0:qe] = ll[0]
+        q0, kv0 = qe, ke
     return out, m, l
 
 

@@ -54,27 +54,36 @@ static int allowed(int mask, int64_t i, int64_t j, int64_t pre, int64_t next)
 
 /*
  * One query row against a key/value sequence.
- *   q: D values;  k_row(j) = k + j*kstride;  v_row(j) = v + j*vstride;
- *   keys j in [0, Skv) filtered by allowed(mask, i, j, ...).
- *   s: scratch of Skv doubles.  probs (optional): Skv outputs, 0 for masked keys.
+ *   q: D values;  k_row(j) = k + j*kstride (D values);  v_row(j) = v + j*vstride (Dv values);
+ *   keys j in [0, Skv) filtered by keep_row[j] when keep_row is given, else by
+ *   allowed(mask, i, j, ...).
+ *   s: scratch of Skv doubles.  out: Dv values.  probs (optional): Skv outputs, 0 for
+ *   masked keys.
  */
+static int visible(const unsigned char* keep_row, int mask, int64_t i, int64_t j, int64_t pre,
+                   int64_t next)
+{
+    return keep_row ? keep_row[j] != 0 : allowed(mask, i, j, pre, next);
+}
+
 static void attend_row(const double* q, const double* k, int64_t kstride,
-                       const double* v, int64_t vstride, int64_t Skv, int64_t D,
+                       const double* v, int64_t vstride, int64_t Skv, int64_t D, int64_t Dv,
                        double scale, int mask, int64_t i, int64_t pre, int64_t next,
+                       const unsigned char* keep_row,
                        double* out, double* m_out, double* l_out, double* s, double* probs)
 {
     /* pass 1: scores and their max */
     double m = -INFINITY;
     int64_t n_allowed = 0;
     for (int64_t j = 0; j < Skv; ++j) {
-        if (!allowed(mask, i, j, pre, next)) continue;
+        if (!visible(keep_row, mask, i, j, pre, next)) continue;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += q[d] * k[j * kstride + d];
         s[j] = scale * dot;
         if (s[j] > m) m = s[j];
         ++n_allowed;
     }
-    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    for (int64_t d = 0; d < Dv; ++d) out[d] = 0.0;
     if (probs)
         for (int64_t j = 0; j < Skv; ++j) probs[j] = 0.0;
     if (n_allowed == 0) {
@@ -85,15 +94,15 @@ static void attend_row(const double* q, const double* k, int64_t kstride,
     /* pass 2: exponentials, their sum, and the weighted sum of values */
     double l = 0.0;
     for (int64_t j = 0; j < Skv; ++j) {
-        if (!allowed(mask, i, j, pre, next)) continue;
+        if (!visible(keep_row, mask, i, j, pre, next)) continue;
         double e = exp(s[j] - m);
         l += e;
-        for (int64_t d = 0; d < D; ++d) out[d] += e * v[j * vstride + d];
+        for (int64_t d = 0; d < Dv; ++d) out[d] += e * v[j * vstride + d];
     }
-    for (int64_t d = 0; d < D; ++d) out[d] /= l;
+    for (int64_t d = 0; d < Dv; ++d) out[d] /= l;
     if (probs)
         for (int64_t j = 0; j < Skv; ++j)
-            if (allowed(mask, i, j, pre, next)) probs[j] = exp(s[j] - m) / l;
+            if (visible(keep_row, mask, i, j, pre, next)) probs[j] = exp(s[j] - m) / l;
     *m_out = m;
     *l_out = l;
 }
@@ -137,7 +146,7 @@ int oracle_attn(const double* q, const double* k, const double* v, double* out,
             const double* vb = v + (b * Nkv + g) * Skv * D;
             double* o = out + ((b * Nq + h) * Sq + i) * D;
             double* pr = probs ? probs + ((b * Nq + h) * Sq + i) * Skv : NULL;
-            attend_row(qr, kb, D, vb, D, Skv, D, scale, mask, i, pre, next,
+            attend_row(qr, kb, D, vb, D, Skv, D, D, scale, mask, i, pre, next, NULL,
                        o, smax + r, ssum + r, s, pr);
         }
         free(s);
@@ -180,9 +189,43 @@ int oracle_attn_varlen(const double* q, const double* k, const double* v, double
             int64_t Skv = cu_kv[b] - kv0;
             const double* kb = k + (kv0 * Nkv + g) * D;
             const double* vb = v + (kv0 * Nkv + g) * D;
-            attend_row(q + (t * Nq + h) * D, kb, Nkv * D, vb, Nkv * D, Skv, D, scale, mask,
-                       t - q0, pre, next, out + (t * Nq + h) * D, smax + h * Tq + t,
+            attend_row(q + (t * Nq + h) * D, kb, Nkv * D, vb, Nkv * D, Skv, D, D, scale, mask,
+                       t - q0, pre, next, NULL, out + (t * Nq + h) * D, smax + h * Tq + t,
                        ssum + h * Tq + t, s, NULL);
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * Dense attention with an explicit visibility matrix and a value head dim of its own.
+ *   q [B][Nq][Sq][D], k [B][Nkv][Skv][D], v [B][Nkv][Skv][Dv], out [B][Nq][Sq][Dv],
+ *   smax/ssum [B][Nq][Sq]; keep [B][Sq][Skv] bytes (nonzero: key j visible from query i),
+ *   shared by the heads of a batch entry.  Each row is the plain definition over its
+ *   visible keys; a row with none gives out = 0, max = -inf, sum = 0.
+ */
+int oracle_attn_keep(const double* q, const double* k, const double* v, double* out,
+                     double* smax, double* ssum, const unsigned char* keep,
+                     int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                     int64_t Dv, double scale, int nthreads)
+{
+    if (B < 0 || Nq <= 0 || Nkv <= 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0) return -1;
+    if (Nq % Nkv != 0 || !keep) return -1;
+    const int64_t G = Nq / Nkv;
+    const int64_t rows = B * Nq * Sq;
+    int nt = pick_threads(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < rows; ++r) {
+            int64_t i = r % Sq, h = (r / Sq) % Nq, b = r / (Sq * Nq);
+            int64_t g = h / G;
+            attend_row(q + ((b * Nq + h) * Sq + i) * D, k + (b * Nkv + g) * Skv * D, D,
+                       v + (b * Nkv + g) * Skv * Dv, Dv, Skv, D, Dv, scale, OR_MASK_NONE, i, 0, 0,
+                       keep + (b * Sq + i) * Skv, out + ((b * Nq + h) * Sq + i) * Dv, smax + r,
+                       ssum + r, s, NULL);
         }
         free(s);
     }

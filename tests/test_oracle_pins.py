@@ -281,6 +281,80 @@ def test_varlen_rejects_bad_offsets():
 
 
 # ------------------------------------------------------------------------------------
+# explicit visibility matrices: bottom-right alignment, prefix, explicit masks, Dv < D
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Sq,Skv", [(5, 9), (9, 5), (7, 7), (1, 6), (6, 1)])
+def test_keep_bottom_right_causal_is_the_shifted_lower_triangle(Sq, Skv):
+    """Bottom-right causal = ones.tril(diagonal = Skv - Sq) (the lower triangle whose
+    diagonal ends at the last query / last key pair); equal to top-left when Sq = Skv."""
+    want = np.tril(np.ones((Sq, Skv), dtype=bool), k=Skv - Sq)
+    assert np.array_equal(oracle.keep_band(Sq, Skv, 1 << 62, 0, "bottom_right"), want)
+    tl = np.tril(np.ones((Sq, Skv), dtype=bool))
+    assert np.array_equal(oracle.keep_band(Sq, Skv, 1 << 62, 0, "top_left"), tl)
+    # a bottom-right band is the top-left band with next and pre shifted by Skv - Sq
+    assert np.array_equal(oracle.keep_band(Sq, Skv, 2, 1, "bottom_right"),
+                          _band_keep(Sq, Skv, 2 - (Skv - Sq), 1 + (Skv - Sq)))
+
+
+@pytest.mark.parametrize("Sq,Skv,P", [(6, 10, 4), (6, 10, 0), (10, 6, 3), (10, 6, 0), (8, 8, 8)])
+def test_keep_prefix_causal_counts(Sq, Skv, P):
+    """Row i sees the first P keys and the bottom-right causal keys: that is
+    clip(max(P, i + Skv - Sq + 1), 0, Skv) keys, all of them a prefix of the key range."""
+    keep = oracle.keep_prefix_causal(Sq, Skv, P)
+    for i in range(Sq):
+        n = min(Skv, max(P, i + Skv - Sq + 1, 0))
+        assert keep[i].sum() == n and keep[i, :n].all()
+
+
+@pytest.mark.parametrize("Dv", [5, 3])
+def test_attn_keep_matches_torch_sdpa_fp64(Dv):
+    """Random explicit masks (some rows empty), GQA, and a value head dim Dv <= D."""
+    rng = np.random.default_rng(14)
+    B, Nq, Nkv, Sq, Skv, D = 2, 4, 2, 9, 13, 5
+    q, k, v = _rand(rng, B, Nq, Sq, D), _rand(rng, B, Nkv, Skv, D), _rand(rng, B, Nkv, Skv, Dv)
+    keep = rng.random((Sq, Skv)) < 0.4
+    keep[3] = False
+    out, m, l = oracle.attn_keep(q, k, v, keep, 0.37)
+    rows = keep.any(1)
+    want = _torch_sdpa(q, k, v, 0.37, keep)
+    assert out.shape == (B, Nq, Sq, Dv)
+    assert np.max(np.abs(out[:, :, rows] - want[:, :, rows])) < TOL
+    wm, wl = _torch_stats(q, k, 0.37, keep)
+    assert np.max(np.abs(m[:, :, rows] - wm[:, :, rows])) < TOL
+    assert np.max(np.abs(l[:, :, rows] / wl[:, :, rows] - 1)) < TOL
+    assert np.all(out[:, :, 3] == 0) and np.all(m[:, :, 3] == -np.inf) and np.all(l[:, :, 3] == 0)
+
+
+def test_attn_keep_zero_query_means_over_prefix_causal():
+    rng = np.random.default_rng(15)
+    Sq, Skv, P = 7, 10, 5
+    q = np.zeros((1, 2, Sq, 4))
+    k, v = _rand(rng, 1, 2, Skv, 4), _rand(rng, 1, 2, Skv, 4)
+    keep = oracle.keep_prefix_causal(Sq, Skv, P)
+    out, m, l = oracle.attn_keep(q, k, v, keep, 0.5)
+    for i in range(Sq):
+        js = np.nonzero(keep[i])[0]
+        assert np.all(l[:, :, i] == len(js)) and np.all(m[:, :, i] == 0)
+        assert np.max(np.abs(out[:, :, i] - v[:, :, js].mean(axis=2))) < TOL
+
+
+def test_attn_varlen_keep_equals_positional_masks():
+    """The per-sequence visibility path with top-left band matrices equals the positional
+    band path (two independent routes through the oracle)."""
+    rng = np.random.default_rng(16)
+    lq, lk = np.array([5, 0, 7, 3]), np.array([6, 4, 2, 3])
+    q, k, v = _rand(rng, lq.sum(), 4, 3), _rand(rng, lk.sum(), 2, 3), _rand(rng, lk.sum(), 2, 3)
+    cq, ck = np.cumsum(lq), np.cumsum(lk)
+    a = oracle.attn_varlen(q, k, v, cq, ck, 0.8, "band", 2, 1)
+    b = oracle.attn_varlen_keep(q, k, v, cq, ck, lambda bi, sq, sk: oracle.keep_band(sq, sk, 2, 1),
+                                0.8)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(np.where(np.isinf(x), 0, x) - np.where(np.isinf(y), 0, y))) < TOL
+        assert np.array_equal(np.isinf(x), np.isinf(y))
+
+
+# ------------------------------------------------------------------------------------
 # merge of partial results (ring-attention update)
 # ------------------------------------------------------------------------------------
 
