@@ -26,13 +26,21 @@
  *      BSND: ((b*S + s)*N + n)*D + d
  *      BSH : same memory as BSND with H = N*D
  *      SBH : ((s*B + b)*N + n)*D + d          (H = N*D; head n owns columns n*D..n*D+D-1)
- *  - Masks act on sequence-local positions i (query) and j (key), top-left aligned:
- *      MIATTN_MASK_NONE   : every key is visible;
- *      MIATTN_MASK_CAUSAL : j <= i;
- *      MIATTN_MASK_BAND   : -pre_tokens <= j - i <= next_tokens  (pre/next signed; the band
- *                           must be non-empty: pre_tokens + next_tokens >= 0, following the
- *                           band rule in the aclnnFlashAttentionVarLenScore constraints).
- *    Tiles that no visible pair touches are never loaded.
+ *  - Masks act on sequence-local positions i (query) and j (key):
+ *      MIATTN_MASK_NONE      : every key is visible;
+ *      MIATTN_MASK_CAUSAL    : j <= i                                  (top-left aligned);
+ *      MIATTN_MASK_BAND      : -pre_tokens <= j - i <= next_tokens     (top-left; pre/next
+ *                              signed; the band must be non-empty: pre_tokens + next_tokens
+ *                              >= 0, the band rule of the aclnnFlashAttentionVarLenScore
+ *                              constraints);
+ *      MIATTN_MASK_CAUSAL_BR : j - i <= Skv - Sq                        (bottom-right aligned:
+ *                              the diagonal ends at the last query / last key of the
+ *                              sequence; the reading of that page's sparseMode 3, which
+ *                              needs Sq <= Skv so that no row is empty);
+ *      MIATTN_MASK_BAND_BR   : -pre_tokens <= j - i - (Skv - Sq) <= next_tokens.
+ *    Sq / Skv are the lengths of each sequence.  Tiles that no visible pair touches are
+ *    never loaded.  attn_fwd_masked / attn_fwd_varlen_masked add a prefix and an explicit
+ *    mask tensor.
  *  - Softmax statistics (fp32, optional, each may be NULL):
  *      softmax_max[row] = max over visible keys of scale * q.k   (natural-log units);
  *      softmax_sum[row] = sum over visible keys of exp(scale * q.k - softmax_max[row]).
@@ -63,7 +71,13 @@ typedef enum {
 /* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
 typedef enum { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2, MIATTN_F64 = 3 } miattn_dtype_t;
 typedef enum { MIATTN_BNSD = 0, MIATTN_BSND = 1, MIATTN_BSH = 2, MIATTN_SBH = 3 } miattn_layout_t;
-typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 2 } miattn_mask_t;
+typedef enum {
+    MIATTN_MASK_NONE = 0,
+    MIATTN_MASK_CAUSAL = 1,
+    MIATTN_MASK_BAND = 2,
+    MIATTN_MASK_CAUSAL_BR = 3,
+    MIATTN_MASK_BAND_BR = 4
+} miattn_mask_t;
 
 /*
  * attn_fwd - dense attention forward over a batch of equal-length sequences.
@@ -82,7 +96,7 @@ typedef enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BAND = 
  *   D: 32, 64, 96 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
  *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
- *   Pass pre_tokens/next_tokens for MIATTN_MASK_BAND; they are ignored otherwise.
+ *   Pass pre_tokens/next_tokens for the band modes; they are ignored otherwise.
  *   Returns MIATTN_OK or an error status; nothing is enqueued on error.
  */
 miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
@@ -192,6 +206,44 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
                                        int64_t Nq, int64_t Nkv, int64_t D,
                                        miattn_dtype_t dtype, float scale,
                                        miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                       void* stream);
+
+/*
+ * attn_fwd_masked / attn_fwd_varlen_masked - attn_fwd / attn_fwd_varlen with the rest of
+ * the mask surface of aclnnFlashAttentionVarLenScore (约束说明: sparseMode, prefixOptional,
+ * attenMaskOptional), under these readings (the page's mode definitions were not part of
+ * the extracted text):
+ *   prefix: DEVICE int64 [B] or NULL.  Keys j < prefix[b] are visible from every row of
+ *     sequence b, in addition to the causal keys (sparseMode 6 is prefix + bottom-right
+ *     causal: use mask MIATTN_MASK_CAUSAL_BR).  Only with MIATTN_MASK_CAUSAL or
+ *     MIATTN_MASK_CAUSAL_BR (else MIATTN_ERR_MASK); values are clamped to [0, Skv].
+ *   atten_mask: DEVICE uint8 [Sq, Skv] (dense) or [max_seqlen_q, max_seqlen_kv] (packed),
+ *     row-major, or NULL.  A nonzero byte at (i, j) removes key j from query i (sequence-local
+ *     positions, top-left), on top of the mask mode and the prefix; it is shared by all
+ *     batch entries / sequences and heads.  The page forbids rows that are entirely masked;
+ *     here such a row gives the empty result (out 0, max -inf, sum 0).
+ *   bf16 / fp16 with atten_mask run on the matrix cores like attn_fwd when the mask pointer
+ *   is 4-byte aligned, its row length (Skv, resp. max_seqlen_kv) a multiple of 4 and its
+ *   size under 2^31 bytes; otherwise (and for fp32) the forward runs in fp32 arithmetic on
+ *   the vector ALUs (inputs widened on load, output rounded to the input type).  Other
+ *   arguments, limits and errors as attn_fwd / attn_fwd_varlen.
+ */
+miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
+                                float* softmax_max, float* softmax_sum,
+                                int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                const int64_t* prefix, const uint8_t* atten_mask, void* stream);
+
+miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* out,
+                                       float* softmax_max, float* softmax_sum,
+                                       const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                       int64_t B, int64_t Tq, int64_t Tkv,
+                                       int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       miattn_dtype_t dtype, float scale,
+                                       miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                       const int64_t* prefix, const uint8_t* atten_mask,
                                        void* stream);
 
 /*

@@ -27,10 +27,11 @@ STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATT
           7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE"}
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
-MASKS = {"none": 0, "causal": 1, "band": 2}
+MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-           "attn_lse_merge", "sparse_csr_attn", "miattn_status_str")
+           "attn_fwd_masked", "attn_fwd_varlen_masked", "attn_lse_merge", "sparse_csr_attn",
+           "miattn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -44,10 +45,13 @@ _lib.attn_fwd.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P
 _lib.attn_fwd_varlen.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_update.argtypes = [_P] * 9 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_varlen_update.argtypes = [_P] * 11 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
+_lib.attn_fwd_masked.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P, _P, _P]
+_lib.attn_fwd_varlen_masked.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P, _P, _P]
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
 for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
-           _lib.attn_lse_merge, _lib.sparse_csr_attn):
+           _lib.attn_fwd_masked, _lib.attn_fwd_varlen_masked, _lib.attn_lse_merge,
+           _lib.sparse_csr_attn):
     _f.restype = ctypes.c_int
 _lib.miattn_status_str.argtypes = [ctypes.c_int]
 _lib.miattn_status_str.restype = ctypes.c_char_p
@@ -124,6 +128,28 @@ def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, 
                                        _enum(dtype, DTYPES), scale, _enum(mask, MASKS),
                                        pre_tokens, next_tokens, _stream(stream)),
            "attn_fwd_varlen_update")
+
+
+def attn_fwd_masked(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, dtype,
+                    layout, scale, mask, pre_tokens=0, next_tokens=0, prefix=None,
+                    atten_mask=None, stream=None):
+    _check(_lib.attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                                _ptr(softmax_sum), B, Nq, Nkv, Sq, Skv, D, _enum(dtype, DTYPES),
+                                _enum(layout, LAYOUTS), scale, _enum(mask, MASKS), pre_tokens,
+                                next_tokens, _ptr(prefix), _ptr(atten_mask), _stream(stream)),
+           "attn_fwd_masked")
+
+
+def attn_fwd_varlen_masked(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+                           B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, dtype, scale,
+                           mask, pre_tokens=0, next_tokens=0, prefix=None, atten_mask=None,
+                           stream=None):
+    _check(_lib.attn_fwd_varlen_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                                       _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+                                       B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
+                                       _enum(dtype, DTYPES), scale, _enum(mask, MASKS),
+                                       pre_tokens, next_tokens, _ptr(prefix), _ptr(atten_mask),
+                                       _stream(stream)), "attn_fwd_varlen_masked")
 
 
 def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, out_max,

@@ -50,11 +50,38 @@ __device__ inline TileCoord decode_tile(const FaParams& p, int L, int tile_m)
     return c;
 }
 
-// Visible key range [lo, hi) of query rows [r0, r1) under the band -pre <= j - i <= next.
-__device__ inline void key_range(const FaParams& p, int r0, int r1, int len_kv, int& lo, int& hi)
+// The visible keys of one sequence: row i sees key j when -pre <= j - i <= next (the band,
+// already shifted to the sequence's diagonal) or j < pfx (the prefix).  The prefix is only
+// given with an unbounded pre, so every row's visible keys form one range
+// [max(0, i - pre), min(len_kv, max(i + next, pfx - 1) + 1)).
+struct Band {
+    int64_t pre, next, pfx;
+};
+
+__device__ inline Band band_of(const FaParams& p, const TileCoord& tc)
 {
-    int64_t a = (int64_t)r0 - p.pre;
-    int64_t z = (int64_t)(r1 - 1) + p.next + 1;
+    const int64_t off = p.align_br ? (int64_t)tc.len_kv - tc.len_q : 0;
+    Band bd;
+    bd.pre = p.pre - off;
+    bd.next = p.next + off;
+    bd.pfx = 0;
+    if (p.prefix) {
+        const int64_t x = p.prefix[tc.b];
+        bd.pfx = x < 0 ? 0 : (x > tc.len_kv ? tc.len_kv : x);
+    }
+    return bd;
+}
+
+// Visible key range [lo, hi) of query rows [r0, r1).
+__device__ inline void key_range(const Band& bd, int r0, int r1, int len_kv, int& lo, int& hi)
+{
+    int64_t a = (int64_t)r0 - bd.pre;
+    int64_t z = (int64_t)(r1 - 1) + bd.next;
+    if (bd.pfx > 0) {
+        a = a < 0 ? a : 0;
+        z = z > bd.pfx - 1 ? z : bd.pfx - 1;
+    }
+    z += 1;
     lo = a < 0 ? 0 : (a > len_kv ? len_kv : (int)a);
     hi = z < 0 ? 0 : (z > len_kv ? len_kv : (int)z);
 }

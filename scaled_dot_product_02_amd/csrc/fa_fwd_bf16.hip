@@ -121,11 +121,32 @@ __device__ inline float pair_sum(float x)
 // the key order of the P operand taken from the S^T accumulator layout.
 __device__ inline int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
+// Packs the 8 mask words of one lane and tile (bytes for keys 32b + 8g + 4hf + e, word
+// 4b + g, byte e) into bit 16b + 4g + e: set where the byte is nonzero (masked out).
+__device__ inline unsigned pack_mask(const unsigned (&w)[8])
+{
+    unsigned bits = 0;
+    #pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        unsigned x = w[k];
+        x |= x >> 4;
+        x |= x >> 2;
+        x |= x >> 1;                                        // bit 8e: byte e nonzero
+        x &= 0x01010101u;
+        bits |= ((x * 0x01020408u) >> 24 & 0xfu) << (4 * k);  // bit 8e -> bit 24 + e
+    }
+    return bits;
+}
+
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
-template <int D, typename T, bool UPDATE>
+// MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
+// masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
+template <int D, typename T, bool UPDATE, bool MASKED>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D>;
+    constexpr int PF = MASKED ? 2 : ::miattn::PF;
+    constexpr int LDSD = MASKED ? 3 : ::miattn::LDSD;
     using X8 = typename Elem<T>::v8;   // one MFMA operand: 8 elements
     using X4 = typename Elem<T>::v4;
     __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF * C::KBUF];
@@ -152,7 +173,8 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 
     // ---- key tiles of the workgroup
     int kv_lo, kv_hi;
-    key_range(p, i0, i1, len_kv, kv_lo, kv_hi);
+    const Band bd = band_of(p, tc);
+    key_range(bd, i0, i1, len_kv, kv_lo, kv_hi);
     const int T0 = kv_lo / BN;
     const int T1 = kv_lo < kv_hi ? (kv_hi + BN - 1) / BN : T0;
     if constexpr (UPDATE) {
@@ -180,19 +202,20 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     int jlo = 0, jhi = -1;          // keys [jlo, jhi] are visible from this lane's row
     if (rb < re) {
         int lo, hi;
-        key_range(p, rb, re, len_kv, lo, hi);
+        key_range(bd, rb, re, len_kv, lo, hi);
         if (lo < hi) {
             w_lo = lo / BN;
             w_hi = (hi + BN - 1) / BN;
         }
-        const int64_t flo = (int64_t)(re - 1) - p.pre;   // first key seen by every row
-        const int64_t fhi = (int64_t)rb + p.next;         // last key seen by every row
+        const int64_t flo = bd.pfx > 0 ? 0 : (int64_t)(re - 1) - bd.pre;   // first key seen by every row
+        const int64_t fhi = max((int64_t)rb + bd.next, bd.pfx - 1);        // last key seen by every row
         const int64_t fl = flo <= 0 ? 0 : (flo + BN - 1) / BN;
         const int64_t fh = fhi < 0 ? 0 : (min(fhi, (int64_t)len_kv - 1) + 1) / BN;
         full_lo = (int)min(fl, (int64_t)1 << 30);
         full_hi = (int)fh;
         const int qi = rb + lq;
-        const int64_t a = (int64_t)qi - p.pre, z = (int64_t)qi + p.next;
+        const int64_t a = bd.pfx > 0 ? 0 : (int64_t)qi - bd.pre;
+        const int64_t z = max((int64_t)qi + bd.next, bd.pfx - 1);
         jlo = (int)max((int64_t)0, min(a, (int64_t)len_kv));
         jhi = (int)max((int64_t)-1, min(z, (int64_t)len_kv - 1));
     }
@@ -242,6 +265,20 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
         const int n = __builtin_amdgcn_readfirstlane((int)bytes);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
+    };
+    // explicit mask: this lane's row, words of one tile in flight, bits of the current one
+    unsigned mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned mbits = 0;
+    __amdgpu_buffer_rsrc_t rmask;
+    uint32_t moff = 0;
+    if constexpr (MASKED) {
+        rmask = rsrc(p.amask, (int64_t)p.Sq * p.amask_ld);
+        moff = (uint32_t)((int64_t)min(rb + lq, p.Sq - 1) * p.amask_ld) + 4 * hf;
+    }
+    auto load_mask = [&](int t) {
+        #pragma unroll
+        for (int k = 0; k < 8; ++k)
+            mw[k] = __builtin_amdgcn_raw_buffer_load_b32(rmask, moff + t * BN + 32 * (k >> 2) + 8 * (k & 3), 0, 0);
     };
     auto load_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
         const int j0 = t * BN;
@@ -331,6 +368,13 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     // ---- online softmax of tile t; leaves bf16 probabilities in pp
     auto softmax = [&](int t, f32x16 (&s)[NKB], X8 (&pp)[2 * NKB]) {
         const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
+        if constexpr (MASKED) {
+            #pragma unroll
+            for (int b = 0; b < NKB; ++b)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if ((mbits >> (16 * b + i)) & 1u) s[b][i] = -INFINITY;
+        }
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
             for (int b = 0; b < NKB; ++b)
@@ -391,6 +435,10 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     X8 pp[2 * NKB];
     auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], u32x4 (&ld)[C::SREG],
                     u32x4 (&sto)[C::SREG]) {
+        if constexpr (MASKED) {
+            mbits = pack_mask(mw);             // mask of tile t, read one step earlier
+            if (t + 1 < T1) load_mask(t + 1);
+        }
         load_tile(t + PF, ld);
         if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
         if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
@@ -403,6 +451,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     if (T0 < T1) {
         // Q and the first two tiles in one memory round trip; the wait also drains Q, so
         // no wait on it is left for the key loop (where it would also wait for prefetches)
+        if constexpr (MASKED) load_mask(T0);
         load_tile(T0, stA);
         load_tile(T0 + 1, stB);
         __builtin_amdgcn_s_waitcnt(0);
@@ -477,15 +526,15 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     }
 }
 
-template <typename T, bool UPDATE>
+template <typename T, bool UPDATE, bool MASKED>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(NT);
     switch (D) {
-    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, T, UPDATE>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, T, UPDATE>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -496,8 +545,12 @@ hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream)
 {
     const bool upd = p.prev_out != nullptr;
-    if (f16) return upd ? launch_t<_Float16, true>(p, D, stream) : launch_t<_Float16, false>(p, D, stream);
-    return upd ? launch_t<__bf16, true>(p, D, stream) : launch_t<__bf16, false>(p, D, stream);
+    if (p.amask) {   // the masked variant has no fused update
+        if (upd) return hipErrorInvalidValue;
+        return f16 ? launch_t<_Float16, false, true>(p, D, stream) : launch_t<__bf16, false, true>(p, D, stream);
+    }
+    if (f16) return upd ? launch_t<_Float16, true, false>(p, D, stream) : launch_t<_Float16, false, false>(p, D, stream);
+    return upd ? launch_t<__bf16, true, false>(p, D, stream) : launch_t<__bf16, false, false>(p, D, stream);
 }
 
 }  // namespace miattn

@@ -1,8 +1,10 @@
-// Attention forward for fp32 inputs (fp32 arithmetic on the vector ALUs).
+// Attention forward in fp32 arithmetic on the vector ALUs.
 //
-// Same operation, batches, masks and statistics as the bf16 MFMA kernel; fp32 is the
-// slower path the SDPA-pitfalls blog describes for FlashAttention backends, and it is
-// kept exact to fp32 rounding rather than rounded through bf16.
+// Same operation, batches, masks and statistics as the MFMA kernel.  It serves fp32
+// inputs (the slower path the SDPA-pitfalls blog describes for FlashAttention backends,
+// kept exact to fp32 rounding rather than rounded through bf16), and any input type when
+// an explicit mask tensor is given (inputs widened to fp32 on load, output rounded to the
+// input type).
 //
 // One workgroup = one wave = 64 query rows, one row per lane; K/V tiles of 32 keys are
 // staged in LDS and read as broadcasts.  Keys are consumed in chunks of 16 with one
@@ -16,8 +18,30 @@ constexpr int BM = kF32TileM;  // query rows per workgroup (one per lane)
 constexpr int BN = 32;         // keys per LDS tile
 constexpr int CH = 16;         // keys per softmax chunk
 
-// UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
-template <int D, bool UPDATE>
+__device__ inline float4 load4(const float* x) { return *(const float4*)x; }
+__device__ inline float4 load4(const __bf16* x)
+{
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+    const v4 y = *(const v4*)x;
+    return float4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+}
+__device__ inline float4 load4(const _Float16* x)
+{
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+    const v4 y = *(const v4*)x;
+    return float4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+}
+__device__ inline void store4(float* x, float4 v) { *(float4*)x = v; }
+template <typename T>
+__device__ inline void store4(T* x, float4 v)
+{
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    *(v4*)x = v4{(T)v.x, (T)v.y, (T)v.z, (T)v.w};
+}
+
+// T: input / output type; UPDATE = true: the epilogue merges the partial result into
+// p.prev_* (ring update); MASKED = true: p.amask removes keys as well.
+template <typename T, int D, bool UPDATE, bool MASKED>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
 {
     __shared__ __attribute__((aligned(16))) float Ks[BN * D];
@@ -30,19 +54,23 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
     const int i1 = min(i0 + BM, tc.len_q);
     const int qi = i0 + lane;
 
-    const float* qg = (const float*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
-    const float* kg = (const float*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
-    const float* vg = (const float*)p.v + (int64_t)tc.b * p.v_sb + tc.kv0 * p.v_ss + (int64_t)tc.kvh * p.v_sh;
-    float* og = (float*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
+    const T* qg = (const T*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
+    const T* kg = (const T*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
+    const T* vg = (const T*)p.v + (int64_t)tc.b * p.v_sb + tc.kv0 * p.v_ss + (int64_t)tc.kvh * p.v_sh;
+    T* og = (T*)p.out + (int64_t)tc.b * p.o_sb + tc.q0 * p.o_ss + (int64_t)tc.h * p.o_sh;
     const int64_t st_base = (int64_t)tc.b * p.st_sb + (int64_t)tc.h * p.st_sh + tc.q0;
 
+    const Band bd = band_of(p, tc);
     int kv_lo, kv_hi;
-    key_range(p, i0, i1, tc.len_kv, kv_lo, kv_hi);
+    key_range(bd, i0, i1, tc.len_kv, kv_lo, kv_hi);
+    // explicit mask row of this lane (rows / keys outside the mask count as masked)
+    const bool mrow = MASKED && qi < p.Sq;
+    const uint8_t* arow = MASKED ? p.amask + (int64_t)(mrow ? qi : 0) * p.amask_ld : nullptr;
 
     float q[D], o[D];
     #pragma unroll
     for (int d = 0; d < D; d += 4) {
-        float4 x = qi < tc.len_q ? *(const float4*)(qg + (int64_t)qi * p.q_ss + d) : float4{0, 0, 0, 0};
+        float4 x = qi < tc.len_q ? load4(qg + (int64_t)qi * p.q_ss + d) : float4{0, 0, 0, 0};
         q[d] = x.x; q[d + 1] = x.y; q[d + 2] = x.z; q[d + 3] = x.w;
         o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
     }
@@ -54,8 +82,8 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
             const int row = c / (D / 4), col = 4 * (c % (D / 4));
             float4 kx{0, 0, 0, 0}, vx{0, 0, 0, 0};
             if (j0 + row < tc.len_kv) {
-                kx = *(const float4*)(kg + (int64_t)(j0 + row) * p.k_ss + col);
-                vx = *(const float4*)(vg + (int64_t)(j0 + row) * p.v_ss + col);
+                kx = load4(kg + (int64_t)(j0 + row) * p.k_ss + col);
+                vx = load4(vg + (int64_t)(j0 + row) * p.v_ss + col);
             }
             *(float4*)(Ks + row * D + col) = kx;
             *(float4*)(Vs + row * D + col) = vx;
@@ -73,7 +101,8 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
                 for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], kr[d], acc);
                 const int j = j0 + c0 + jj;
                 const int64_t dj = (int64_t)j - qi;
-                const bool vis = j < tc.len_kv && dj <= p.next && -dj <= p.pre;
+                bool vis = j < tc.len_kv && ((dj <= bd.next && -dj <= bd.pre) || j < bd.pfx);
+                if constexpr (MASKED) vis = vis && mrow && j < p.Skv && arow[j] == 0;
                 s[jj] = vis ? acc * p.scale_log2 : -INFINITY;
                 mx = fmaxf(mx, s[jj]);
             }
@@ -117,44 +146,56 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
             }
             m_out = m;
         }
-        float* orow = og + (int64_t)qi * p.o_ss;
+        T* orow = og + (int64_t)qi * p.o_ss;
         #pragma unroll
         for (int d = 0; d < D; d += 4) {
             float4 y{o[d] * wc, o[d + 1] * wc, o[d + 2] * wc, o[d + 3] * wc};
             if constexpr (UPDATE) {
                 // an empty prior (weight 0) is not read: its buffer may hold anything
                 if (wp != 0.f) {
-                    const float4 po = *(const float4*)((const float*)p.prev_out + (orow - (float*)p.out) + d);
+                    const float4 po = load4((const T*)p.prev_out + (orow - (T*)p.out) + d);
                     y = float4{__builtin_fmaf(po.x, wp, y.x), __builtin_fmaf(po.y, wp, y.y),
                                __builtin_fmaf(po.z, wp, y.z), __builtin_fmaf(po.w, wp, y.w)};
                 }
             }
-            *(float4*)(orow + d) = y;
+            store4(orow + d, y);
         }
         if (p.smax) p.smax[st_base + qi] = m_out;
         if (p.ssum) p.ssum[st_base + qi] = l_out;
     }
 }
 
-template <bool UPDATE>
+template <typename T, bool UPDATE, bool MASKED>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(64);
     switch (D) {
-    case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<32, UPDATE>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<64, UPDATE>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<96, UPDATE>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<128, UPDATE>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 32, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 64, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 96, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, UPDATE, MASKED>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_type(const FaParams& p, int D, hipStream_t stream)
+{
+    if (p.amask)
+        return p.prev_out ? launch_t<T, true, true>(p, D, stream) : launch_t<T, false, true>(p, D, stream);
+    return p.prev_out ? launch_t<T, true, false>(p, D, stream) : launch_t<T, false, false>(p, D, stream);
+}
+
 }  // namespace
 
-hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream)
+// dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the C-ABI enum values); bf16 / fp16 only with a mask
+hipError_t launch_fa_fwd_f32(const FaParams& p, int D, int dtype, hipStream_t stream)
 {
-    return p.prev_out ? launch_t<true>(p, D, stream) : launch_t<false>(p, D, stream);
+    if (dtype == 1 && p.amask) return launch_type<__bf16>(p, D, stream);
+    if (dtype == 2 && p.amask) return launch_type<_Float16>(p, D, stream);
+    if (dtype == 0) return launch_type<float>(p, D, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace miattn

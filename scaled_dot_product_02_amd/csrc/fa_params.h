@@ -32,7 +32,13 @@ struct FaParams {
     int32_t Sq, Skv;            // dense: lengths; packed: upper bounds (max_seqlen)
     int32_t n_levels;           // q tiles per sequence at the longest length
     int32_t n_slots;            // workgroups in the grid (multiple of 8 * group)
-    int64_t pre, next;          // visible band: -pre <= j - i <= next (clamped)
+    int64_t pre, next;          // visible band: -pre <= j - i - off <= next (clamped)
+    int32_t align_br;           // off = len_kv - len_q of the sequence (bottom-right), else 0
+    const int64_t* prefix;      // device [B] or null: keys j < prefix[b] are seen by every row
+                                // (only with pre unbounded, so the visible keys stay a range)
+    const uint8_t* amask;       // device [Sq][Skv] bytes or null: nonzero = masked out,
+                                // sequence-local positions (VALU kernel only)
+    int64_t amask_ld;           // row stride of amask
     float scale;                // softmax scale
     float scale_log2;           // scale * log2(e)
 };
@@ -68,7 +74,9 @@ struct SparseParams {
 // the MFMA forward for bf16 (f16 = false) or fp16 (f16 = true) inputs; both forwards
 // merge into p.prev_* when p.prev_out is set
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
-hipError_t launch_fa_fwd_f32(const FaParams& p, int D, hipStream_t stream);
+// the VALU forward: fp32 inputs (dtype 0), or any input type (0, 1 = bf16, 2 = fp16) with
+// an explicit mask (p.amask)
+hipError_t launch_fa_fwd_f32(const FaParams& p, int D, int dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream);
 

@@ -25,15 +25,19 @@ Strides strides_of(int layout, int64_t B, int64_t N, int64_t S, int64_t D)
     }
 }
 
-miattn_status_t check_mask(int mask, int64_t pre, int64_t next, int64_t& pre_c, int64_t& next_c)
+// Band of a mask mode; the bottom-right modes shift it per sequence (FaParams::align_br).
+miattn_status_t check_mask(int mask, int64_t pre, int64_t next, FaParams& p)
 {
     auto clamp = [](int64_t x) { return x > kTokensClamp ? kTokensClamp : (x < -kTokensClamp ? -kTokensClamp : x); };
+    int64_t& pre_c = p.pre;
+    int64_t& next_c = p.next;
+    p.align_br = mask == MIATTN_MASK_CAUSAL_BR || mask == MIATTN_MASK_BAND_BR;
     if (mask == MIATTN_MASK_NONE) {
         pre_c = next_c = kTokensClamp;
-    } else if (mask == MIATTN_MASK_CAUSAL) {
+    } else if (mask == MIATTN_MASK_CAUSAL || mask == MIATTN_MASK_CAUSAL_BR) {
         pre_c = kTokensClamp;
         next_c = 0;
-    } else if (mask == MIATTN_MASK_BAND) {
+    } else if (mask == MIATTN_MASK_BAND || mask == MIATTN_MASK_BAND_BR) {
         // the band must be non-empty: pre + next >= 0 (evaluated without overflow)
         if ((__int128)pre + (__int128)next < 0) return MIATTN_ERR_MASK;
         pre_c = clamp(pre);
@@ -70,12 +74,16 @@ miattn_status_t size_grid(FaParams& p, int64_t max_len_q, int tile_m)
 
 miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
 {
-    const bool mfma = dtype == MIATTN_BF16 || dtype == MIATTN_F16;
+    // an explicit mask stays on the matrix cores when its rows are 4-byte aligned words
+    // (read as 32-bit buffer loads with 32-bit offsets); otherwise it takes the VALU kernel
+    const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
+                                         (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
+    const bool mfma = (dtype == MIATTN_BF16 || dtype == MIATTN_F16) && mask_words;
     const int tile_m = mfma ? kBf16TileM : kF32TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
     hipError_t e = mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
-                        : launch_fa_fwd_f32(p, (int)D, stream);
+                        : launch_fa_fwd_f32(p, (int)D, dtype, stream);
     return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 
@@ -110,7 +118,8 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
                           void* out, float* softmax_max, float* softmax_sum,
                           int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
                           int dtype, int layout, float scale,
-                          int mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+                          int mask, int64_t pre_tokens, int64_t next_tokens,
+                          const int64_t* prefix, const uint8_t* atten_mask, void* stream)
 {
     if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -121,10 +130,15 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     if (B * Sq > (int64_t(1) << 31) || B * Skv > (int64_t(1) << 31)) return MIATTN_ERR_SHAPE;
     if (Nq % Nkv != 0) return MIATTN_ERR_GQA_RATIO;
     FaParams p{};
-    st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
+    st = check_mask(mask, pre_tokens, next_tokens, p);
     if (st != MIATTN_OK) return st;
+    if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
+        return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
     if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    p.prefix = prefix;
+    p.amask = atten_mask;
+    p.amask_ld = Skv;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     p.q = q; p.k = k; p.v = v; p.out = out;
@@ -152,7 +166,8 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
                            int64_t max_seqlen_q, int64_t max_seqlen_kv,
                            int64_t Nq, int64_t Nkv, int64_t D,
                            int dtype, float scale,
-                           int mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
+                           int mask, int64_t pre_tokens, int64_t next_tokens,
+                           const int64_t* prefix, const uint8_t* atten_mask, void* stream)
 {
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_kv) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -164,10 +179,15 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     if (Nq < 1 || Nkv < 1 || Nq > 256 || Nkv > 256 || D < 1 || D > 768) return MIATTN_ERR_SHAPE;
     if (Nq % Nkv != 0) return MIATTN_ERR_GQA_RATIO;
     FaParams p{};
-    st = check_mask(mask, pre_tokens, next_tokens, p.pre, p.next);
+    st = check_mask(mask, pre_tokens, next_tokens, p);
     if (st != MIATTN_OK) return st;
+    if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
+        return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
     if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    p.prefix = prefix;
+    p.amask = atten_mask;
+    p.amask_ld = max_seqlen_kv;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;
@@ -196,7 +216,8 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
                          miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
 {
     return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
-                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, stream);
+                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
+                     nullptr, stream);
 }
 
 miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
@@ -210,7 +231,7 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
 {
     return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, dtype, scale, mask, pre_tokens, next_tokens, stream);
+                      D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
 }
 
 miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
@@ -222,7 +243,8 @@ miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
 {
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_dense(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum, B, Nq, Nkv,
-                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, stream);
+                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
+                     nullptr, stream);
 }
 
 miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void* v,
@@ -240,7 +262,35 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_varlen(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, dtype, scale, mask, pre_tokens, next_tokens, stream);
+                      D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
+}
+
+miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
+                                float* softmax_max, float* softmax_sum,
+                                int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                const int64_t* prefix, const uint8_t* atten_mask, void* stream)
+{
+    return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
+                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, prefix,
+                     atten_mask, stream);
+}
+
+miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* out,
+                                       float* softmax_max, float* softmax_sum,
+                                       const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                       int64_t B, int64_t Tq, int64_t Tkv,
+                                       int64_t max_seqlen_q, int64_t max_seqlen_kv,
+                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       miattn_dtype_t dtype, float scale,
+                                       miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
+                                       const int64_t* prefix, const uint8_t* atten_mask,
+                                       void* stream)
+{
+    return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
+                      cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
+                      D, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask, stream);
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

@@ -23,7 +23,8 @@ def _declared():
 def test_header_declares_every_entry_point():
     d = _declared()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-                 "attn_lse_merge", "sparse_csr_attn", "miattn_status_str"):
+                 "attn_fwd_masked", "attn_fwd_varlen_masked", "attn_lse_merge", "sparse_csr_attn",
+                 "miattn_status_str"):
         assert name in d, d
 
 
@@ -161,8 +162,38 @@ def test_attn_fwd_varlen_update_validation(mi):
         assert call(**{name: None}) == "MIATTN_ERR_NULL", name
     assert call(B=0) == "MIATTN_ERR_SHAPE"
     assert call(mq=101) == "MIATTN_ERR_SHAPE"
-    assert call(mask=4) == "MIATTN_ERR_MASK"
+    assert call(mask=7) == "MIATTN_ERR_MASK"
     assert call(D=100) == "MIATTN_ERR_UNSUPPORTED"
+
+
+def test_attn_fwd_masked_validation(mi):
+    def call(**kw):
+        a = dict(q=P, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64, dtype="bf16", layout="BNSD",
+                 scale=0.125, mask="causal_br", pre=0, nxt=0, prefix=None, am=None)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_fwd_masked(a["q"], P, P, P, None, None, a["B"], a["Nq"], a["Nkv"], a["Sq"],
+                               a["Skv"], a["D"], a["dtype"], a["layout"], a["scale"], a["mask"],
+                               a["pre"], a["nxt"], a["prefix"], a["am"], stream=0)
+        return mi.STATUS[e.value.status]
+    assert call(q=None, prefix=P) == "MIATTN_ERR_NULL"
+    assert call(mask=5) == "MIATTN_ERR_MASK"
+    assert call(mask="band_br", pre=2, nxt=-3) == "MIATTN_ERR_MASK"      # empty band
+    assert call(mask="band", pre=4, nxt=0, prefix=P) == "MIATTN_ERR_MASK"  # prefix: causal only
+    assert call(mask="none", prefix=P) == "MIATTN_ERR_MASK"
+    assert call(D=80, am=P) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(dtype="f64", am=P) == "MIATTN_ERR_DTYPE"
+
+    def vcall(**kw):
+        a = dict(mask="causal", prefix=P, D=128)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_fwd_varlen_masked(P, P, P, P, None, None, P, P, 3, 100, 100, 50, 50, 8, 2,
+                                      a["D"], "bf16", 0.1, a["mask"], 3, 3, a["prefix"], P,
+                                      stream=0)
+        return mi.STATUS[e.value.status]
+    assert vcall(mask="band") == "MIATTN_ERR_MASK"
+    assert vcall(D=48) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_attn_lse_merge_validation(mi):
