@@ -238,7 +238,7 @@ def main():
 
         def step_prefix():
             mi.attn_fwd_varlen_masked(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen,
-                                      Nq, Nkv, D, "bf16", scale, "causal_br", 0, 0, pdev, None,
+                                      Nq, Nkv, D, D, "bf16", scale, "causal_br", 0, 0, pdev, None,
                                       stream.cuda_stream)
 
         pms = time_launches(step_prefix, args.steps, args.warmup, stream)
@@ -261,7 +261,7 @@ def main():
         xflops = 4.0 * D * 8 * xpairs
 
         def step_amask():
-            mi.attn_fwd_masked(xq, xk, xv, xo, None, None, 1, 8, 8, Sx, Sx, D, "bf16", "BNSD",
+            mi.attn_fwd_masked(xq, xk, xv, xo, None, None, 1, 8, 8, Sx, Sx, D, D, "bf16", "BNSD",
                                scale, "causal", 0, 0, None, xam, stream.cuda_stream)
 
         xms = time_launches(step_amask, 5, 1, stream)

@@ -210,7 +210,7 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
 
 /*
  * attn_fwd_masked / attn_fwd_varlen_masked - attn_fwd / attn_fwd_varlen with the rest of
- * the mask surface of aclnnFlashAttentionVarLenScore (约束说明: sparseMode, prefixOptional,
+ * the mask surface and the value head dim of aclnnFlashAttentionVarLenScore (约束说明: sparseMode, prefixOptional,
  * attenMaskOptional), under these readings (the page's mode definitions were not part of
  * the extracted text):
  *   prefix: DEVICE int64 [B] or NULL.  Keys j < prefix[b] are visible from every row of
@@ -227,11 +227,15 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
  *   size under 2^31 bytes; otherwise (and for fp32) the forward runs in fp32 arithmetic on
  *   the vector ALUs (inputs widened on load, output rounded to the input type).  Other
  *   arguments, limits and errors as attn_fwd / attn_fwd_varlen.
+ *   Dv: head dim of v and out (aclnnFlashAttentionVarLenScore 约束说明: qD == kD >= vD);
+ *     v is [B, Nkv, Skv, Dv] / [Tkv, Nkv, Dv] and out [B, Nq, Sq, Dv] / [Tq, Nq, Dv] in the
+ *     same layout.  Dv = D always; Dv < D for (D, Dv) in {(64, 32), (96, 64), (128, 64),
+ *     (128, 96)} without atten_mask (else MIATTN_ERR_UNSUPPORTED); Dv > D -> MIATTN_ERR_SHAPE.
  */
 miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
                                 float* softmax_max, float* softmax_sum,
                                 int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
-                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout, float scale,
                                 miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                 const int64_t* prefix, const uint8_t* atten_mask, void* stream);
 
@@ -240,7 +244,7 @@ miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void*
                                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                                        int64_t B, int64_t Tq, int64_t Tkv,
                                        int64_t max_seqlen_q, int64_t max_seqlen_kv,
-                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       int64_t Nq, int64_t Nkv, int64_t D, int64_t Dv,
                                        miattn_dtype_t dtype, float scale,
                                        miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                        const int64_t* prefix, const uint8_t* atten_mask,

@@ -45,8 +45,8 @@ _lib.attn_fwd.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P
 _lib.attn_fwd_varlen.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_update.argtypes = [_P] * 9 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_varlen_update.argtypes = [_P] * 11 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
-_lib.attn_fwd_masked.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P, _P, _P]
-_lib.attn_fwd_varlen_masked.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P, _P, _P]
+_lib.attn_fwd_masked.argtypes = [_P] * 6 + [_I64] * 7 + [_E, _E, _F, _E, _I64, _I64, _P, _P, _P]
+_lib.attn_fwd_varlen_masked.argtypes = [_P] * 8 + [_I64] * 9 + [_E, _F, _E, _I64, _I64, _P, _P, _P]
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
 for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
@@ -130,23 +130,23 @@ def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, 
            "attn_fwd_varlen_update")
 
 
-def attn_fwd_masked(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, dtype,
+def attn_fwd_masked(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, Dv, dtype,
                     layout, scale, mask, pre_tokens=0, next_tokens=0, prefix=None,
                     atten_mask=None, stream=None):
     _check(_lib.attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
-                                _ptr(softmax_sum), B, Nq, Nkv, Sq, Skv, D, _enum(dtype, DTYPES),
+                                _ptr(softmax_sum), B, Nq, Nkv, Sq, Skv, D, Dv, _enum(dtype, DTYPES),
                                 _enum(layout, LAYOUTS), scale, _enum(mask, MASKS), pre_tokens,
                                 next_tokens, _ptr(prefix), _ptr(atten_mask), _stream(stream)),
            "attn_fwd_masked")
 
 
 def attn_fwd_varlen_masked(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
-                           B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, dtype, scale,
+                           B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv, dtype, scale,
                            mask, pre_tokens=0, next_tokens=0, prefix=None, atten_mask=None,
                            stream=None):
     _check(_lib.attn_fwd_varlen_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                        _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
-                                       B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
+                                       B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv,
                                        _enum(dtype, DTYPES), scale, _enum(mask, MASKS),
                                        pre_tokens, next_tokens, _ptr(prefix), _ptr(atten_mask),
                                        _stream(stream)), "attn_fwd_varlen_masked")

@@ -1,9 +1,11 @@
 """Build the HIP library libmiattn.so in-tree for gfx950 with hipcc."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -23,10 +25,7 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _hipcc(out: str, srcs, verbose: bool) -> None:
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
-           *DEVICE_FLAGS, "-o", out + ".tmp", *srcs]
+def _run(cmd, what: str, verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or res.returncode != 0:
         msg = "\n".join(l for l in res.stderr.splitlines()
@@ -34,7 +33,23 @@ def _hipcc(out: str, srcs, verbose: bool) -> None:
         if msg.strip():
             print(msg)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+        raise RuntimeError(f"hipcc failed building {what}")
+
+
+def _hipcc(out: str, srcs, verbose: bool) -> None:
+    """Compile each source to an object in parallel, then link the shared library."""
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS]
+    with tempfile.TemporaryDirectory(prefix="miattn_build_") as tmp:
+        objs = [os.path.join(tmp, f"{i}_{os.path.basename(src)}.o") for i, src in enumerate(srcs)]
+        jobs = [([HIPCC, *flags, "-c", "-o", o, src], os.path.basename(src))
+                for src, o in zip(srcs, objs)]
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            for f in [pool.submit(_run, cmd, what, verbose) for cmd, what in jobs]:
+                f.result()
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs],
+             os.path.basename(out), verbose)
     os.replace(out + ".tmp", out)
 
 

@@ -89,19 +89,20 @@ template <> struct Elem<_Float16> {
     }
 };
 
-template <int D>
+// D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
+template <int D, int DV>
 struct Cfg {
     static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
     static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per K row
     static constexpr int KCH = BN * CPR;              // K chunks per tile
     static constexpr int KPT = (KCH + NT - 1) / NT;   // K chunks per thread (some repeat)
-    static constexpr int VUNITS = (BN / 2) * CPR;     // V units (2 keys x 8 dims) per tile
+    static constexpr int VUNITS = (BN / 2) * (DV / 8); // V units (2 keys x 8 dims) per tile
     static constexpr int SREG = KPT + 2;              // staging registers (16 B each)
-    static constexpr int KK = D / 16;                 // MFMA k-steps over the head dim
-    static constexpr int RT = D / 32;                 // 32-row output tiles over the head dim
+    static constexpr int KK = D / 16;                 // MFMA k-steps over the Q/K head dim
+    static constexpr int RT = DV / 32;                // 32-row output tiles over the V head dim
     static constexpr int KBUF = BN * KS;
-    static constexpr int VBUF = D * VS;
+    static constexpr int VBUF = DV * VS;
 };
 
 // max / sum of x over the lane pair (l, l ^ 32); v_permlane32_swap(x, x) leaves
@@ -141,10 +142,10 @@ __device__ inline unsigned pack_mask(const unsigned (&w)[8])
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
 // masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
-template <int D, typename T, bool UPDATE, bool MASKED>
+template <int D, int DV, typename T, bool UPDATE, bool MASKED>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
-    using C = Cfg<D>;
+    using C = Cfg<D, DV>;
     constexpr int PF = MASKED ? 2 : ::miattn::PF;
     constexpr int LDSD = MASKED ? 3 : ::miattn::LDSD;
     using X8 = typename Elem<T>::v8;   // one MFMA operand: 8 elements
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
                 if (p.prev_max[si] == -INFINITY) {
                     p.ssum[si] = 0.f;
                     T* orow = og + (int64_t)(i0 + r) * p.o_ss;
-                    for (int d = 0; d < D; d += 4) *(X4*)(orow + d) = X4{};
+                    for (int d = 0; d < DV; d += 4) *(X4*)(orow + d) = X4{};
                 }
             }
             return;
@@ -531,12 +532,30 @@ hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(NT);
     switch (D) {
-    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, 32, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 64, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, 96, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 128, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// value head dim below the Q/K head dim (plain forward only)
+template <typename T>
+hipError_t launch_dv(const FaParams& p, int D, int Dv, hipStream_t stream)
+{
+    dim3 grid(p.n_slots), block(NT);
+    if (D == 64 && Dv == 32)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 32, T, false, false>), grid, block, 0, stream, p);
+    else if (D == 96 && Dv == 64)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, 64, T, false, false>), grid, block, 0, stream, p);
+    else if (D == 128 && Dv == 64)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 64, T, false, false>), grid, block, 0, stream, p);
+    else if (D == 128 && Dv == 96)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 96, T, false, false>), grid, block, 0, stream, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -545,6 +564,10 @@ hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream)
 {
     const bool upd = p.prev_out != nullptr;
+    if (p.Dv != D) {
+        if (upd || p.amask) return hipErrorInvalidValue;
+        return f16 ? launch_dv<_Float16>(p, D, p.Dv, stream) : launch_dv<__bf16>(p, D, p.Dv, stream);
+    }
     if (p.amask) {   // the masked variant has no fused update
         if (upd) return hipErrorInvalidValue;
         return f16 ? launch_t<_Float16, false, true>(p, D, stream) : launch_t<__bf16, false, true>(p, D, stream);

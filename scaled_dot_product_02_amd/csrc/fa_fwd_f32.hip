@@ -41,11 +41,12 @@ __device__ inline void store4(T* x, float4 v)
 
 // T: input / output type; UPDATE = true: the epilogue merges the partial result into
 // p.prev_* (ring update); MASKED = true: p.amask removes keys as well.
-template <typename T, int D, bool UPDATE, bool MASKED>
+// D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
+template <typename T, int D, int DV, bool UPDATE, bool MASKED>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
 {
     __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-    __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs[BN * DV];
 
     const TileCoord tc = decode_tile(p, blockIdx.x, BM);
     if (!tc.live) return;
@@ -67,26 +68,29 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
     const bool mrow = MASKED && qi < p.Sq;
     const uint8_t* arow = MASKED ? p.amask + (int64_t)(mrow ? qi : 0) * p.amask_ld : nullptr;
 
-    float q[D], o[D];
+    float q[D], o[DV];
     #pragma unroll
     for (int d = 0; d < D; d += 4) {
         float4 x = qi < tc.len_q ? load4(qg + (int64_t)qi * p.q_ss + d) : float4{0, 0, 0, 0};
         q[d] = x.x; q[d + 1] = x.y; q[d + 2] = x.z; q[d + 3] = x.w;
-        o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
     }
+    #pragma unroll
+    for (int d = 0; d < DV; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
     for (int j0 = (kv_lo / BN) * BN; j0 < kv_hi; j0 += BN) {
         __syncthreads();
         for (int c = lane; c < BN * D / 4; c += 64) {
             const int row = c / (D / 4), col = 4 * (c % (D / 4));
-            float4 kx{0, 0, 0, 0}, vx{0, 0, 0, 0};
-            if (j0 + row < tc.len_kv) {
-                kx = load4(kg + (int64_t)(j0 + row) * p.k_ss + col);
-                vx = load4(vg + (int64_t)(j0 + row) * p.v_ss + col);
-            }
+            float4 kx{0, 0, 0, 0};
+            if (j0 + row < tc.len_kv) kx = load4(kg + (int64_t)(j0 + row) * p.k_ss + col);
             *(float4*)(Ks + row * D + col) = kx;
-            *(float4*)(Vs + row * D + col) = vx;
+        }
+        for (int c = lane; c < BN * DV / 4; c += 64) {
+            const int row = c / (DV / 4), col = 4 * (c % (DV / 4));
+            float4 vx{0, 0, 0, 0};
+            if (j0 + row < tc.len_kv) vx = load4(vg + (int64_t)(j0 + row) * p.v_ss + col);
+            *(float4*)(Vs + row * DV + col) = vx;
         }
         __syncthreads();
 
@@ -111,14 +115,14 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             l_run *= alpha;
             #pragma unroll
-            for (int d = 0; d < D; ++d) o[d] *= alpha;
+            for (int d = 0; d < DV; ++d) o[d] *= alpha;
             #pragma unroll
             for (int jj = 0; jj < CH; ++jj) {
                 const float e = __builtin_amdgcn_exp2f(s[jj] - m_use);
                 l_run += e;
-                const float* vr = Vs + (c0 + jj) * D;
+                const float* vr = Vs + (c0 + jj) * DV;
                 #pragma unroll
-                for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(e, vr[d], o[d]);
+                for (int d = 0; d < DV; ++d) o[d] = __builtin_fmaf(e, vr[d], o[d]);
             }
             m_run = m_new;
         }
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
         }
         T* orow = og + (int64_t)qi * p.o_ss;
         #pragma unroll
-        for (int d = 0; d < D; d += 4) {
+        for (int d = 0; d < DV; d += 4) {
             float4 y{o[d] * wc, o[d + 1] * wc, o[d + 2] * wc, o[d + 3] * wc};
             if constexpr (UPDATE) {
                 // an empty prior (weight 0) is not read: its buffer may hold anything
@@ -169,11 +173,25 @@ template <typename T, bool UPDATE, bool MASKED>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(64);
+    if (p.Dv != D) {   // value head dim below the Q/K head dim: plain fp32 forward only
+        if constexpr (UPDATE || MASKED || sizeof(T) != 4) return hipErrorInvalidValue;
+        else if (D == 64 && p.Dv == 32)
+            hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 64, 32, false, false>), grid, block, 0, stream, p);
+        else if (D == 96 && p.Dv == 64)
+            hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 96, 64, false, false>), grid, block, 0, stream, p);
+        else if (D == 128 && p.Dv == 64)
+            hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, 64, false, false>), grid, block, 0, stream, p);
+        else if (D == 128 && p.Dv == 96)
+            hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, 96, false, false>), grid, block, 0, stream, p);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     switch (D) {
-    case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 32, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 64, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 96, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 32, 32, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 64, 64, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 96, 96, UPDATE, MASKED>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, 128, UPDATE, MASKED>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -30,6 +30,7 @@ struct FaParams {
     int64_t st_sb, st_sh;       // stats element index = b*st_sb + h*st_sh + (seq start + i)
     int32_t B, Nq, Nkv, group;  // group = Nq / Nkv
     int32_t Sq, Skv;            // dense: lengths; packed: upper bounds (max_seqlen)
+    int32_t Dv;                 // head dim of V and the output (<= the Q/K head dim)
     int32_t n_levels;           // q tiles per sequence at the longest length
     int32_t n_slots;            // workgroups in the grid (multiple of 8 * group)
     int64_t pre, next;          // visible band: -pre <= j - i - off <= next (clamped)

@@ -53,6 +53,18 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 // head dims with a built attention kernel (every dtype)
 bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
+// (Q/K head dim, V head dim) pairs with a built kernel; a smaller V head dim only for the
+// plain forward (no fused update, no mask tensor)
+miattn_status_t check_head_dims(int64_t D, int64_t Dv, bool update, bool amask)
+{
+    if (Dv < 1 || Dv > D) return MIATTN_ERR_SHAPE;   // the varlen operator: kD >= vD
+    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    if (Dv == D) return MIATTN_OK;
+    const bool pair = (D == 64 && Dv == 32) || (D == 96 && Dv == 64) || (D == 128 && Dv == 64) ||
+                      (D == 128 && Dv == 96);
+    return pair && !update && !amask ? MIATTN_OK : MIATTN_ERR_UNSUPPORTED;
+}
+
 miattn_status_t check_dtype_fa(int dtype)
 {
     if (dtype == MIATTN_F32 || dtype == MIATTN_BF16 || dtype == MIATTN_F16) return MIATTN_OK;
@@ -117,7 +129,7 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
                           const void* prev_out, const float* prev_max, const float* prev_sum,
                           void* out, float* softmax_max, float* softmax_sum,
                           int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
-                          int dtype, int layout, float scale,
+                          int64_t Dv, int dtype, int layout, float scale,
                           int mask, int64_t pre_tokens, int64_t next_tokens,
                           const int64_t* prefix, const uint8_t* atten_mask, void* stream)
 {
@@ -135,20 +147,23 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
         return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
+    if (st != MIATTN_OK) return st;
+    p.Dv = (int32_t)Dv;
     p.prefix = prefix;
     p.amask = atten_mask;
     p.amask_ld = Skv;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
+    const Strides so = strides_of(layout, B, Nq, Sq, Dv), sv = strides_of(layout, B, Nkv, Skv, Dv);
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;
     p.prev_out = prev_out; p.prev_max = prev_max; p.prev_sum = prev_sum;
     p.cu_q = p.cu_kv = nullptr;
     p.q_sb = sq.sb; p.q_ss = sq.ss; p.q_sh = sq.sh;
-    p.o_sb = sq.sb; p.o_ss = sq.ss; p.o_sh = sq.sh;
+    p.o_sb = so.sb; p.o_ss = so.ss; p.o_sh = so.sh;
     p.k_sb = skv.sb; p.k_ss = skv.ss; p.k_sh = skv.sh;
-    p.v_sb = skv.sb; p.v_ss = skv.ss; p.v_sh = skv.sh;
+    p.v_sb = sv.sb; p.v_ss = sv.ss; p.v_sh = sv.sh;
     p.st_sb = Nq * Sq; p.st_sh = Sq;
     p.B = (int32_t)B; p.Nq = (int32_t)Nq; p.Nkv = (int32_t)Nkv; p.group = (int32_t)(Nq / Nkv);
     p.Sq = (int32_t)Sq; p.Skv = (int32_t)Skv;
@@ -164,7 +179,7 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
                            const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                            int64_t B, int64_t Tq, int64_t Tkv,
                            int64_t max_seqlen_q, int64_t max_seqlen_kv,
-                           int64_t Nq, int64_t Nkv, int64_t D,
+                           int64_t Nq, int64_t Nkv, int64_t D, int64_t Dv,
                            int dtype, float scale,
                            int mask, int64_t pre_tokens, int64_t next_tokens,
                            const int64_t* prefix, const uint8_t* atten_mask, void* stream)
@@ -184,7 +199,9 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
         return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
+    if (st != MIATTN_OK) return st;
+    p.Dv = (int32_t)Dv;
     p.prefix = prefix;
     p.amask = atten_mask;
     p.amask_ld = max_seqlen_kv;
@@ -194,9 +211,9 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     p.prev_out = prev_out; p.prev_max = prev_max; p.prev_sum = prev_sum;
     p.cu_q = cu_seqlens_q; p.cu_kv = cu_seqlens_kv;
     p.q_sb = 0; p.q_ss = Nq * D; p.q_sh = D;
-    p.o_sb = 0; p.o_ss = Nq * D; p.o_sh = D;
+    p.o_sb = 0; p.o_ss = Nq * Dv; p.o_sh = Dv;
     p.k_sb = 0; p.k_ss = Nkv * D; p.k_sh = D;
-    p.v_sb = 0; p.v_ss = Nkv * D; p.v_sh = D;
+    p.v_sb = 0; p.v_ss = Nkv * Dv; p.v_sh = Dv;
     p.st_sb = 0; p.st_sh = Tq;
     p.B = (int32_t)B; p.Nq = (int32_t)Nq; p.Nkv = (int32_t)Nkv; p.group = (int32_t)(Nq / Nkv);
     p.Sq = (int32_t)max_seqlen_q; p.Skv = (int32_t)max_seqlen_kv;
@@ -216,7 +233,7 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
                          miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens, void* stream)
 {
     return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
-                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
+                     Sq, Skv, D, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
                      nullptr, stream);
 }
 
@@ -231,7 +248,7 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
 {
     return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
+                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
 }
 
 miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
@@ -243,7 +260,7 @@ miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
 {
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_dense(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum, B, Nq, Nkv,
-                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
+                     Sq, Skv, D, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
                      nullptr, stream);
 }
 
@@ -262,18 +279,18 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_varlen(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
+                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
 }
 
 miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
                                 float* softmax_max, float* softmax_sum,
                                 int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
-                                miattn_dtype_t dtype, miattn_layout_t layout, float scale,
+                                int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout, float scale,
                                 miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                 const int64_t* prefix, const uint8_t* atten_mask, void* stream)
 {
     return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
-                     Sq, Skv, D, dtype, layout, scale, mask, pre_tokens, next_tokens, prefix,
+                     Sq, Skv, D, Dv, dtype, layout, scale, mask, pre_tokens, next_tokens, prefix,
                      atten_mask, stream);
 }
 
@@ -282,7 +299,7 @@ miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void*
                                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                                        int64_t B, int64_t Tq, int64_t Tkv,
                                        int64_t max_seqlen_q, int64_t max_seqlen_kv,
-                                       int64_t Nq, int64_t Nkv, int64_t D,
+                                       int64_t Nq, int64_t Nkv, int64_t D, int64_t Dv,
                                        miattn_dtype_t dtype, float scale,
                                        miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                        const int64_t* prefix, const uint8_t* atten_mask,
@@ -290,7 +307,7 @@ miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void*
 {
     return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask, stream);
+                      D, Dv, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask, stream);
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

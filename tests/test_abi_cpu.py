@@ -168,13 +168,13 @@ def test_attn_fwd_varlen_update_validation(mi):
 
 def test_attn_fwd_masked_validation(mi):
     def call(**kw):
-        a = dict(q=P, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64, dtype="bf16", layout="BNSD",
+        a = dict(q=P, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64, Dv=64, dtype="bf16", layout="BNSD",
                  scale=0.125, mask="causal_br", pre=0, nxt=0, prefix=None, am=None)
         a.update(kw)
         with pytest.raises(mi.MiattnError) as e:
             mi.attn_fwd_masked(a["q"], P, P, P, None, None, a["B"], a["Nq"], a["Nkv"], a["Sq"],
-                               a["Skv"], a["D"], a["dtype"], a["layout"], a["scale"], a["mask"],
-                               a["pre"], a["nxt"], a["prefix"], a["am"], stream=0)
+                               a["Skv"], a["D"], a["Dv"], a["dtype"], a["layout"], a["scale"],
+                               a["mask"], a["pre"], a["nxt"], a["prefix"], a["am"], stream=0)
         return mi.STATUS[e.value.status]
     assert call(q=None, prefix=P) == "MIATTN_ERR_NULL"
     assert call(mask=5) == "MIATTN_ERR_MASK"
@@ -183,17 +183,21 @@ def test_attn_fwd_masked_validation(mi):
     assert call(mask="none", prefix=P) == "MIATTN_ERR_MASK"
     assert call(D=80, am=P) == "MIATTN_ERR_UNSUPPORTED"
     assert call(dtype="f64", am=P) == "MIATTN_ERR_DTYPE"
+    assert call(D=64, Dv=96) == "MIATTN_ERR_SHAPE"               # kD >= vD
+    assert call(D=64, Dv=48) == "MIATTN_ERR_UNSUPPORTED"         # pair not built
+    assert call(D=128, Dv=64, am=P) == "MIATTN_ERR_UNSUPPORTED"  # Dv < D without a mask tensor
 
     def vcall(**kw):
-        a = dict(mask="causal", prefix=P, D=128)
+        a = dict(mask="causal", prefix=P, D=128, Dv=128)
         a.update(kw)
         with pytest.raises(mi.MiattnError) as e:
             mi.attn_fwd_varlen_masked(P, P, P, P, None, None, P, P, 3, 100, 100, 50, 50, 8, 2,
-                                      a["D"], "bf16", 0.1, a["mask"], 3, 3, a["prefix"], P,
-                                      stream=0)
+                                      a["D"], a["Dv"], "bf16", 0.1, a["mask"], 3, 3, a["prefix"],
+                                      P, stream=0)
         return mi.STATUS[e.value.status]
     assert vcall(mask="band") == "MIATTN_ERR_MASK"
-    assert vcall(D=48) == "MIATTN_ERR_UNSUPPORTED"
+    assert vcall(D=48, Dv=48) == "MIATTN_ERR_UNSUPPORTED"
+    assert vcall(Dv=0) == "MIATTN_ERR_SHAPE"
 
 
 def test_attn_lse_merge_validation(mi):

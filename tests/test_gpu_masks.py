@@ -30,14 +30,15 @@ def _bnsd(w, x, n):
 
 def _dense_gpu(mi, w, scale, mask, pre=0, nxt=0, prefix=None, amask=None):
     B, Nq, Nkv, Sq, Skv, D = (w[x] for x in ("B", "Nq", "Nkv", "Sq", "Skv", "D"))
+    Dv = w.get("Dv", D)
     dt = w["dtype"]
     q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
-    out = empty_like_storage(q.shape, dt)
+    out = empty_like_storage(synthetic.storage_shape(w["layout"], B, Nq, Sq, Dv), dt)
     m, l = nan_stats((B, Nq, Sq)), nan_stats((B, Nq, Sq))
     pf = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
     am = None if amask is None else torch.from_numpy(np.ascontiguousarray(amask, np.uint8)).to("cuda:0")
-    mi.attn_fwd_masked(q, k, v, out, m, l, B, Nq, Nkv, Sq, Skv, D, dt, w["layout"], scale, mask,
-                       pre, nxt, pf, am)
+    mi.attn_fwd_masked(q, k, v, out, m, l, B, Nq, Nkv, Sq, Skv, D, Dv, dt, w["layout"], scale,
+                       mask, pre, nxt, pf, am)
     torch.cuda.synchronize()
     return synthetic.to_bnsd(host_values(out), w["layout"], Nq), host_values(m), host_values(l)
 
@@ -100,13 +101,14 @@ def _varlen_gpu(mi, w, scale, mask, pre=0, nxt=0, prefix=None, amask=None):
     q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
     cq = torch.from_numpy(w["cu_q"]).to("cuda:0")
     ck = torch.from_numpy(w["cu_kv"]).to("cuda:0")
-    out = empty_like_storage(q.shape, dt)
+    Dv = w.get("Dv", w["D"])
+    out = empty_like_storage((w["Tq"], w["Nq"], Dv), dt)
     m, l = nan_stats((w["Nq"], w["Tq"])), nan_stats((w["Nq"], w["Tq"]))
     pf = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
     am = None if amask is None else torch.from_numpy(np.ascontiguousarray(amask, np.uint8)).to("cuda:0")
     mi.attn_fwd_varlen_masked(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"],
                               int(w["lengths_q"].max()), int(w["lengths_kv"].max()), w["Nq"],
-                              w["Nkv"], w["D"], dt, scale, mask, pre, nxt, pf, am)
+                              w["Nkv"], w["D"], Dv, dt, scale, mask, pre, nxt, pf, am)
     torch.cuda.synchronize()
     return host_values(out), host_values(m), host_values(l)
 
@@ -154,6 +156,36 @@ def test_varlen_explicit_mask(mi, dtype, lk):
     _check_varlen(mi, w, 1 / math.sqrt(128), "causal",
                   lambda b, sq, sk: oracle.keep_band(sq, sk, BIG, 0) & ~amask[:sq, :sk],
                   amask=amask)
+
+
+def _with_dv(w, Dv, seed):
+    """The inputs with V redrawn at head dim Dv (same recipe: standard normal float32, then
+    the storage type)."""
+    rng = np.random.default_rng(seed)
+    if "layout" in w:
+        shape = synthetic.storage_shape(w["layout"], w["B"], w["Nkv"], w["Skv"], Dv)
+    else:
+        shape = (w["Tkv"], w["Nkv"], Dv)
+    v = synthetic.to_storage(rng.standard_normal(shape, dtype=np.float32), w["dtype"])
+    return dict(w, v=v, Dv=Dv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D,Dv", [(64, 32), (96, 64), (128, 64), (128, 96)])
+@pytest.mark.parametrize("layout", ["BNSD", "SBH"])
+def test_dense_value_head_dim_below_qk(mi, dtype, D, Dv, layout):
+    """qD == kD >= vD: the value / output head dim below the query / key one."""
+    w = _with_dv(synthetic.dense_inputs(91, 2, 4, 2, 300, 333, D, dtype, layout), Dv, 92)
+    keep = oracle.keep_band(300, 333, BIG, 0)
+    _check_dense(mi, w, 1 / math.sqrt(D), "causal", keep)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_value_head_dim_below_qk(mi, dtype):
+    w = _with_dv(synthetic.varlen_inputs(93, Nq=8, Nkv=2, D=128, dtype=dtype, lengths_q=LQ,
+                                         lengths_kv=LK), 64, 94)
+    _check_varlen(mi, w, 1 / math.sqrt(128), "causal_br",
+                  lambda b, sq, sk: oracle.keep_band(sq, sk, BIG, 0, "bottom_right"))
 
 
 def test_update_bottom_right(mi):
