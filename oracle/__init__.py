@@ -182,6 +182,93 @@ def attn_varlen_keep(q, k, v, cu_q, cu_kv, keep_of, scale: float, threads: int =
     return out, m, l
 
 
+# ------------------------------------------------------------------------------------
+# dropout on the attention probabilities (the dropout_p of the MultiHeadAttention page and
+# the SDPA-pitfalls blog).  The pages specify no generator; both sides implement the
+# counter-based Philox4x32-10 from its published definition (Salmon, Moraes, Dror, Shaw,
+# "Parallel random numbers: as easy as 1, 2, 3", SC 2011): 10 rounds of two 32x32->64
+# multiplications by 0xD2511F53 and 0xCD9E8D57 with the Weyl key schedule 0x9E3779B9,
+# 0xBB67AE85.
+# ------------------------------------------------------------------------------------
+
+def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
+    """Philox4x32-10 of the counters (uint32 arrays, broadcast) under key (k0, k1):
+    four uint32 arrays."""
+    c = [np.asarray(x, dtype=np.uint32) for x in (c0, c1, c2, c3)]
+    c = [np.broadcast_to(x, np.broadcast(*c).shape).copy() for x in c]
+    key = [int(k0) & 0xFFFFFFFF, int(k1) & 0xFFFFFFFF]
+    for r in range(10):
+        p0 = np.uint64(0xD2511F53) * c[0].astype(np.uint64)
+        p1 = np.uint64(0xCD9E8D57) * c[2].astype(np.uint64)
+        hi0, lo0 = (p0 >> np.uint64(32)).astype(np.uint32), p0.astype(np.uint32)
+        hi1, lo1 = (p1 >> np.uint64(32)).astype(np.uint32), p1.astype(np.uint32)
+        c = [hi1 ^ c[1] ^ np.uint32(key[0]), lo1, hi0 ^ c[3] ^ np.uint32(key[1]), lo0]
+        key = [(key[0] + 0x9E3779B9) & 0xFFFFFFFF, (key[1] + 0xBB67AE85) & 0xFFFFFFFF]
+    return c
+
+
+def dropout_threshold(p: float) -> int:
+    """Byte threshold of dropout probability p (0 <= p < 1): a probability is dropped when
+    its random byte is below round(256 p); kept ones are scaled by 256 / (256 - thr)."""
+    return int(round(float(p) * 256.0))
+
+
+def dropout_keep(seed: int, offset: int, b: int, h: int, Sq: int, Skv: int, p: float):
+    """Keep matrix [Sq, Skv] of (sequence / batch entry b, query head h): the random byte of
+    (i, j) is byte j % 4 of word (j % 16) // 4 of Philox4x32-10 with counter
+    (j // 16, i, h + 256 b, offset) and key (seed low 32 bits, seed high 32 bits)."""
+    i = np.arange(Sq, dtype=np.uint32)[:, None]
+    j = np.arange(Skv, dtype=np.uint32)[None, :]
+    w = philox4x32_10(j // 16, i, np.uint32(h + 256 * b), np.uint32(offset), seed, seed >> 32)
+    word = np.choose((j % 16) // 4, w) if Skv and Sq else np.zeros((Sq, Skv), np.uint32)
+    byte = (word >> (8 * (j % 4))) & np.uint32(0xFF)
+    return byte >= np.uint32(dropout_threshold(p))
+
+
+def attn_dropout(q, k, v, scale: float, mask: str, pre: int, next: int, p: float, seed: int,
+                 offset: int, batch_index=None, threads: int = 0):
+    """Dense attention with dropout on the probabilities: out = (P * keep * 256 / (256 -
+    thr)) V, with P the oracle's softmax probabilities; the statistics are those of P.
+    batch_index[b] gives the b used in the counter (default b)."""
+    out, m, l, probs = attn(q, k, v, scale, mask, pre, next, threads, return_probs=True)
+    B, Nq, Sq, _ = out.shape
+    Skv = probs.shape[-1]
+    G = Nq // k.shape[1]
+    thr = dropout_threshold(p)
+    vv = _f64(v)
+    res = np.empty_like(out)
+    for b in range(B):
+        bi = b if batch_index is None else int(batch_index[b])
+        for h in range(Nq):
+            keep = dropout_keep(seed, offset, bi, h, Sq, Skv, p)
+            pd = probs[b, h] * keep * (256.0 / (256 - thr))
+            res[b, h] = pd @ vv[b, h // G]
+    return res, m, l
+
+
+def attn_varlen_dropout(q, k, v, cu_q, cu_kv, scale: float, mask: str, pre: int, next: int,
+                        p: float, seed: int, offset: int, threads: int = 0):
+    """Packed attention with dropout: each sequence b is attn_dropout on its own rows, with
+    sequence index b in the counter.  Shapes as attn_varlen."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Tq, Nq, D = q.shape
+    out = np.zeros_like(q)
+    m = np.full((Nq, Tq), -np.inf)
+    l = np.zeros((Nq, Tq))
+    q0 = kv0 = 0
+    for b, (qe, ke) in enumerate(zip(np.asarray(cu_q), np.asarray(cu_kv))):
+        qe, ke = int(qe), int(ke)
+        if qe > q0 and ke > kv0:
+            o, mm, ll = attn_dropout(q[q0:qe].transpose(1, 0, 2)[None], k[kv0:ke].transpose(1, 0, 2)[None],
+                                     v[kv0:ke].transpose(1, 0, 2)[None], scale, mask, pre, next, p,
+                                     seed, offset, batch_index=[b], threads=threads)
+            out[q0:qe] = o[0].transpose(1, 0, 2)
+            m[:, q0:qe] = mm[0]
+            l[:, q0:qe] = ll[0]
+        q0, kv0 = qe, ke
+    return out, m, l
+
+
 def merge(o1, m1, l1, o2, m2, l2, threads: int = 0):
     """Merge two partials.  o* (B,N,S,D), m*/l* (B,N,S) -> out, softmax_max, softmax_sum."""
     o1, o2 = _f64(o1), _f64(o2)

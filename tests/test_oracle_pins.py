@@ -355,6 +355,55 @@ def test_attn_varlen_keep_equals_positional_masks():
 
 
 # ------------------------------------------------------------------------------------
+# dropout: Philox4x32-10 and the keep decision
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ctr,key,want", [
+    # known-answer vectors of Philox4x32-10 published with the generator's reference
+    # implementation (Random123)
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+])
+def test_philox4x32_10_known_answers(ctr, key, want):
+    got = oracle.philox4x32_10(*ctr, *key)
+    assert tuple(int(x) for x in got) == want
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_dropout_keep_rate(p):
+    keep = oracle.dropout_keep(2024, 3, 1, 5, 512, 2048, p)
+    want = 1 - oracle.dropout_threshold(p) / 256
+    assert abs(keep.mean() - want) < 0.004            # ~4 sigma for 2^20 draws
+    # rows, columns and heads draw different bytes
+    assert not np.array_equal(keep[0], keep[1]) and not np.array_equal(keep[:, 0], keep[:, 16])
+    assert not np.array_equal(keep, oracle.dropout_keep(2024, 3, 1, 6, 512, 2048, p))
+
+
+def test_dropout_zero_is_plain_attention_and_stats_are_undropped():
+    rng = np.random.default_rng(17)
+    q, k, v = _rand(rng, 2, 4, 20, 8), _rand(rng, 2, 2, 33, 8), _rand(rng, 2, 2, 33, 8)
+    plain = oracle.attn(q, k, v, 0.3, "causal")
+    got = oracle.attn_dropout(q, k, v, 0.3, "causal", 0, 0, 0.0, 99, 0)
+    assert np.max(np.abs(got[0] - plain[0])) < TOL
+    drop = oracle.attn_dropout(q, k, v, 0.3, "causal", 0, 0, 0.4, 99, 0)
+    assert np.array_equal(drop[1], plain[1]) and np.array_equal(drop[2], plain[2])
+    assert np.max(np.abs(drop[0] - plain[0])) > 0.01
+
+
+def test_dropout_is_unbiased_over_offsets():
+    """E[dropout(P) V] = P V: the mean over 400 offsets approaches the plain output."""
+    rng = np.random.default_rng(18)
+    q, k, v = _rand(rng, 1, 1, 6, 4), _rand(rng, 1, 1, 32, 4), _rand(rng, 1, 1, 32, 4)
+    plain = oracle.attn(q, k, v, 0.2)[0]
+    acc = np.zeros_like(plain)
+    for off in range(400):
+        acc += oracle.attn_dropout(q, k, v, 0.2, "none", 0, 0, 0.25, 7, off)[0]
+    assert np.max(np.abs(acc / 400 - plain)) < 0.04
+
+
+# ------------------------------------------------------------------------------------
 # merge of partial results (ring-attention update)
 # ------------------------------------------------------------------------------------
 
