@@ -9,8 +9,9 @@ The metric counts 4 * D * Nq * (visible (query, key) pairs) flops per step.
 Also measured in the same run (reported under "secondary"):
   * the same forward with fp16 storage (same lengths and draws; 2.5 PFLOP/s fp16 peak);
   * the same forward with bottom-right causal plus a prefix of L/3 keys per sequence;
-  * an explicit mask tensor (vector-ALU path) on dense bf16 [1, 8, 4096, 128], causal with
-    25% of keys masked out at random;
+  * the same forward with dropout 0.1 on the probabilities;
+  * an explicit mask tensor on dense bf16 [1, 8, 4096, 128], causal with 25% of keys masked
+    out at random;
   * attn_lse_merge on the ring-merge workload (S 8192, N 32, D 128, SBH bf16), timed over
     rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
   * causal attention over that workload's 4 key chunks of 2048 (a ring on one GPU): the
@@ -237,9 +238,9 @@ def main():
         pflops = 4.0 * D * Nq * ppairs
 
         def step_prefix():
-            mi.attn_fwd_varlen_masked(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen,
+            mi.attn_fwd_varlen_ext(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen,
                                       Nq, Nkv, D, D, "bf16", scale, "causal_br", 0, 0, pdev, None,
-                                      stream.cuda_stream)
+                                      stream=stream.cuda_stream)
 
         pms = time_launches(step_prefix, args.steps, args.warmup, stream)
         ptf = pflops / (pms * 1e-3) / 1e12
@@ -249,8 +250,21 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ptf / PEAK_BF16_TFLOPS, 4)}}
 
-        # explicit mask tensor (vector-ALU path): dense bf16 [1, 8, 4096, 128], causal plus a
-        # random 25% of keys masked out
+        # the same workload with dropout 0.1 on the probabilities (Philox4x32-10 bytes)
+        def step_dropout():
+            mi.attn_fwd_varlen_ext(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen,
+                                   Nq, Nkv, D, D, "bf16", scale, "causal", 0, 0, None, None,
+                                   0.1, 2026, 0, stream=stream.cuda_stream)
+
+        dms_ = time_launches(step_dropout, args.steps, args.warmup, stream)
+        dtf_ = flops / (dms_ * 1e-3) / 1e12
+        sec["attn_fwd_varlen_dropout"] = {
+            "workload": name + "_dropout_0.1", "ms_per_launch": round(dms_, 4),
+            "roofline": {"bound": "mfma", "achieved": round(dtf_, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(dtf_ / PEAK_BF16_TFLOPS, 4)}}
+
+        # explicit mask tensor: dense bf16 [1, 8, 4096, 128], causal plus a random 25% of
+        # keys masked out (rows of whole 4-byte words: the MFMA path)
         Sx = 4096
         wx = synthetic.dense_inputs(0, 1, 8, 8, Sx, Sx, D, "bf16", "BNSD")
         xq, xk, xv = up(wx["q"], "bf16"), up(wx["k"], "bf16"), up(wx["v"], "bf16")
@@ -261,16 +275,16 @@ def main():
         xflops = 4.0 * D * 8 * xpairs
 
         def step_amask():
-            mi.attn_fwd_masked(xq, xk, xv, xo, None, None, 1, 8, 8, Sx, Sx, D, D, "bf16", "BNSD",
-                               scale, "causal", 0, 0, None, xam, stream.cuda_stream)
+            mi.attn_fwd_ext(xq, xk, xv, xo, None, None, 1, 8, 8, Sx, Sx, D, D, "bf16", "BNSD",
+                               scale, "causal", 0, 0, None, xam, stream=stream.cuda_stream)
 
         xms = time_launches(step_amask, 5, 1, stream)
         xtf = xflops / (xms * 1e-3) / 1e12
         sec["attn_fwd_explicit_mask"] = {
             "workload": "dense_bf16_b1n8s4096d128_causal_random_mask_25pct",
             "ms_per_launch": round(xms, 3), "flop_per_launch": xflops,
-            "roofline": {"bound": "alu", "achieved": round(xtf, 3), "peak": PEAK_F32_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(xtf / PEAK_F32_TFLOPS, 4)}}
+            "roofline": {"bound": "mfma", "achieved": round(xtf, 3), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(xtf / PEAK_BF16_TFLOPS, 4)}}
         del xq, xk, xv, xo, xam
         S, N, Dm = 8192, 32, 128
         rng = np.random.default_rng(0)

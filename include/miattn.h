@@ -39,7 +39,7 @@
  *                              needs Sq <= Skv so that no row is empty);
  *      MIATTN_MASK_BAND_BR   : -pre_tokens <= j - i - (Skv - Sq) <= next_tokens.
  *    Sq / Skv are the lengths of each sequence.  Tiles that no visible pair touches are
- *    never loaded.  attn_fwd_masked / attn_fwd_varlen_masked add a prefix and an explicit
+ *    never loaded.  attn_fwd_ext / attn_fwd_varlen_ext add a prefix and an explicit
  *    mask tensor.
  *  - Softmax statistics (fp32, optional, each may be NULL):
  *      softmax_max[row] = max over visible keys of scale * q.k   (natural-log units);
@@ -65,7 +65,8 @@ typedef enum {
     MIATTN_ERR_MASK = 6,        /* unknown mask, or an empty band (pre + next < 0) */
     MIATTN_ERR_UNSUPPORTED = 7, /* valid per the operator spec but not built (e.g. head_dim) */
     MIATTN_ERR_LAUNCH = 8,      /* the HIP launch failed */
-    MIATTN_ERR_SCALE = 9        /* scale is not a finite positive number */
+    MIATTN_ERR_SCALE = 9,       /* scale is not a finite positive number */
+    MIATTN_ERR_DROPOUT = 10     /* dropout_p is not in [0, 1) (or rounds to 256/256) */
 } miattn_status_t;
 
 /* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
@@ -209,8 +210,8 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
                                        void* stream);
 
 /*
- * attn_fwd_masked / attn_fwd_varlen_masked - attn_fwd / attn_fwd_varlen with the rest of
- * the mask surface and the value head dim of aclnnFlashAttentionVarLenScore (约束说明: sparseMode, prefixOptional,
+ * attn_fwd_ext / attn_fwd_varlen_ext - attn_fwd / attn_fwd_varlen with the rest of
+ * the mask surface and the value head dim of aclnnFlashAttentionVarLenScore, and dropout (约束说明: sparseMode, prefixOptional,
  * attenMaskOptional), under these readings (the page's mode definitions were not part of
  * the extracted text):
  *   prefix: DEVICE int64 [B] or NULL.  Keys j < prefix[b] are visible from every row of
@@ -231,15 +232,26 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
  *     v is [B, Nkv, Skv, Dv] / [Tkv, Nkv, Dv] and out [B, Nq, Sq, Dv] / [Tq, Nq, Dv] in the
  *     same layout.  Dv = D always; Dv < D for (D, Dv) in {(64, 32), (96, 64), (128, 64),
  *     (128, 96)} without atten_mask (else MIATTN_ERR_UNSUPPORTED); Dv > D -> MIATTN_ERR_SHAPE.
+ *   dropout_p, seed, offset: dropout on the probabilities (the dropout_p of the
+ *     MultiHeadAttention page and the SDPA-pitfalls blog); the pages name no generator, so
+ *     it is defined here: probability (i, j) of query head h in batch entry / sequence b is
+ *     dropped when byte j % 4 of word (j % 16) / 4 of Philox4x32-10 (Salmon et al., SC 2011)
+ *     with counter (j / 16, i, h + 256 b, offset) and key (seed & 0xffffffff, seed >> 32)
+ *     is below thr = round(256 dropout_p); kept probabilities are scaled by 256 / (256 - thr)
+ *     (so E[out] = attention without dropout).  i, j are sequence-local.  softmax_max /
+ *     softmax_sum stay those of the undropped softmax.  dropout_p = 0 (thr 0) is no dropout;
+ *     not finite, < 0, or thr = 256 -> MIATTN_ERR_DROPOUT; dropout with atten_mask or Dv < D
+ *     -> MIATTN_ERR_UNSUPPORTED.
  */
-miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
+miattn_status_t attn_fwd_ext(const void* q, const void* k, const void* v, void* out,
                                 float* softmax_max, float* softmax_sum,
                                 int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
                                 int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout, float scale,
                                 miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
-                                const int64_t* prefix, const uint8_t* atten_mask, void* stream);
+                                const int64_t* prefix, const uint8_t* atten_mask,
+                                float dropout_p, uint64_t seed, uint32_t offset, void* stream);
 
-miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* out,
+miattn_status_t attn_fwd_varlen_ext(const void* q, const void* k, const void* v, void* out,
                                        float* softmax_max, float* softmax_sum,
                                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                                        int64_t B, int64_t Tq, int64_t Tkv,
@@ -248,6 +260,7 @@ miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void*
                                        miattn_dtype_t dtype, float scale,
                                        miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                        const int64_t* prefix, const uint8_t* atten_mask,
+                                       float dropout_p, uint64_t seed, uint32_t offset,
                                        void* stream);
 
 /*

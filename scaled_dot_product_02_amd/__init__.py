@@ -24,13 +24,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATTN_ERR_DTYPE",
           4: "MIATTN_ERR_LAYOUT", 5: "MIATTN_ERR_GQA_RATIO", 6: "MIATTN_ERR_MASK",
-          7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE"}
+          7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE",
+          10: "MIATTN_ERR_DROPOUT"}
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-           "attn_fwd_masked", "attn_fwd_varlen_masked", "attn_lse_merge", "sparse_csr_attn",
+           "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
            "miattn_status_str")
 
 
@@ -45,12 +46,15 @@ _lib.attn_fwd.argtypes = [_P] * 6 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P
 _lib.attn_fwd_varlen.argtypes = [_P] * 8 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_update.argtypes = [_P] * 9 + [_I64] * 6 + [_E, _E, _F, _E, _I64, _I64, _P]
 _lib.attn_fwd_varlen_update.argtypes = [_P] * 11 + [_I64] * 8 + [_E, _F, _E, _I64, _I64, _P]
-_lib.attn_fwd_masked.argtypes = [_P] * 6 + [_I64] * 7 + [_E, _E, _F, _E, _I64, _I64, _P, _P, _P]
-_lib.attn_fwd_varlen_masked.argtypes = [_P] * 8 + [_I64] * 9 + [_E, _F, _E, _I64, _I64, _P, _P, _P]
+_U64, _U32 = ctypes.c_uint64, ctypes.c_uint32
+_lib.attn_fwd_ext.argtypes = ([_P] * 6 + [_I64] * 7 + [_E, _E, _F, _E, _I64, _I64, _P, _P]
+                              + [_F, _U64, _U32, _P])
+_lib.attn_fwd_varlen_ext.argtypes = ([_P] * 8 + [_I64] * 9 + [_E, _F, _E, _I64, _I64, _P, _P]
+                                     + [_F, _U64, _U32, _P])
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
 for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
-           _lib.attn_fwd_masked, _lib.attn_fwd_varlen_masked, _lib.attn_lse_merge,
+           _lib.attn_fwd_ext, _lib.attn_fwd_varlen_ext, _lib.attn_lse_merge,
            _lib.sparse_csr_attn):
     _f.restype = ctypes.c_int
 _lib.miattn_status_str.argtypes = [ctypes.c_int]
@@ -130,26 +134,27 @@ def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, 
            "attn_fwd_varlen_update")
 
 
-def attn_fwd_masked(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, Dv, dtype,
+def attn_fwd_ext(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, Dv, dtype,
                     layout, scale, mask, pre_tokens=0, next_tokens=0, prefix=None,
-                    atten_mask=None, stream=None):
-    _check(_lib.attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                    atten_mask=None, dropout_p=0.0, seed=0, offset=0, stream=None):
+    _check(_lib.attn_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                 _ptr(softmax_sum), B, Nq, Nkv, Sq, Skv, D, Dv, _enum(dtype, DTYPES),
                                 _enum(layout, LAYOUTS), scale, _enum(mask, MASKS), pre_tokens,
-                                next_tokens, _ptr(prefix), _ptr(atten_mask), _stream(stream)),
-           "attn_fwd_masked")
+                                next_tokens, _ptr(prefix), _ptr(atten_mask), dropout_p, seed,
+                                offset, _stream(stream)), "attn_fwd_ext")
 
 
-def attn_fwd_varlen_masked(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
+def attn_fwd_varlen_ext(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
                            B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv, dtype, scale,
                            mask, pre_tokens=0, next_tokens=0, prefix=None, atten_mask=None,
-                           stream=None):
-    _check(_lib.attn_fwd_varlen_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
+                           dropout_p=0.0, seed=0, offset=0, stream=None):
+    _check(_lib.attn_fwd_varlen_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                        _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
                                        B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv,
                                        _enum(dtype, DTYPES), scale, _enum(mask, MASKS),
                                        pre_tokens, next_tokens, _ptr(prefix), _ptr(atten_mask),
-                                       _stream(stream)), "attn_fwd_varlen_masked")
+                                       dropout_p, seed, offset, _stream(stream)),
+           "attn_fwd_varlen_ext")
 
 
 def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, out_max,

@@ -72,6 +72,27 @@ __device__ inline Band band_of(const FaParams& p, const TileCoord& tc)
     return bd;
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): ten rounds of two 32x32->64-bit
+// products by 0xD2511F53 and 0xCD9E8D57, the key bumped by 0x9E3779B9 / 0xBB67AE85 between
+// rounds.  Dropout draws the byte of probability (i, j) of head h in sequence / batch entry
+// b from counter (j / 16, i, h + 256 b, offset): byte j % 4 of output word (j % 16) / 4.
+__device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+    #pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = (uint32_t)p1;
+        c[2] = n2;
+        c[3] = (uint32_t)p0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
 // Visible key range [lo, hi) of query rows [r0, r1).
 __device__ inline void key_range(const Band& bd, int r0, int r1, int len_kv, int& lo, int& hi)
 {

@@ -142,7 +142,8 @@ __device__ inline unsigned pack_mask(const unsigned (&w)[8])
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
 // masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
-template <int D, int DV, typename T, bool UPDATE, bool MASKED>
+// DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
+template <int D, int DV, typename T, bool UPDATE, bool MASKED, bool DROP = false>
 __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D, DV>;
@@ -425,10 +426,27 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
             }
         l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
         // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8(j%2) + e of block j/2
-        #pragma unroll
-        for (int j = 0; j < 2 * NKB; ++j)
+        if constexpr (DROP) {
+            // MFMA j covers the 16 keys of Philox block 4t + j; slot e takes byte e%4 of
+            // word 2(e/4) + hf
             #pragma unroll
-            for (int e = 0; e < 8; ++e) pp[j][e] = (T)s[j >> 1][8 * (j & 1) + e];
+            for (int j = 0; j < 2 * NKB; ++j) {
+                uint32_t c[4] = {(uint32_t)(t * (BN / 16) + j), (uint32_t)(rb + lq),
+                                 (uint32_t)(tc.h + 256 * tc.b), p.drop_offset};
+                philox4x32_10(c, p.seed_lo, p.seed_hi);
+                const uint32_t wa = hf ? c[1] : c[0], wb = hf ? c[3] : c[2];
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t byte = ((e < 4 ? wa : wb) >> (8 * (e & 3))) & 0xffu;
+                    pp[j][e] = byte >= p.drop_thr ? (T)s[j >> 1][8 * (j & 1) + e] : (T)0.f;
+                }
+            }
+        } else {
+            #pragma unroll
+            for (int j = 0; j < 2 * NKB; ++j)
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) pp[j][e] = (T)s[j >> 1][8 * (j & 1) + e];
+        }
     };
 
     // Iteration t: prefetch tile t+PF into registers; S(t+1) = K Q^T and O += P(t-1) V(t-1)
@@ -484,7 +502,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         const float mc = any ? m_true * 0.69314718055994530942f : -INFINITY;
         float m_out = mc;
         float l_out = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
-        float wc = any ? 1.f / lt : 0.f;   // weight of the accumulator O
+        float wc = any ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;   // weight of the accumulator O
         float wp = 0.f;                    // weight of the prior output
         if constexpr (UPDATE) {
             const float mp = p.prev_max[st_base + qi], lp = p.prev_sum[st_base + qi];
@@ -541,6 +559,21 @@ hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
     return hipGetLastError();
 }
 
+// dropout on the probabilities (plain forward, value head dim = head dim)
+template <typename T>
+hipError_t launch_drop(const FaParams& p, int D, hipStream_t stream)
+{
+    dim3 grid(p.n_slots), block(NT);
+    switch (D) {
+    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, 32, T, false, false, true>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 64, T, false, false, true>), grid, block, 0, stream, p); break;
+    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, 96, T, false, false, true>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 128, T, false, false, true>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // value head dim below the Q/K head dim (plain forward only)
 template <typename T>
 hipError_t launch_dv(const FaParams& p, int D, int Dv, hipStream_t stream)
@@ -564,6 +597,10 @@ hipError_t launch_dv(const FaParams& p, int D, int Dv, hipStream_t stream)
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream)
 {
     const bool upd = p.prev_out != nullptr;
+    if (p.drop_thr) {
+        if (upd || p.amask || p.Dv != D) return hipErrorInvalidValue;
+        return f16 ? launch_drop<_Float16>(p, D, stream) : launch_drop<__bf16>(p, D, stream);
+    }
     if (p.Dv != D) {
         if (upd || p.amask) return hipErrorInvalidValue;
         return f16 ? launch_dv<_Float16>(p, D, p.Dv, stream) : launch_dv<__bf16>(p, D, p.Dv, stream);

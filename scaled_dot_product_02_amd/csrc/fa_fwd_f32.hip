@@ -42,7 +42,8 @@ __device__ inline void store4(T* x, float4 v)
 // T: input / output type; UPDATE = true: the epilogue merges the partial result into
 // p.prev_* (ring update); MASKED = true: p.amask removes keys as well.
 // D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
-template <typename T, int D, int DV, bool UPDATE, bool MASKED>
+// DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
+template <typename T, int D, int DV, bool UPDATE, bool MASKED, bool DROP = false>
 __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
 {
     __shared__ __attribute__((aligned(16))) float Ks[BN * D];
@@ -116,10 +117,20 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
             l_run *= alpha;
             #pragma unroll
             for (int d = 0; d < DV; ++d) o[d] *= alpha;
+            uint32_t dw[4] = {0, 0, 0, 0};   // dropout bytes of the chunk's 16 keys
+            if constexpr (DROP) {
+                dw[0] = (uint32_t)((j0 + c0) >> 4);
+                dw[1] = (uint32_t)qi;
+                dw[2] = (uint32_t)(tc.h + 256 * tc.b);
+                dw[3] = p.drop_offset;
+                philox4x32_10(dw, p.seed_lo, p.seed_hi);
+            }
             #pragma unroll
             for (int jj = 0; jj < CH; ++jj) {
-                const float e = __builtin_amdgcn_exp2f(s[jj] - m_use);
+                float e = __builtin_amdgcn_exp2f(s[jj] - m_use);
                 l_run += e;
+                if constexpr (DROP)
+                    if (((dw[jj >> 2] >> (8 * (jj & 3))) & 0xffu) < p.drop_thr) e = 0.f;
                 const float* vr = Vs + (c0 + jj) * DV;
                 #pragma unroll
                 for (int d = 0; d < DV; ++d) o[d] = __builtin_fmaf(e, vr[d], o[d]);
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
         const bool any = l_run > 0.f;
         const float mc = any ? m_run * 0.69314718055994530942f : -INFINITY;
         float m_out = mc, l_out = l_run;
-        float wc = any ? 1.f / l_run : 0.f, wp = 0.f;
+        float wc = any ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f, wp = 0.f;
         if constexpr (UPDATE) {
             const float mp = p.prev_max[st_base + qi], lp = p.prev_sum[st_base + qi];
             const float m = fmaxf(mp, mc);
@@ -173,6 +184,18 @@ template <typename T, bool UPDATE, bool MASKED>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
     dim3 grid(p.n_slots), block(64);
+    if (p.drop_thr) {   // dropout: plain fp32 forward with Dv = D
+        if constexpr (UPDATE || MASKED || sizeof(T) != 4) return hipErrorInvalidValue;
+        else if (p.Dv != D) return hipErrorInvalidValue;
+        else switch (D) {
+        case 32: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 32, 32, false, false, true>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 64, 64, false, false, true>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 96, 96, false, false, true>), grid, block, 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((fa_fwd_f32_kernel<T, 128, 128, false, false, true>), grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (p.Dv != D) {   // value head dim below the Q/K head dim: plain fp32 forward only
         if constexpr (UPDATE || MASKED || sizeof(T) != 4) return hipErrorInvalidValue;
         else if (D == 64 && p.Dv == 32)

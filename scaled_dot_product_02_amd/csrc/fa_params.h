@@ -40,6 +40,10 @@ struct FaParams {
     const uint8_t* amask;       // device [Sq][Skv] bytes or null: nonzero = masked out,
                                 // sequence-local positions (VALU kernel only)
     int64_t amask_ld;           // row stride of amask
+    uint32_t drop_thr;          // dropout: a probability is dropped when its byte < drop_thr
+    float drop_scale;           // 256 / (256 - drop_thr), applied to the kept ones
+    uint32_t seed_lo, seed_hi;  // Philox4x32-10 key
+    uint32_t drop_offset;       // fourth counter word
     float scale;                // softmax scale
     float scale_log2;           // scale * log2(e)
 };

@@ -53,6 +53,21 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 // head dims with a built attention kernel (every dtype)
 bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
+// Dropout probability p -> byte threshold round(256 p) and the scale of kept probabilities;
+// p must be finite in [0, 1) with threshold < 256.  Threshold 0 is no dropout.
+miattn_status_t set_dropout(FaParams& p, float prob, uint64_t seed, uint32_t offset)
+{
+    if (!(prob >= 0.f && prob < 1.f)) return MIATTN_ERR_DROPOUT;
+    const int thr = (int)lrintf(prob * 256.f);
+    if (thr >= 256) return MIATTN_ERR_DROPOUT;
+    p.drop_thr = (uint32_t)thr;
+    p.drop_scale = 256.f / (float)(256 - thr);
+    p.seed_lo = (uint32_t)seed;
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.drop_offset = offset;
+    return MIATTN_OK;
+}
+
 // (Q/K head dim, V head dim) pairs with a built kernel; a smaller V head dim only for the
 // plain forward (no fused update, no mask tensor)
 miattn_status_t check_head_dims(int64_t D, int64_t Dv, bool update, bool amask)
@@ -116,6 +131,7 @@ const char* miattn_status_str(miattn_status_t s)
     case MIATTN_ERR_UNSUPPORTED: return "valid but not built (head_dim, dtype or grid size)";
     case MIATTN_ERR_LAUNCH: return "kernel launch failed";
     case MIATTN_ERR_SCALE: return "scale must be finite and positive";
+    case MIATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1) with round(256 p) < 256";
     }
     return "unknown status";
 }
@@ -131,7 +147,8 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
                           int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
                           int64_t Dv, int dtype, int layout, float scale,
                           int mask, int64_t pre_tokens, int64_t next_tokens,
-                          const int64_t* prefix, const uint8_t* atten_mask, void* stream)
+                          const int64_t* prefix, const uint8_t* atten_mask,
+                          float dropout_p, uint64_t seed, uint32_t offset, void* stream)
 {
     if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -150,9 +167,12 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
     if (st != MIATTN_OK) return st;
     p.Dv = (int32_t)Dv;
+    st = set_dropout(p, dropout_p, seed, offset);
+    if (st != MIATTN_OK) return st;
     p.prefix = prefix;
     p.amask = atten_mask;
     p.amask_ld = Skv;
+    if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     const Strides so = strides_of(layout, B, Nq, Sq, Dv), sv = strides_of(layout, B, Nkv, Skv, Dv);
@@ -182,7 +202,8 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
                            int64_t Nq, int64_t Nkv, int64_t D, int64_t Dv,
                            int dtype, float scale,
                            int mask, int64_t pre_tokens, int64_t next_tokens,
-                           const int64_t* prefix, const uint8_t* atten_mask, void* stream)
+                           const int64_t* prefix, const uint8_t* atten_mask,
+                          float dropout_p, uint64_t seed, uint32_t offset, void* stream)
 {
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_kv) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -202,9 +223,12 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
     if (st != MIATTN_OK) return st;
     p.Dv = (int32_t)Dv;
+    st = set_dropout(p, dropout_p, seed, offset);
+    if (st != MIATTN_OK) return st;
     p.prefix = prefix;
     p.amask = atten_mask;
     p.amask_ld = max_seqlen_kv;
+    if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;
@@ -234,7 +258,7 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
 {
     return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
                      Sq, Skv, D, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
-                     nullptr, stream);
+                     nullptr, 0.f, 0, 0, stream);
 }
 
 miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
@@ -248,7 +272,8 @@ miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, voi
 {
     return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
+                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, 0.f, 0,
+                      0, stream);
 }
 
 miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
@@ -261,7 +286,7 @@ miattn_status_t attn_fwd_update(const void* q, const void* k, const void* v,
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_dense(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum, B, Nq, Nkv,
                      Sq, Skv, D, D, dtype, layout, scale, mask, pre_tokens, next_tokens, nullptr,
-                     nullptr, stream);
+                     nullptr, 0.f, 0, 0, stream);
 }
 
 miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void* v,
@@ -279,22 +304,24 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
     if (!prev_out || !prev_max || !prev_sum || !out_max || !out_sum) return MIATTN_ERR_NULL;
     return fwd_varlen(q, k, v, prev_out, prev_max, prev_sum, out, out_max, out_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, stream);
+                      D, D, dtype, scale, mask, pre_tokens, next_tokens, nullptr, nullptr, 0.f, 0,
+                      0, stream);
 }
 
-miattn_status_t attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
+miattn_status_t attn_fwd_ext(const void* q, const void* k, const void* v, void* out,
                                 float* softmax_max, float* softmax_sum,
                                 int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
                                 int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout, float scale,
                                 miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
-                                const int64_t* prefix, const uint8_t* atten_mask, void* stream)
+                                const int64_t* prefix, const uint8_t* atten_mask,
+                                float dropout_p, uint64_t seed, uint32_t offset, void* stream)
 {
     return fwd_dense(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum, B, Nq, Nkv,
                      Sq, Skv, D, Dv, dtype, layout, scale, mask, pre_tokens, next_tokens, prefix,
-                     atten_mask, stream);
+                     atten_mask, dropout_p, seed, offset, stream);
 }
 
-miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* out,
+miattn_status_t attn_fwd_varlen_ext(const void* q, const void* k, const void* v, void* out,
                                        float* softmax_max, float* softmax_sum,
                                        const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
                                        int64_t B, int64_t Tq, int64_t Tkv,
@@ -303,11 +330,13 @@ miattn_status_t attn_fwd_varlen_masked(const void* q, const void* k, const void*
                                        miattn_dtype_t dtype, float scale,
                                        miattn_mask_t mask, int64_t pre_tokens, int64_t next_tokens,
                                        const int64_t* prefix, const uint8_t* atten_mask,
+                                       float dropout_p, uint64_t seed, uint32_t offset,
                                        void* stream)
 {
     return fwd_varlen(q, k, v, nullptr, nullptr, nullptr, out, softmax_max, softmax_sum,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
-                      D, Dv, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask, stream);
+                      D, Dv, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask,
+                      dropout_p, seed, offset, stream);
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

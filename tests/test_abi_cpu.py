@@ -23,7 +23,7 @@ def _declared():
 def test_header_declares_every_entry_point():
     d = _declared()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-                 "attn_fwd_masked", "attn_fwd_varlen_masked", "attn_lse_merge", "sparse_csr_attn",
+                 "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
                  "miattn_status_str"):
         assert name in d, d
 
@@ -166,13 +166,13 @@ def test_attn_fwd_varlen_update_validation(mi):
     assert call(D=100) == "MIATTN_ERR_UNSUPPORTED"
 
 
-def test_attn_fwd_masked_validation(mi):
+def test_attn_fwd_ext_validation(mi):
     def call(**kw):
         a = dict(q=P, B=1, Nq=4, Nkv=2, Sq=16, Skv=16, D=64, Dv=64, dtype="bf16", layout="BNSD",
                  scale=0.125, mask="causal_br", pre=0, nxt=0, prefix=None, am=None)
         a.update(kw)
         with pytest.raises(mi.MiattnError) as e:
-            mi.attn_fwd_masked(a["q"], P, P, P, None, None, a["B"], a["Nq"], a["Nkv"], a["Sq"],
+            mi.attn_fwd_ext(a["q"], P, P, P, None, None, a["B"], a["Nq"], a["Nkv"], a["Sq"],
                                a["Skv"], a["D"], a["Dv"], a["dtype"], a["layout"], a["scale"],
                                a["mask"], a["pre"], a["nxt"], a["prefix"], a["am"], stream=0)
         return mi.STATUS[e.value.status]
@@ -187,11 +187,24 @@ def test_attn_fwd_masked_validation(mi):
     assert call(D=64, Dv=48) == "MIATTN_ERR_UNSUPPORTED"         # pair not built
     assert call(D=128, Dv=64, am=P) == "MIATTN_ERR_UNSUPPORTED"  # Dv < D without a mask tensor
 
+    def dcall(p, **kw):
+        with pytest.raises(mi.MiattnError) as e:
+            mi.attn_fwd_ext(P, P, P, P, None, None, 1, 4, 2, 16, 16, kw.get("D", 64),
+                            kw.get("Dv", 64), "bf16", "BNSD", 0.125, "causal", 0, 0, None,
+                            kw.get("am"), p, 1, 0, stream=0)
+        return mi.STATUS[e.value.status]
+    assert dcall(1.0) == "MIATTN_ERR_DROPOUT"
+    assert dcall(-0.01) == "MIATTN_ERR_DROPOUT"
+    assert dcall(float("nan")) == "MIATTN_ERR_DROPOUT"
+    assert dcall(0.999) == "MIATTN_ERR_DROPOUT"                   # rounds to 256/256
+    assert dcall(0.5, am=P) == "MIATTN_ERR_UNSUPPORTED"
+    assert dcall(0.5, D=128, Dv=64) == "MIATTN_ERR_UNSUPPORTED"
+
     def vcall(**kw):
         a = dict(mask="causal", prefix=P, D=128, Dv=128)
         a.update(kw)
         with pytest.raises(mi.MiattnError) as e:
-            mi.attn_fwd_varlen_masked(P, P, P, P, None, None, P, P, 3, 100, 100, 50, 50, 8, 2,
+            mi.attn_fwd_varlen_ext(P, P, P, P, None, None, P, P, 3, 100, 100, 50, 50, 8, 2,
                                       a["D"], a["Dv"], "bf16", 0.1, a["mask"], 3, 3, a["prefix"],
                                       P, stream=0)
         return mi.STATUS[e.value.status]

@@ -1,6 +1,6 @@
 """GPU parity of the mask modes against the CPU fp64 oracle's explicit visibility matrices:
 bottom-right causal and band (attn_fwd, attn_fwd_varlen, attn_fwd_update), the prefix
-(attn_fwd_varlen_masked / attn_fwd_masked), and an explicit mask tensor (any dtype; rows of
+(attn_fwd_varlen_ext / attn_fwd_ext), and an explicit mask tensor (any dtype; rows of
 whole 4-byte words on the matrix cores for bf16 / fp16, other rows on the vector ALUs).  Sizes span several tiles with ragged ends; Sq > Skv gives empty rows.
 """
 import math
@@ -37,7 +37,7 @@ def _dense_gpu(mi, w, scale, mask, pre=0, nxt=0, prefix=None, amask=None):
     m, l = nan_stats((B, Nq, Sq)), nan_stats((B, Nq, Sq))
     pf = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
     am = None if amask is None else torch.from_numpy(np.ascontiguousarray(amask, np.uint8)).to("cuda:0")
-    mi.attn_fwd_masked(q, k, v, out, m, l, B, Nq, Nkv, Sq, Skv, D, Dv, dt, w["layout"], scale,
+    mi.attn_fwd_ext(q, k, v, out, m, l, B, Nq, Nkv, Sq, Skv, D, Dv, dt, w["layout"], scale,
                        mask, pre, nxt, pf, am)
     torch.cuda.synchronize()
     return synthetic.to_bnsd(host_values(out), w["layout"], Nq), host_values(m), host_values(l)
@@ -106,7 +106,7 @@ def _varlen_gpu(mi, w, scale, mask, pre=0, nxt=0, prefix=None, amask=None):
     m, l = nan_stats((w["Nq"], w["Tq"])), nan_stats((w["Nq"], w["Tq"]))
     pf = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
     am = None if amask is None else torch.from_numpy(np.ascontiguousarray(amask, np.uint8)).to("cuda:0")
-    mi.attn_fwd_varlen_masked(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"],
+    mi.attn_fwd_varlen_ext(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"],
                               int(w["lengths_q"].max()), int(w["lengths_kv"].max()), w["Nq"],
                               w["Nkv"], w["D"], Dv, dt, scale, mask, pre, nxt, pf, am)
     torch.cuda.synchronize()
