@@ -10,8 +10,8 @@ Also measured in the same run (reported under "secondary"):
   * the same forward with fp16 storage (same lengths and draws; 2.5 PFLOP/s fp16 peak);
   * the same forward with bottom-right causal plus a prefix of L/3 keys per sequence;
   * the same forward with dropout 0.1 on the probabilities;
-  * an explicit mask tensor on dense bf16 [1, 8, 4096, 128], causal with 25% of keys masked
-    out at random;
+  * an explicit mask tensor on dense bf16 [2, 32, 4096, 128], causal with 25% of keys
+    masked out at random;
   * attn_lse_merge on the ring-merge workload (S 8192, N 32, D 128, SBH bf16), timed over
     rotating buffer sets (about 830 MB, larger than the 256 MB last-level cache);
   * causal attention over that workload's 4 key chunks of 2048 (a ring on one GPU): the
@@ -263,25 +263,25 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(dtf_, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(dtf_ / PEAK_BF16_TFLOPS, 4)}}
 
-        # explicit mask tensor: dense bf16 [1, 8, 4096, 128], causal plus a random 25% of
+        # explicit mask tensor: dense bf16 [2, 32, 4096, 128], causal plus a random 25% of
         # keys masked out (rows of whole 4-byte words: the MFMA path)
-        Sx = 4096
-        wx = synthetic.dense_inputs(0, 1, 8, 8, Sx, Sx, D, "bf16", "BNSD")
+        Sx, Bx, Nx = 4096, 2, 32
+        wx = synthetic.dense_inputs(0, Bx, Nx, Nx, Sx, Sx, D, "bf16", "BNSD")
         xq, xk, xv = up(wx["q"], "bf16"), up(wx["k"], "bf16"), up(wx["v"], "bf16")
         xo = torch.empty_like(xq)
         am_np = np.random.default_rng(0).random((Sx, Sx)) < 0.25
         xam = torch.from_numpy(am_np.astype(np.uint8)).to(dev)
         xpairs = int((np.tril(np.ones((Sx, Sx), dtype=bool)) & ~am_np).sum())
-        xflops = 4.0 * D * 8 * xpairs
+        xflops = 4.0 * D * Bx * Nx * xpairs
 
         def step_amask():
-            mi.attn_fwd_ext(xq, xk, xv, xo, None, None, 1, 8, 8, Sx, Sx, D, D, "bf16", "BNSD",
+            mi.attn_fwd_ext(xq, xk, xv, xo, None, None, Bx, Nx, Nx, Sx, Sx, D, D, "bf16", "BNSD",
                                scale, "causal", 0, 0, None, xam, stream=stream.cuda_stream)
 
         xms = time_launches(step_amask, 5, 1, stream)
         xtf = xflops / (xms * 1e-3) / 1e12
         sec["attn_fwd_explicit_mask"] = {
-            "workload": "dense_bf16_b1n8s4096d128_causal_random_mask_25pct",
+            "workload": "dense_bf16_b2n32s4096d128_causal_random_mask_25pct",
             "ms_per_launch": round(xms, 3), "flop_per_launch": xflops,
             "roofline": {"bound": "mfma", "achieved": round(xtf, 3), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(xtf / PEAK_BF16_TFLOPS, 4)}}
