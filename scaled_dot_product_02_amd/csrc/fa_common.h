@@ -10,6 +10,7 @@ struct TileCoord {
     int t;                  // q-tile index inside the sequence
     int64_t q0, kv0;        // first packed row of the sequence (0 for dense batches)
     int len_q, len_kv;      // sequence lengths
+    int r0, r1;             // query rows [r0, r1) of the tile
     bool live;
 };
 
@@ -47,6 +48,11 @@ __device__ inline TileCoord decode_tile(const FaParams& p, int L, int tile_m)
         c.len_kv = (int)(p.cu_kv[c.b] - c.kv0);
     }
     if (c.live && (int64_t)c.t * tile_m >= c.len_q) c.live = false;
+    // Tiles end at the sequence end: the ragged tile is the first one (the rows that see the
+    // fewest keys under a causal mask), and the heaviest tiles are full.
+    const int pad = (tile_m - c.len_q % tile_m) % tile_m;
+    c.r0 = max(0, c.t * tile_m - pad);
+    c.r1 = min(c.len_q, (c.t + 1) * tile_m - pad);
     return c;
 }
 

@@ -164,8 +164,8 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     const int hf = lane >> 5;   // half of the wave
 
     const int len_q = tc.len_q, len_kv = tc.len_kv;
-    const int i0 = tc.t * BM;
-    const int i1 = min(i0 + BM, len_q);
+    const int i0 = tc.r0;
+    const int i1 = tc.r1;
 
     const __bf16* qg = (const __bf16*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
     const __bf16* kg = (const __bf16*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;

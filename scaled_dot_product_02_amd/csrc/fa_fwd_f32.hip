@@ -52,8 +52,8 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FaParams p)
     const TileCoord tc = decode_tile(p, blockIdx.x, BM);
     if (!tc.live) return;
     const int lane = threadIdx.x;
-    const int i0 = tc.t * BM;
-    const int i1 = min(i0 + BM, tc.len_q);
+    const int i0 = tc.r0;
+    const int i1 = tc.r1;
     const int qi = i0 + lane;
 
     const T* qg = (const T*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
