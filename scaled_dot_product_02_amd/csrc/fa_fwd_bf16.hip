@@ -428,13 +428,33 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 = element 8(j%2) + e of block j/2
         if constexpr (DROP) {
             // MFMA j covers the 16 keys of Philox block 4t + j; slot e takes byte e%4 of
-            // word 2(e/4) + hf
+            // word 2(e/4) + hf.  Lanes l and l + 32 hold the same query row: each computes
+            // the blocks j = hf + 2k and hands the partner the two words it needs.
+            static_assert(2 * NKB == 4, "dropout assumes four 16-key blocks per tile");
+            uint32_t W[2][4];
+            #pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                W[k][0] = (uint32_t)(t * (BN / 16) + hf + 2 * k);
+                W[k][1] = (uint32_t)(rb + lq);
+                W[k][2] = (uint32_t)(tc.h + 256 * tc.b);
+                W[k][3] = p.drop_offset;
+                philox4x32_10(W[k], p.seed_lo, p.seed_hi);
+            }
+            uint32_t got[4];   // the partner's words hf and 2 + hf of its blocks
+            #pragma unroll
+            for (int k = 0; k < 2; ++k)
+                #pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t x = hf ? W[k][2 * w] : W[k][2 * w + 1];
+                    auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                    got[2 * k + w] = hf ? r[0] : r[1];
+                }
             #pragma unroll
             for (int j = 0; j < 2 * NKB; ++j) {
-                uint32_t c[4] = {(uint32_t)(t * (BN / 16) + j), (uint32_t)(rb + lq),
-                                 (uint32_t)(tc.h + 256 * tc.b), p.drop_offset};
-                philox4x32_10(c, p.seed_lo, p.seed_hi);
-                const uint32_t wa = hf ? c[1] : c[0], wb = hf ? c[3] : c[2];
+                const int k = j >> 1;
+                const bool own = (j & 1) == hf;
+                const uint32_t wa = own ? (hf ? W[k][1] : W[k][0]) : got[2 * k];
+                const uint32_t wb = own ? (hf ? W[k][3] : W[k][2]) : got[2 * k + 1];
                 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t byte = ((e < 4 ? wa : wb) >> (8 * (e & 3))) & 0xffu;
