@@ -9,7 +9,8 @@
 //   * chunk max and sum by wave butterflies; the running max / sum are rescaled once per
 //     chunk (online softmax in the log2 domain);
 //   * value phase: the chunk's (probability, column) pairs are broadcast lane by lane and
-//     every lane accumulates its own head-dim slice of sum_c p_c v_c (coalesced row reads).
+//     every lane accumulates its own head-dim slice of sum_c p_c v_c (coalesced row reads),
+//     16 value rows per batch with all their loads in flight together.
 // Work per row is proportional to its entry count; four consecutive rows of one slice
 // share a workgroup so their common columns are re-read from L1/L2.
 #include "fa_params.h"
@@ -105,7 +106,27 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
         l_run = l_run * alpha + wave_sum(pv);
         #pragma unroll
         for (int u = 0; u < PL; ++u) o[u] *= alpha;
-        for (int e = 0; e < cnt; ++e) {
+        // value rows in batches of VB entries: all loads of a batch are in flight together
+        // (one entry at a time would wait out a full memory latency per entry)
+        constexpr int VB = 16;
+        int e = 0;
+        for (; e + VB <= cnt; e += VB) {
+            T vv[VB][PL];
+            #pragma unroll
+            for (int x = 0; x < VB; ++x) {
+                const T* vr = vb + (int64_t)__builtin_amdgcn_readlane(c, e + x) * D;
+                #pragma unroll
+                for (int u = 0; u < PL; ++u)
+                    vv[x][u] = (D % 64 == 0 || lane + 64 * u < D) ? vr[lane + 64 * u] : (T)0;
+            }
+            #pragma unroll
+            for (int x = 0; x < VB; ++x) {
+                const T pe = lane_value(pv, e + x);
+                #pragma unroll
+                for (int u = 0; u < PL; ++u) o[u] = fma(pe, vv[x][u], o[u]);
+            }
+        }
+        for (; e < cnt; ++e) {
             const T pe = lane_value(pv, e);
             const int ce = __builtin_amdgcn_readlane(c, e);
             const T* vr = vb + (int64_t)ce * D;
