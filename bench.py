@@ -74,7 +74,7 @@ def load_probes():
     """The peak probes (include/miattn_probes.h) through ctypes."""
     import ctypes
     if not os.path.exists(PROBES_LIB):
-        raise SystemExit(f"{PROBES_LIB} is missing: run __graft_entry__.build() first")
+        raise SystemExit(f"{PROBES_LIB} is missing: build it with `python -m scaled_dot_product_02_amd.build`")
     lib = ctypes.CDLL(PROBES_LIB)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.miattn_probe_mfma_bf16.argtypes = [P, I32, I32, P]

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmiattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m scaled_dot_product_02_amd.build` "
-        "(or __graft_entry__.build()); there is no non-HIP fallback")
+        f"{LIB_PATH} is missing: build it with `python -m scaled_dot_product_02_amd.build`; "
+        "there is no non-HIP fallback")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
