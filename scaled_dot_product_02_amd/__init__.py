@@ -5,7 +5,9 @@ the C entry point; pointer arguments accept torch tensors (their data_ptr()), pl
 integers or None; enum arguments accept the C values or their names ("bf16", "SBH",
 "causal").  `stream` defaults to torch's current HIP stream.  A non-OK status raises
 MiattnError.  All computation runs in the HIP kernels of libmiattn.so; there is no
-fallback: importing this package fails if the library has not been built.
+fallback: importing this package fails if the library has not been built.  With
+MIATTN_CHECK=1 the device metadata (cumulative lengths, CSR rows) is copied back and
+validated before the call (a debugging aid that synchronizes).
 """
 from __future__ import annotations
 
@@ -88,6 +90,49 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _metadata_checks() -> bool:
+    """MIATTN_CHECK=1: validate device metadata on the host before a call (copies it back,
+    so it synchronizes; a debugging aid, off by default)."""
+    return os.environ.get("MIATTN_CHECK") == "1"
+
+
+def _host_ints(x):
+    import numpy as np
+    if hasattr(x, "detach"):
+        return x.detach().cpu().numpy().astype(np.int64).ravel()
+    return None
+
+
+def _check_cu(cu, B, T, name):
+    """Cumulative END offsets: B entries, non-decreasing from >= 0, last = T."""
+    h = _host_ints(cu)
+    if h is None:
+        return
+    import numpy as np
+    if len(h) < B or (B and (h[0] < 0 or np.any(np.diff(h[:B]) < 0) or h[B - 1] != T)):
+        raise ValueError(f"{name}: cumulative lengths must be {B} non-decreasing end offsets "
+                         f"ending at {T}")
+
+
+def _check_csr(offset, columns, nnz, B, N, S):
+    """CSR rows: offset[b][n] starts at 0, is non-decreasing and ends at most nnz; the used
+    columns lie in [0, S)."""
+    off = _host_ints(offset)
+    if off is None:
+        return
+    import numpy as np
+    off = off.reshape(B * N, S + 1)
+    if np.any(off[:, 0] != 0) or np.any(np.diff(off, axis=1) < 0) or np.any(off[:, -1] > nnz):
+        raise ValueError("csr_offset: rows must start at 0, be non-decreasing and end <= nnz")
+    cols = _host_ints(columns)
+    if cols is not None and nnz:
+        cols = cols.reshape(B * N, nnz)
+        for r in range(B * N):
+            used = cols[r, :off[r, -1]]
+            if used.size and (used.min() < 0 or used.max() >= S):
+                raise ValueError("csr_columns: columns must lie in [0, S)")
+
+
 def _check(rc: int, where: str):
     if rc != 0:
         raise MiattnError(rc, where)
@@ -104,6 +149,9 @@ def attn_fwd(q, k, v, out, softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D,
 def attn_fwd_varlen(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_kv,
                     B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask,
                     pre_tokens=0, next_tokens=0, stream=None):
+    if _metadata_checks():
+        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                 _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
                                 B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
@@ -125,6 +173,9 @@ def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, 
                            cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q,
                            max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask, pre_tokens=0,
                            next_tokens=0, stream=None):
+    if _metadata_checks():
+        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen_update(_ptr(q), _ptr(k), _ptr(v), _ptr(prev_out),
                                        _ptr(prev_max), _ptr(prev_sum), _ptr(out), _ptr(out_max),
                                        _ptr(out_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
@@ -148,6 +199,9 @@ def attn_fwd_varlen_ext(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu
                            B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv, dtype, scale,
                            mask, pre_tokens=0, next_tokens=0, prefix=None, atten_mask=None,
                            dropout_p=0.0, seed=0, offset=0, stream=None):
+    if _metadata_checks():
+        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                        _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
                                        B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv,
@@ -167,6 +221,8 @@ def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out,
 
 def sparse_csr_attn(q, k, v, out, csr_offset, csr_columns, nnz, B, N, S, D, dtype, scale,
                     stream=None):
+    if _metadata_checks():
+        _check_csr(csr_offset, csr_columns, nnz, B, N, S)
     _check(_lib.sparse_csr_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(csr_offset),
                                 _ptr(csr_columns), nnz, B, N, S, D, _enum(dtype, DTYPES),
                                 scale, _stream(stream)), "sparse_csr_attn")

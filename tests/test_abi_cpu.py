@@ -255,3 +255,24 @@ def test_status_strings(mi):
     for code in range(10):
         assert mi.status_str(code) and mi.status_str(code) != "unknown status"
     assert mi.status_str(99) == "unknown status"
+
+
+def test_host_metadata_checks(mi, monkeypatch):
+    """MIATTN_CHECK=1 validates cumulative lengths and CSR rows on the host before the call
+    (CPU tensors here, so no GPU is touched: every case fails before the C entry point)."""
+    import torch
+    monkeypatch.setenv("MIATTN_CHECK", "1")
+    cu_bad = torch.tensor([3, 2, 6], dtype=torch.int64)      # decreasing
+    cu_short = torch.tensor([3, 4, 5], dtype=torch.int64)    # last != T
+    for cu in (cu_bad, cu_short):
+        with pytest.raises(ValueError):
+            mi.attn_fwd_varlen(P, P, P, P, None, None, cu, cu, 3, 6, 6, 4, 4, 2, 2, 64, "bf16",
+                               0.1, "causal", stream=0)
+    off = torch.tensor([[[0, 2, 1, 3]]], dtype=torch.int32)  # non-decreasing violated
+    col = torch.zeros((1, 1, 4), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mi.sparse_csr_attn(P, P, P, P, off, col, 4, 1, 1, 3, 64, "f32", 0.1, stream=0)
+    off = torch.tensor([[[0, 1, 2, 3]]], dtype=torch.int32)
+    col = torch.tensor([[[0, 5, 1, 0]]], dtype=torch.int32)  # column 5 >= S = 3
+    with pytest.raises(ValueError):
+        mi.sparse_csr_attn(P, P, P, P, off, col, 4, 1, 1, 3, 64, "f32", 0.1, stream=0)
