@@ -193,7 +193,7 @@ def main():
     # ---------------- measured ceilings: dense bf16 MFMA rate of the chip ----------------
     probes = load_probes()
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count   # 8 waves per CU
-    iters = 512
+    iters = 4096   # about a millisecond per launch: long enough for the clock to settle
     pout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
 
     def mfma_probe():
@@ -206,7 +206,7 @@ def main():
     result["measured_peaks"] = {
         "mfma_bf16_tflops": round(mfma_meas, 1),
         "mfma_method": f"{blocks} workgroups x 4 waves, back-to-back v_mfma_f32_32x32x16_bf16 "
-                       "on 8 independent accumulators"}
+                       "on 8 independent accumulators, random bf16 operands rotating per MFMA"}
     result["roofline"]["measured_peak"] = round(mfma_meas, 1)
     result["roofline"]["frac_of_measured_peak"] = round(tflops / mfma_meas, 4)
     del pout

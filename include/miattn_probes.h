@@ -3,7 +3,8 @@
  *
  * Measurement aids for the roofline figures of the benchmark, not part of the attention
  * library: the dense bf16 matrix-core rate of the whole chip (back-to-back
- * v_mfma_f32_32x32x16_bf16 on independent accumulators) and the bandwidth of a plain
+ * v_mfma_f32_32x32x16_bf16 on independent accumulators, with random operands: the chip
+ * clocks lower on random data than on constant operands) and the bandwidth of a plain
  * streaming pass that reads two arrays and writes one.  The caller times the launches
  * (e.g. with events on `stream`); the functions only enqueue work.  All pointers are device
  * pointers owned by the caller.  Each returns 0 on success or the HIP error code.

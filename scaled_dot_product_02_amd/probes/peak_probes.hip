@@ -14,22 +14,44 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChains = 8;   // independent accumulators: the matrix pipe never waits on a result
 
-__global__ __launch_bounds__(kThreads) void mfma_bf16_loop(float* out, int iters)
+__device__ inline unsigned mix32(unsigned x)
 {
-    const int lane = threadIdx.x & 63;
-    bf16x8 a, b;
+    x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+    return x;
+}
+
+// eight bf16 values of magnitude in [0.5, 1) with random signs and mantissas.  The MFMA rate
+// the chip sustains depends on the operand data: constant operands barely toggle the
+// multipliers and run at a higher clock than the random data of a real workload.
+__device__ inline bf16x8 random_operand(unsigned key)
+{
+    bf16x8 v;
     #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        a[e] = (__bf16)(0.001f * (float)(lane + e));
-        b[e] = (__bf16)(0.002f * (float)(lane - e));
+        const unsigned h = mix32(key * 8u + (unsigned)e);
+        v[e] = __builtin_bit_cast(__bf16, (unsigned short)((h & 0x8000u) | (0x3f00u + ((h >> 4) & 0xffu))));
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_bf16_loop(float* out, int iters)
+{
+    const unsigned key = (blockIdx.x * kThreads + threadIdx.x) * 8u;
+    bf16x8 a[4], b[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = random_operand(key + i);
+        b[i] = random_operand(0x9e3779b9u + key + i);
     }
     f32x16 acc[kChains];
     #pragma unroll
     for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
     for (int i = 0; i < iters; ++i) {
+        // every MFMA takes a different operand pair from the one before it (the indices are
+        // compile-time constants, so the operands stay in registers)
         #pragma unroll
         for (int c = 0; c < kChains; ++c)
-            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c & 3], b[(c + 1 + (c >> 2)) & 3], acc[c], 0, 0, 0);
     }
     float s = 0.f;
     #pragma unroll
