@@ -9,14 +9,14 @@
 // Design (one workgroup = 8 waves = 256 query rows of one head; two waves per SIMD):
 //   * Each wave owns one 32-row query block, held in VGPRs for the whole kernel as MFMA
 //     B operands.  A wave needs under 256 registers with every accumulator in ordinary
-//     VGPRs, so two waves share each SIMD and the hardware overlaps one wave's softmax
-//     (vector ALU) with the other's matrix-core work.  Waves w and w + 4 share a SIMD,
-//     which evens out the causal triangle across the four SIMDs.
+//     VGPRs, so two waves share each SIMD.  Waves w and w + 4 share a SIMD, which evens
+//     out the causal triangle across the four SIMDs, and they run one phase apart (below)
+//     so that one wave's softmax (vector ALU) overlaps the other's matrix-core work.
 //   * Keys advance in tiles of 64.  K (row-major) and V (transposed, V^T[d][key]) tiles
 //     are staged from 128-bit buffer loads through registers into a 4-deep ring of LDS
-//     buffers with one barrier per tile; a tile's loads are issued two steps before its
-//     LDS stores (two register sets), which covers the memory latency under load.  Every
-//     thread stages the same share of each tile, with no branch.
+//     buffers; a tile's loads are issued two steps before its LDS stores (two register
+//     sets), which covers the memory latency under load.  Every thread stages the same
+//     share of each tile, with no branch.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns ONE query column and 16 of the
 //     32 keys, so the row max / row sum are in-lane reductions plus one exchange with the
 //     lane 32 apart.
@@ -24,8 +24,11 @@
 //     the S^T accumulator registers as the B operand.  The order of keys inside each MFMA
 //     follows the S^T register layout; the V^T rows in LDS store their keys in that same
 //     order (bits 2 and 3 of the key index swapped), so each A operand is one 128-bit read.
-//   * Software pipeline: iteration t issues QK(t+1) and PV(t-1) on the matrix cores and
-//     then runs the softmax of tile t on the vector ALUs, which overlap.
+//   * Software pipeline: step t issues QK(t) and PV(t-1) on the matrix cores (phase M) and
+//     then runs the softmax of tile t on the vector ALUs (phase S), each phase closed by a
+//     barrier.  Waves 4-7 run one phase behind waves 0-3, so each SIMD always has one wave
+//     in each phase; the M phase runs at raised wave priority so that the matrix issue is
+//     not starved by the partner's vector work.
 //   * Online softmax in the log2 domain (scale * log2(e) folded into one FMA before
 //     v_exp_f32).  The reference max m_ref moves only when a tile's max exceeds it by more
 //     than 2^8 (probabilities stay <= 256, safe in bf16 and fp32), so the O accumulator is
@@ -58,7 +61,7 @@ constexpr int BN = FA_BN;       // keys per tile
 constexpr int NKB = BN / 32;    // 32-key blocks per tile
 constexpr int PF = FA_PREFETCH; // tiles in flight ahead of the one in softmax (2 or 3)
 #ifndef FA_LDSD
-#define FA_LDSD 4
+#define FA_LDSD 6
 #endif
 #ifndef FA_SCHED
 #define FA_SCHED 1
@@ -469,24 +472,37 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         }
     };
 
-    // Iteration t: prefetch tile t+PF into registers; S(t+1) = K Q^T and O += P(t-1) V(t-1)
-    // on the matrix cores; softmax(t) on the vector ALUs; land tile t+2 in LDS.
+    // Step t is two phases, each closed by a barrier:
+    //   M: prefetch tile t+PF into registers; S(t) = K(t) Q^T and O += P(t-1) V(t-1) on the
+    //      matrix cores (the P V MFMAs cover the latency of S(t));
+    //   S: softmax(t) on the vector ALUs; land tile t+2 in LDS.
+    // Waves 4-7 run the same code one phase behind waves 0-3, so on every SIMD one wave is
+    // in its M phase while the other is in its S phase and the matrix cores and the vector
+    // ALUs work at the same time.  The M phase runs at raised wave priority: the SIMD
+    // otherwise favours the older wave, and a softmax of waves 0-3 would starve the MFMA
+    // issue of waves 4-7.  Tile t+2 is complete after the barrier that closes the late
+    // waves' S phase of step t, two phases before the first read of it, and overwrites the
+    // buffer of tile t-2, whose last reader (P V in the late waves' M phase of step t-1)
+    // finished one barrier earlier.
     X8 pp[2 * NKB];
-    auto step = [&](int t, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], u32x4 (&ld)[C::SREG],
-                    u32x4 (&sto)[C::SREG]) {
+    f32x16 sa[NKB];
+    const bool late = wave >= 4;
+    auto step = [&](int t, u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
         if constexpr (MASKED) {
             mbits = pack_mask(mw);             // mask of tile t, read one step earlier
             if (t + 1 < T1) load_mask(t + 1);
         }
+        __builtin_amdgcn_s_setprio(3);
         load_tile(t + PF, ld);
-        if (t + 1 < T1 && wave_active(t + 1)) qk(t + 1, sn);
+        if (wave_active(t)) qk(t, sa);
         if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
-        if (wave_active(t)) softmax(t, sc, pp);
+        __builtin_amdgcn_s_setprio(0);
+        __syncthreads();
+        if (wave_active(t)) softmax(t, sa, pp);
         store_tile(t + 2, sto);
         __syncthreads();
     };
 
-    f32x16 sa[NKB], sb[NKB];
     if (T0 < T1) {
         // Q and the first two tiles in one memory round trip; the wait also drains Q, so
         // no wait on it is left for the key loop (where it would also wait for prefetches)
@@ -498,16 +514,17 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         store_tile(T0 + 1, stB);
         if (PF == 3) load_tile(T0 + 2, stB);
         __syncthreads();
-        qk(T0, sa);
+        if (late) __syncthreads();    // the late waves' first phase is empty
         int t = T0;
         // tile t+2 sits in the register set loaded one step earlier when PF == 3
         u32x4 (&sB)[C::SREG] = PF == 3 ? stB : stA;
         for (; t + 1 < T1; t += 2) {
-            step(t, sa, sb, stA, sB);
-            step(t + 1, sb, sa, sB, stA);
+            step(t, stA, sB);
+            step(t + 1, sB, stA);
         }
-        if (t < T1) step(t, sa, sb, stA, sB);
+        if (t < T1) step(t, stA, sB);
         if (wave_active(T1 - 1)) pv(T1 - 1, pp);
+        if (!late) __syncthreads();   // the early waves' last phase is empty
     }
 
     // ---- epilogue: normalize, round to the storage type, store; emit the row statistics.
