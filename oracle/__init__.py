@@ -323,6 +323,48 @@ def sparse(q, k, v, offset, columns, scale: float, threads: int = 0):
     return out, m, l
 
 
+def mha_self_attn(x, w_qkv, b_qkv, w_out, b_out, N: int, keep=None, dropout=None,
+                  round_to=None, threads: int = 0):
+    """Forward of the multi-head self-attention module of "flash attention的调用" (its
+    MultiHeadAttention example): [q | k | v] = x W_qkv^T + b_qkv with the 3E outputs split
+    into thirds, each reshaped to N heads of D = E / N columns; per head softmax(q k^T /
+    sqrt(D)) v (no causal mask); the heads concatenated back; out = o W_out^T + b_out.
+
+    x (B,S,E); w_qkv (3E,E); b_qkv (3E,) or None; w_out (E,E); b_out (E,) or None.
+    keep: optional (S,S) bool visibility (True = the pair takes part).
+    dropout: optional (p, seed, offset), applied as attn_dropout (batch b, head h counters).
+    round_to: optional function applied where a storage type would round (the projections'
+    outputs and the attention output), so that a low-precision product can be compared
+    against the same roundings.  Returns out (B,S,E) in float64."""
+    x = _f64(x)
+    B, S, E = x.shape
+    if E % N:
+        raise ValueError("E must be a multiple of N")
+    D = E // N
+    qkv = x @ _f64(w_qkv).T
+    if b_qkv is not None:
+        qkv = qkv + _f64(b_qkv)
+    if round_to is not None:
+        qkv = round_to(qkv)
+    q, k, v = (np.ascontiguousarray(qkv[..., i * E:(i + 1) * E].reshape(B, S, N, D).transpose(0, 2, 1, 3))
+               for i in range(3))
+    scale = 1.0 / np.sqrt(D)
+    if dropout is not None:
+        p, seed, offset = dropout
+        o = attn_dropout(q, k, v, scale, "none", 0, 0, p, seed, offset, threads=threads)[0]
+    elif keep is not None:
+        o = attn_keep(q, k, v, keep, scale, threads)[0]
+    else:
+        o = attn(q, k, v, scale, "none", threads=threads)[0]
+    o = o.transpose(0, 2, 1, 3).reshape(B, S, E)
+    if round_to is not None:
+        o = round_to(o)
+    y = o @ _f64(w_out).T
+    if b_out is not None:
+        y = y + _f64(b_out)
+    return y
+
+
 def max_threads() -> int:
     """Threads the oracle uses when threads=0 (the OpenMP default of this process)."""
     try:

@@ -589,3 +589,69 @@ def test_sparse_rejects_out_of_range_columns():
     q = np.zeros((1, 1, 2, 2))
     with pytest.raises(ValueError):
         oracle.sparse(q, q, q, np.array([[[0, 1, 2]]], np.int32), np.array([[[0, 2]]], np.int32), 1.0)
+
+
+# ---- the multi-head self-attention module ("flash attention的调用", MultiHeadAttention) ----
+
+def _mha_torch(x, w_qkv, b_qkv, w_out, b_out, N, attend=None):
+    """The module's forward written with torch's float64 CPU primitives: linear layers,
+    chunk into thirds, per-head SDPA, heads merged, output linear layer."""
+    t = lambda a: None if a is None else torch.from_numpy(np.asarray(a, dtype=np.float64))
+    B, S, E = x.shape
+    q, k, v = torch.nn.functional.linear(t(x), t(w_qkv), t(b_qkv)).chunk(3, dim=-1)
+    q, k, v = (a.reshape(B, S, N, E // N).transpose(1, 2) for a in (q, k, v))
+    mask = None if attend is None else torch.from_numpy(attend)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    o = o.transpose(1, 2).reshape(B, S, E)
+    return torch.nn.functional.linear(o, t(w_out), t(b_out)).numpy()
+
+
+@pytest.mark.parametrize("B,S,E,N,bias", [(2, 9, 16, 2, True), (1, 5, 24, 3, False), (3, 4, 8, 1, True)])
+def test_mha_matches_torch_module(B, S, E, N, bias):
+    rng = np.random.default_rng(B * 100 + S)
+    x = rng.standard_normal((B, S, E))
+    w_qkv, w_out = rng.standard_normal((3 * E, E)) / 3, rng.standard_normal((E, E)) / 3
+    b_qkv = rng.standard_normal(3 * E) if bias else None
+    b_out = rng.standard_normal(E) if bias else None
+    got = oracle.mha_self_attn(x, w_qkv, b_qkv, w_out, b_out, N)
+    want = _mha_torch(x, w_qkv, b_qkv, w_out, b_out, N)
+    assert np.max(np.abs(got - want)) <= TOL
+
+
+def test_mha_with_mask_matches_torch_module():
+    rng = np.random.default_rng(7)
+    B, S, E, N = 2, 8, 16, 4
+    x = rng.standard_normal((B, S, E))
+    w_qkv, w_out = rng.standard_normal((3 * E, E)) / 3, rng.standard_normal((E, E)) / 3
+    b_qkv, b_out = rng.standard_normal(3 * E), rng.standard_normal(E)
+    keep = rng.random((S, S)) < 0.6
+    keep[np.arange(S), rng.integers(0, S, S)] = True   # every row keeps at least one key
+    got = oracle.mha_self_attn(x, w_qkv, b_qkv, w_out, b_out, N, keep=keep)
+    want = _mha_torch(x, w_qkv, b_qkv, w_out, b_out, N, attend=keep)
+    assert np.max(np.abs(got - want)) <= TOL
+
+
+def test_mha_brute_force_loops():
+    """B 1, S 3, E 4, N 2 by explicit loops over every index (no matrix library)."""
+    rng = np.random.default_rng(11)
+    S, E, N = 3, 4, 2
+    D = E // N
+    x = rng.standard_normal((1, S, E))
+    w_qkv, b_qkv = rng.standard_normal((3 * E, E)), rng.standard_normal(3 * E)
+    w_out, b_out = rng.standard_normal((E, E)), rng.standard_normal(E)
+    proj = [[b_qkv[f] + sum(x[0, s, c] * w_qkv[f, c] for c in range(E)) for f in range(3 * E)]
+            for s in range(S)]
+    o = [[0.0] * E for _ in range(S)]
+    for h in range(N):
+        for i in range(S):
+            sc = [sum(proj[i][h * D + d] * proj[j][E + h * D + d] for d in range(D)) / math.sqrt(D)
+                  for j in range(S)]
+            mx = max(sc)
+            ws = [math.exp(a - mx) for a in sc]
+            tot = sum(ws)
+            for d in range(D):
+                o[i][h * D + d] = sum(ws[j] * proj[j][2 * E + h * D + d] for j in range(S)) / tot
+    want = np.array([[b_out[f] + sum(o[s][c] * w_out[f, c] for c in range(E)) for f in range(E)]
+                     for s in range(S)])[None]
+    got = oracle.mha_self_attn(x, w_qkv, b_qkv, w_out, b_out, N)
+    assert np.max(np.abs(got - want)) <= TOL
