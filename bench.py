@@ -17,7 +17,9 @@ Also measured in the same run (reported under "secondary"):
   * causal attention over that workload's 4 key chunks of 2048 (a ring on one GPU): the
     fused attn_fwd_update chain vs attn_fwd + attn_lse_merge, and one full forward;
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, band 128 + 64 random), in
-    fp32 and in fp64 (same pattern and draws).
+    fp32 and in fp64 (same pattern and draws);
+  * the multi-head self-attention module (mha_self_attn_fwd) at its defaults, embed 512 and
+    8 heads, on B 8 x S 4096 bf16 in eval mode (projections + attention flops).
 
 measured_peaks: the dense bf16 MFMA rate of the chip and the bandwidth of a plain 2-read /
 1-write stream at the merge's size, from the peak probes (libmiattn_probes.so); each
@@ -417,6 +419,32 @@ def main():
             "tflops": round(dtf, 3),
             "roofline": {"bound": "alu", "achieved": round(dtf, 3), "peak": 78.6,
                          "unit": "TFLOP/s", "frac": round(dtf / 78.6, 4)}}
+
+        # the multi-head self-attention module at its defaults (embed 512, 8 heads), eval
+        # mode: two rocBLAS projections around the attention kernel
+        Bm, Sm, Em, Nm = 8, 4096, 512, 8
+        gm = torch.Generator(device=dev); gm.manual_seed(0)
+        mx = torch.randn((Bm, Sm, Em), device=dev, generator=gm).to(torch.bfloat16)
+        a_ = 1.0 / math.sqrt(Em)
+        mw = [(torch.rand(shape, device=dev, generator=gm) * 2 - 1).mul_(a_).to(torch.bfloat16)
+              for shape in ((3 * Em, Em), (3 * Em,), (Em, Em), (Em,))]
+        mo = torch.empty_like(mx)
+        mws_bytes = mi.mha_workspace_bytes(Bm, Sm, Em, "bf16")
+        mws = torch.empty(mws_bytes, dtype=torch.uint8, device=dev)
+        mflops = 8.0 * Bm * Sm * Em * Em + 4.0 * Bm * Sm * Sm * Em   # projections + attention
+
+        def step_mha():
+            mi.mha_self_attn_fwd(mx, mw[0], mw[1], mw[2], mw[3], mo, mws, mws_bytes, Bm, Sm, Em, Nm,
+                                 "bf16", stream=stream.cuda_stream)
+
+        mms = time_launches(step_mha, 10, 2, stream)
+        mtf = mflops / (mms * 1e-3) / 1e12
+        sec["mha_self_attn"] = {
+            "workload": "mha_self_attn_bf16_b8s4096_e512_h8", "ms_per_call": round(mms, 4),
+            "flop_per_call": mflops,
+            "roofline": {"bound": "mfma", "achieved": round(mtf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(mtf / PEAK_BF16_TFLOPS, 4)}}
+        del mx, mw, mo, mws
         result["secondary"] = sec
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------

@@ -66,7 +66,9 @@ typedef enum {
     MIATTN_ERR_UNSUPPORTED = 7, /* valid per the operator spec but not built (e.g. head_dim) */
     MIATTN_ERR_LAUNCH = 8,      /* the HIP launch failed */
     MIATTN_ERR_SCALE = 9,       /* scale is not a finite positive number */
-    MIATTN_ERR_DROPOUT = 10     /* dropout_p is not in [0, 1) (or rounds to 256/256) */
+    MIATTN_ERR_DROPOUT = 10,    /* dropout_p is not in [0, 1) (or rounds to 256/256) */
+    MIATTN_ERR_BLAS = 11,       /* a rocBLAS call (handle creation or GEMM) failed */
+    MIATTN_ERR_WORKSPACE = 12   /* the workspace is NULL or smaller than required */
 } miattn_status_t;
 
 /* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
@@ -281,6 +283,40 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
                                 const int32_t* csr_offset, const int32_t* csr_columns,
                                 int64_t nnz, int64_t B, int64_t N, int64_t S, int64_t D,
                                 miattn_dtype_t dtype, float scale, void* stream);
+
+/*
+ * mha_self_attn_fwd - forward of the multi-head self-attention module of the page "flash
+ * attention的调用" (its MultiHeadAttention example): a fused QKV projection, scaled dot-product
+ * attention per head with scale 1/sqrt(D), no causal mask, optional attention mask and
+ * dropout on the probabilities, and the output projection:
+ *     [q | k | v] = x W_qkv^T + b_qkv          (the 3E outputs split into thirds)
+ *     o_h         = attention(q_h, k_h, v_h)   (heads h = 0..N-1 of D = E/N columns each)
+ *     out         = [o_0 .. o_{N-1}] W_out^T + b_out
+ * The projections are rocBLAS GEMMs (fp32 accumulation, one rounding to the storage type:
+ * the output buffer is first filled with the broadcast bias and the GEMM runs with
+ * beta = 1); the attention is attn_fwd_ext on the BSND views of q, k, v.
+ *
+ *   x: DEVICE [B, S, E] contiguous;  out: DEVICE [B, S, E] contiguous (must not alias x);
+ *   w_qkv: DEVICE [3E, E] row-major (out_features x in_features, as a linear layer stores
+ *   it);  b_qkv: DEVICE [3E] or NULL (no bias);  w_out: DEVICE [E, E];  b_out: DEVICE [E] or
+ *   NULL.  All of the storage type `dtype`: MIATTN_BF16, MIATTN_F16 or MIATTN_F32.
+ *   workspace: DEVICE scratch of at least mha_workspace_bytes(B, S, E, dtype) bytes (q, k, v
+ *   and the attention output), owned by the caller; its contents are overwritten.
+ *   N divides E with D = E / N in {32, 64, 96, 128}; 1 <= N <= 256; B * S <= 2^31 - 1.
+ *   atten_mask: DEVICE uint8 [S, S] or NULL, nonzero = the pair is masked out (the
+ *   convention of attn_fwd_ext), with the same alignment rules as there.
+ *   dropout_p, seed, offset: as attn_fwd_ext (dropout is not combined with atten_mask).
+ * Errors are reported before any work is enqueued, except MIATTN_ERR_BLAS / _LAUNCH.  The
+ * first call on a device creates that device's rocBLAS handle (kept until the process ends).
+ */
+int64_t mha_workspace_bytes(int64_t B, int64_t S, int64_t E, miattn_dtype_t dtype);
+
+miattn_status_t mha_self_attn_fwd(const void* x, const void* w_qkv, const void* b_qkv,
+                                  const void* w_out, const void* b_out, void* out,
+                                  void* workspace, int64_t workspace_bytes,
+                                  int64_t B, int64_t S, int64_t E, int64_t N,
+                                  miattn_dtype_t dtype, const uint8_t* atten_mask,
+                                  float dropout_p, uint64_t seed, uint32_t offset, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* miattn_status_str(miattn_status_t status);

@@ -27,14 +27,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATTN_ERR_DTYPE",
           4: "MIATTN_ERR_LAYOUT", 5: "MIATTN_ERR_GQA_RATIO", 6: "MIATTN_ERR_MASK",
           7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE",
-          10: "MIATTN_ERR_DROPOUT"}
+          10: "MIATTN_ERR_DROPOUT", 11: "MIATTN_ERR_BLAS", 12: "MIATTN_ERR_WORKSPACE"}
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
            "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
-           "miattn_status_str")
+           "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -55,9 +55,12 @@ _lib.attn_fwd_varlen_ext.argtypes = ([_P] * 8 + [_I64] * 9 + [_E, _F, _E, _I64, 
                                      + [_F, _U64, _U32, _P])
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
+_lib.mha_workspace_bytes.argtypes = [_I64] * 3 + [_E]
+_lib.mha_workspace_bytes.restype = ctypes.c_int64
+_lib.mha_self_attn_fwd.argtypes = [_P] * 7 + [_I64] * 5 + [_E, _P, _F, _U64, _U32, _P]
 for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
            _lib.attn_fwd_ext, _lib.attn_fwd_varlen_ext, _lib.attn_lse_merge,
-           _lib.sparse_csr_attn):
+           _lib.sparse_csr_attn, _lib.mha_self_attn_fwd):
     _f.restype = ctypes.c_int
 _lib.miattn_status_str.argtypes = [ctypes.c_int]
 _lib.miattn_status_str.restype = ctypes.c_char_p
@@ -226,3 +229,21 @@ def sparse_csr_attn(q, k, v, out, csr_offset, csr_columns, nnz, B, N, S, D, dtyp
     _check(_lib.sparse_csr_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(csr_offset),
                                 _ptr(csr_columns), nnz, B, N, S, D, _enum(dtype, DTYPES),
                                 scale, _stream(stream)), "sparse_csr_attn")
+
+
+def mha_workspace_bytes(B, S, E, dtype) -> int:
+    n = _lib.mha_workspace_bytes(B, S, E, _enum(dtype, DTYPES))
+    if n < 0:
+        raise MiattnError(2, "mha_workspace_bytes")
+    return n
+
+
+def mha_self_attn_fwd(x, w_qkv, b_qkv, w_out, b_out, out, workspace, workspace_bytes, B, S, E,
+                      N, dtype, atten_mask=None, dropout_p=0.0, seed=0, offset=0, stream=None):
+    _check(_lib.mha_self_attn_fwd(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_out), _ptr(b_out),
+                                  _ptr(out), _ptr(workspace), workspace_bytes, B, S, E, N,
+                                  _enum(dtype, DTYPES), _ptr(atten_mask), dropout_p, seed,
+                                  offset, _stream(stream)), "mha_self_attn_fwd")
+
+
+from .mha import MultiHeadAttention  # noqa: E402  (the module form of mha_self_attn_fwd)

@@ -36,7 +36,7 @@ def _run(cmd, what: str, verbose: bool) -> None:
         raise RuntimeError(f"hipcc failed building {what}")
 
 
-def _hipcc(out: str, srcs, verbose: bool) -> None:
+def _hipcc(out: str, srcs, verbose: bool, libs=()) -> None:
     """Compile each source to an object in parallel, then link the shared library."""
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS]
@@ -48,7 +48,7 @@ def _hipcc(out: str, srcs, verbose: bool) -> None:
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
             for f in [pool.submit(_run, cmd, what, verbose) for cmd, what in jobs]:
                 f.result()
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs],
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs, *libs],
              os.path.basename(out), verbose)
     os.replace(out + ".tmp", out)
 
@@ -56,7 +56,8 @@ def _hipcc(out: str, srcs, verbose: bool) -> None:
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip into libmiattn.so, and the peak probes (a measurement aid
     of the benchmark) into libmiattn_probes.so.  Always recompiles."""
-    _hipcc(LIB, sources(), verbose)
+    # rocBLAS runs the two projections of the multi-head module (mha.hip)
+    _hipcc(LIB, sources(), verbose, libs=("-L/opt/rocm/lib", "-lrocblas"))
     _hipcc(PROBES_LIB, [PROBES_SRC], verbose)
     return LIB
 

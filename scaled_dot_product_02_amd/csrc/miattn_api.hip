@@ -132,6 +132,8 @@ const char* miattn_status_str(miattn_status_t s)
     case MIATTN_ERR_LAUNCH: return "kernel launch failed";
     case MIATTN_ERR_SCALE: return "scale must be finite and positive";
     case MIATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1) with round(256 p) < 256";
+    case MIATTN_ERR_BLAS: return "a rocBLAS call failed";
+    case MIATTN_ERR_WORKSPACE: return "workspace missing or smaller than mha_workspace_bytes()";
     }
     return "unknown status";
 }

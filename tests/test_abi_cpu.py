@@ -17,14 +17,14 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmiattn.so no
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, re.M)))
 
 
 def test_header_declares_every_entry_point():
     d = _declared()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
                  "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
-                 "miattn_status_str"):
+                 "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str"):
         assert name in d, d
 
 
@@ -251,8 +251,44 @@ def test_sparse_csr_attn_validation(mi):
     assert call(D=48) == "MIATTN_ERR_UNSUPPORTED"
 
 
+def test_mha_self_attn_fwd_validation(mi):
+    need = mi.mha_workspace_bytes(2, 16, 512, "bf16")
+    assert need == 4 * 2 * 16 * 512 * 2
+    assert mi.mha_workspace_bytes(2, 16, 512, "f32") == 2 * need
+    with pytest.raises(mi.MiattnError):
+        mi.mha_workspace_bytes(0, 16, 512, "bf16")
+    with pytest.raises(mi.MiattnError):
+        mi.mha_workspace_bytes(2, 16, 512, "f64")
+
+    def call(**kw):
+        a = dict(x=P, wq=P, bq=P, wo=P, bo=P, out=P, ws=P, wsb=need, B=2, S=16, E=512, N=8,
+                 dtype="bf16", mask=None, p=0.0)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.mha_self_attn_fwd(a["x"], a["wq"], a["bq"], a["wo"], a["bo"], a["out"], a["ws"],
+                                 a["wsb"], a["B"], a["S"], a["E"], a["N"], a["dtype"],
+                                 atten_mask=a["mask"], dropout_p=a["p"], stream=0)
+        return mi.STATUS[e.value.status]
+    assert call(x=None) == "MIATTN_ERR_NULL"
+    assert call(wq=None) == "MIATTN_ERR_NULL"
+    assert call(wo=None) == "MIATTN_ERR_NULL"
+    assert call(out=None) == "MIATTN_ERR_NULL"
+    assert call(dtype="f64") == "MIATTN_ERR_DTYPE"
+    assert call(B=0) == "MIATTN_ERR_SHAPE"
+    assert call(S=0) == "MIATTN_ERR_SHAPE"
+    assert call(N=7) == "MIATTN_ERR_SHAPE"          # 512 is not a multiple of 7
+    assert call(N=512) == "MIATTN_ERR_SHAPE"        # more than 256 heads
+    assert call(N=16, E=256) == "MIATTN_ERR_UNSUPPORTED"   # D = 16 is not built
+    assert call(ws=None) == "MIATTN_ERR_WORKSPACE"
+    assert call(wsb=need - 1) == "MIATTN_ERR_WORKSPACE"
+    assert call(out=P + 2) == "MIATTN_ERR_SHAPE"    # not 16-byte aligned
+    assert call(bq=P + 8) == "MIATTN_ERR_SHAPE"
+    assert call(p=1.0) == "MIATTN_ERR_DROPOUT"
+    assert call(p=0.1, mask=P) == "MIATTN_ERR_UNSUPPORTED"   # dropout with a mask tensor
+
+
 def test_status_strings(mi):
-    for code in range(10):
+    for code in range(13):
         assert mi.status_str(code) and mi.status_str(code) != "unknown status"
     assert mi.status_str(99) == "unknown status"
 
