@@ -18,6 +18,7 @@ Also measured in the same run (reported under "secondary"):
     fused attn_fwd_update chain vs attn_fwd + attn_lse_merge, and one full forward;
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, band 128 + 64 random), in
     fp32 and in fp64 (same pattern and draws);
+  * head dim 256: dense causal bf16, S 8192, N 16 (4-wave workgroups, 32-key tiles);
   * the multi-head self-attention module (mha_self_attn_fwd) at its defaults, embed 512 and
     8 heads, on B 8 x S 4096 bf16 in eval mode (projections + attention flops).
 
@@ -419,6 +420,27 @@ def main():
             "tflops": round(dtf, 3),
             "roofline": {"bound": "alu", "achieved": round(dtf, 3), "peak": 78.6,
                          "unit": "TFLOP/s", "frac": round(dtf / 78.6, 4)}}
+
+        # head dim 256 (4-wave workgroups, 32-key tiles): dense causal bf16, S 8192, N 16
+        Sd, Nd, Dd = 8192, 16, 256
+        gd = torch.Generator(device=dev); gd.manual_seed(0)
+        dq, dk, dv_ = (torch.randn((1, Nd, Sd, Dd), device=dev, generator=gd).to(torch.bfloat16)
+                       for _ in range(3))
+        do_ = torch.empty_like(dq)
+        dflops = 4.0 * Dd * Nd * (Sd * (Sd + 1) // 2)
+
+        def step_d256():
+            mi.attn_fwd(dq, dk, dv_, do_, None, None, 1, Nd, Nd, Sd, Sd, Dd, "bf16", "BNSD",
+                        1 / math.sqrt(Dd), "causal", stream=stream.cuda_stream)
+
+        d2ms = time_launches(step_d256, 10, 2, stream)
+        d2tf = dflops / (d2ms * 1e-3) / 1e12
+        sec["attn_fwd_head_dim_256"] = {
+            "workload": "dense_causal_bf16_b1n16s8192d256", "ms_per_launch": round(d2ms, 4),
+            "flop_per_launch": dflops,
+            "roofline": {"bound": "mfma", "achieved": round(d2tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(d2tf / PEAK_BF16_TFLOPS, 4)}}
+        del dq, dk, dv_, do_
 
         # the multi-head self-attention module at its defaults (embed 512, 8 heads), eval
         # mode: two rocBLAS projections around the attention kernel

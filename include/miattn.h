@@ -96,7 +96,9 @@ typedef enum {
  *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
  *   dtype: MIATTN_BF16 or MIATTN_F16 (MFMA path: fp32 accumulation, the softmax weights
  *   rounded to the input type for the P V product, RNE output) or MIATTN_F32.
- *   D: 32, 64, 96 or 128 (the operator spec allows 1..768; other values -> UNSUPPORTED).
+ *   D: 32, 64, 96 or 128 in every dtype; 160, 192, 224 or 256 in bf16 / fp16 (the entry
+ *   points below: with Dv = D, no mask tensor and no dropout).  The operator spec allows
+ *   1..768; other values -> UNSUPPORTED.
  *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
  *   Pass pre_tokens/next_tokens for the band modes; they are ignored otherwise.
@@ -124,7 +126,7 @@ miattn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out,
  *   cu_seqlens_q, cu_seqlens_kv: DEVICE int64 [B], monotone, last = Tq / Tkv;
  *   max_seqlen_q, max_seqlen_kv: host upper bounds of the sequence lengths (the grid is
  *   sized from max_seqlen_q; rows of a longer sequence are NOT computed).
- *   Ranges: 1 <= B <= 2048, 1 <= Tq, Tkv <= 2^20, 1 <= Nq, Nkv <= 256, D in {32, 64, 96, 128}.
+ *   Ranges: 1 <= B <= 2048, 1 <= Tq, Tkv <= 2^20, 1 <= Nq, Nkv <= 256, D as attn_fwd.
  *   dtype, scale, mask, pre/next: as for attn_fwd.
  */
 miattn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
@@ -302,7 +304,8 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
  *   NULL.  All of the storage type `dtype`: MIATTN_BF16, MIATTN_F16 or MIATTN_F32.
  *   workspace: DEVICE scratch of at least mha_workspace_bytes(B, S, E, dtype) bytes (q, k, v
  *   and the attention output), owned by the caller; its contents are overwritten.
- *   N divides E with D = E / N in {32, 64, 96, 128}; 1 <= N <= 256; B * S <= 2^31 - 1.
+ *   N divides E with D = E / N in {32, 64, 96, 128} (and 160..256 as attn_fwd, without a
+ *   mask or dropout); 1 <= N <= 256; B * S <= 2^31 - 1.
  *   atten_mask: DEVICE uint8 [S, S] or NULL, nonzero = the pair is masked out (the
  *   convention of attn_fwd_ext), with the same alignment rules as there.
  *   dropout_p, seed, offset: as attn_fwd_ext (dropout is not combined with atten_mask).

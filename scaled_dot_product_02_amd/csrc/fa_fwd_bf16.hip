@@ -93,15 +93,26 @@ template <> struct Elem<_Float16> {
 };
 
 // D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
+// Head dims up to 128 run 8 waves (two per SIMD) on 64-key tiles.  Larger ones (160..256)
+// run 4 waves, one per SIMD, so that a wave may hold up to 512 registers (the O
+// accumulators of D 256 alone take 128), on 32-key tiles so that the 4-deep K and V^T
+// rings fit in LDS (about 146 KB at D 256).
 template <int D, int DV>
 struct Cfg {
+    static constexpr bool BIG = D > 128;
+    static constexpr int NW = BIG ? 4 : 8;            // waves per workgroup
+    static constexpr int NT = 64 * NW;                // threads per workgroup
+    static constexpr int BM = 32 * NW;                // query rows per workgroup
+    static constexpr int BN = BIG ? 32 : ::miattn::BN; // keys per tile
+    static constexpr int NKB = BN / 32;               // 32-key blocks per tile
     static constexpr int KS = D + 8;                  // K row stride in LDS (bf16)
     static constexpr int VS = BN + 8;                 // V^T row stride in LDS (bf16)
     static constexpr int CPR = D / 8;                 // 16-byte chunks per K row
     static constexpr int KCH = BN * CPR;              // K chunks per tile
     static constexpr int KPT = (KCH + NT - 1) / NT;   // K chunks per thread (some repeat)
     static constexpr int VUNITS = (BN / 2) * (DV / 8); // V units (2 keys x 8 dims) per tile
-    static constexpr int SREG = KPT + 2;              // staging registers (16 B each)
+    static constexpr int VPT = (VUNITS + NT - 1) / NT; // V units per thread (some repeat)
+    static constexpr int SREG = KPT + 2 * VPT;        // staging registers (16 B each)
     static constexpr int KK = D / 16;                 // MFMA k-steps over the Q/K head dim
     static constexpr int RT = DV / 32;                // 32-row output tiles over the V head dim
     static constexpr int KBUF = BN * KS;
@@ -147,9 +158,11 @@ __device__ inline unsigned pack_mask(const unsigned (&w)[8])
 // masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
 // DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
 template <int D, int DV, typename T, bool UPDATE, bool MASKED, bool DROP = false>
-__global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
+__global__ __launch_bounds__((Cfg<D, DV>::NT)) void fa_fwd_bf16_kernel(FaParams p)
 {
     using C = Cfg<D, DV>;
+    constexpr int NT = C::NT, BM = C::BM, BN = C::BN, NKB = C::NKB;
+    static_assert(!(C::BIG && (MASKED || DROP)), "the mask tensor and dropout assume 64-key tiles");
     constexpr int PF = MASKED ? 2 : ::miattn::PF;
     constexpr int LDSD = MASKED ? 3 : ::miattn::LDSD;
     using X8 = typename Elem<T>::v8;   // one MFMA operand: 8 elements
@@ -250,17 +263,24 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     //      inside a tile is a constant.  With fewer V units than threads, threads repeat a
     //      unit and store identical values.
     u32x4 stA[C::SREG], stB[C::SREG];
-    const int vu = tid % C::VUNITS;
-    const int kp = vu % (BN / 2), vc = vu / (BN / 2);
+    int kp[C::VPT], vc[C::VPT];   // V unit u of this thread: keys 2 kp, 2 kp + 1, dims 8 vc ..
+    #pragma unroll
+    for (int u = 0; u < C::VPT; ++u) {
+        const int vu = (tid + NT * u) % C::VUNITS;
+        kp[u] = vu % (BN / 2);
+        vc[u] = vu / (BN / 2);
+    }
     const int64_t krb = 2 * p.k_ss, vrb = 2 * p.v_ss;   // row strides in bytes
-    uint32_t koff[C::KPT], voff[2];
+    uint32_t koff[C::KPT], voff[2 * C::VPT];
     #pragma unroll
     for (int u = 0; u < C::KPT; ++u) {
         const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
         koff[u] = (uint32_t)((c / C::CPR) * krb + 16 * (c % C::CPR));
     }
     #pragma unroll
-    for (int r = 0; r < 2; ++r) voff[r] = (uint32_t)((2 * kp + r) * vrb + 16 * vc);
+    for (int u = 0; u < C::VPT; ++u)
+        #pragma unroll
+        for (int r = 0; r < 2; ++r) voff[2 * u + r] = (uint32_t)((2 * kp[u] + r) * vrb + 16 * vc[u]);
 
     // descriptor inputs are workgroup-uniform; readfirstlane keeps them in scalar registers
     // (a descriptor the compiler thinks divergent would be looped over lane by lane)
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) stage[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0);
         #pragma unroll
-        for (int r = 0; r < 2; ++r) stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
+        for (int r = 0; r < 2 * C::VPT; ++r) stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
     };
     auto store_tile = [&](int t, const u32x4 (&stage)[C::SREG]) {
         const int bf = t & (NBUF - 1);
@@ -304,14 +324,17 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
             *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
         }
         // dims 8 vc + e of keys 2 kp, 2 kp + 1 -> one 32-bit word of V^T row 8 vc + e
-        __bf16* vb = Vt + bf * C::VBUF + 8 * vc * C::VS + vt_pos(2 * kp);
-        const u32x4 x0 = stage[C::KPT], x1 = stage[C::KPT + 1];
         #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // low halves (even e) or high halves (odd e) of the two keys' words: v_perm_b32
-            // takes bytes 0-3 from its second operand and 4-7 from its first
-            const unsigned w = __builtin_amdgcn_perm(x1[e >> 1], x0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-            *(unsigned*)(vb + e * C::VS) = w;
+        for (int u = 0; u < C::VPT; ++u) {
+            __bf16* vb = Vt + bf * C::VBUF + 8 * vc[u] * C::VS + vt_pos(2 * kp[u]);
+            const u32x4 x0 = stage[C::KPT + 2 * u], x1 = stage[C::KPT + 2 * u + 1];
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // low halves (even e) or high halves (odd e) of the two keys' words:
+                // v_perm_b32 takes bytes 0-3 from its second operand and 4-7 from its first
+                const unsigned w = __builtin_amdgcn_perm(x1[e >> 1], x0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+                *(unsigned*)(vb + e * C::VS) = w;
+            }
         }
     };
 
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     // finished one barrier earlier.
     X8 pp[2 * NKB];
     f32x16 sa[NKB];
-    const bool late = wave >= 4;
+    const bool late = C::NW == 8 && wave >= 4;   // one wave per SIMD: no partner to skew against
     auto step = [&](int t, u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
         if constexpr (MASKED) {
             mbits = pack_mask(mw);             // mask of tile t, read one step earlier
@@ -582,16 +605,31 @@ __global__ __launch_bounds__(NT) void fa_fwd_bf16_kernel(FaParams p)
     }
 }
 
+template <int D, typename T, bool UPDATE, bool MASKED>
+void launch_d(const FaParams& p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, D, T, UPDATE, MASKED>), dim3(p.n_slots),
+                       dim3(Cfg<D, D>::NT), 0, stream, p);
+}
+
 template <typename T, bool UPDATE, bool MASKED>
 hipError_t launch_t(const FaParams& p, int D, hipStream_t stream)
 {
-    dim3 grid(p.n_slots), block(NT);
     switch (D) {
-    case 32: hipLaunchKernelGGL((fa_fwd_bf16_kernel<32, 32, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 64, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, 96, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 128, T, UPDATE, MASKED>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+    case 32: launch_d<32, T, UPDATE, MASKED>(p, stream); break;
+    case 64: launch_d<64, T, UPDATE, MASKED>(p, stream); break;
+    case 96: launch_d<96, T, UPDATE, MASKED>(p, stream); break;
+    case 128: launch_d<128, T, UPDATE, MASKED>(p, stream); break;
+    default:
+        // head dims above 128 (4-wave workgroups, 32-key tiles): no mask tensor
+        if constexpr (MASKED) return hipErrorInvalidValue;
+        else switch (D) {
+            case 160: launch_d<160, T, UPDATE, false>(p, stream); break;
+            case 192: launch_d<192, T, UPDATE, false>(p, stream); break;
+            case 224: launch_d<224, T, UPDATE, false>(p, stream); break;
+            case 256: launch_d<256, T, UPDATE, false>(p, stream); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }

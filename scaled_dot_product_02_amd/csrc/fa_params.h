@@ -87,6 +87,7 @@ hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t
 
 // Row tile heights, used by the C-ABI layer to size the grids.
 constexpr int kBf16TileM = 256;
+constexpr int kBf16TileMBig = 128;   // the MFMA kernel at head dims above 128 (4 waves)
 constexpr int kF32TileM = 64;
 
 }  // namespace miattn

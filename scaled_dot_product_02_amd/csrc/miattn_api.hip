@@ -53,6 +53,10 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 // head dims with a built attention kernel (every dtype)
 bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
+// larger head dims, built for the MFMA kernel only: bf16 / fp16, V head dim equal, no mask
+// tensor and no dropout
+bool big_head_dim(int64_t D) { return D == 160 || D == 192 || D == 224 || D == 256; }
+
 // Dropout probability p -> byte threshold round(256 p) and the scale of kept probabilities;
 // p must be finite in [0, 1) with threshold < 256.  Threshold 0 is no dropout.
 miattn_status_t set_dropout(FaParams& p, float prob, uint64_t seed, uint32_t offset)
@@ -73,6 +77,7 @@ miattn_status_t set_dropout(FaParams& p, float prob, uint64_t seed, uint32_t off
 miattn_status_t check_head_dims(int64_t D, int64_t Dv, bool update, bool amask)
 {
     if (Dv < 1 || Dv > D) return MIATTN_ERR_SHAPE;   // the varlen operator: kD >= vD
+    if (big_head_dim(D)) return Dv == D && !amask ? MIATTN_OK : MIATTN_ERR_UNSUPPORTED;
     if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
     if (Dv == D) return MIATTN_OK;
     const bool pair = (D == 64 && Dv == 32) || (D == 96 && Dv == 64) || (D == 128 && Dv == 64) ||
@@ -106,7 +111,7 @@ miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream,
     const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
     const bool mfma = (dtype == MIATTN_BF16 || dtype == MIATTN_F16) && mask_words;
-    const int tile_m = mfma ? kBf16TileM : kF32TileM;
+    const int tile_m = mfma ? (D > 128 ? kBf16TileMBig : kBf16TileM) : kF32TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
     hipError_t e = mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
@@ -175,6 +180,7 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     p.amask = atten_mask;
     p.amask_ld = Skv;
     if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
+    if (big_head_dim(D) && (dtype == MIATTN_F32 || p.drop_thr)) return MIATTN_ERR_UNSUPPORTED;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     const Strides so = strides_of(layout, B, Nq, Sq, Dv), sv = strides_of(layout, B, Nkv, Skv, Dv);
@@ -231,6 +237,7 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     p.amask = atten_mask;
     p.amask_ld = max_seqlen_kv;
     if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
+    if (big_head_dim(D) && (dtype == MIATTN_F32 || p.drop_thr)) return MIATTN_ERR_UNSUPPORTED;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;

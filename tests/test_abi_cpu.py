@@ -99,6 +99,9 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, scale=float("inf")) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, D=80) == "MIATTN_ERR_UNSUPPORTED"           # in spec, not built (32/64/96/128 are)
     assert _fwd(mi, D=1) == "MIATTN_ERR_UNSUPPORTED"
+    assert _fwd(mi, D=288) == "MIATTN_ERR_UNSUPPORTED"
+    assert _fwd(mi, D=160, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"   # 160..256: bf16 / fp16 only
+    assert _fwd(mi, D=256, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"
 
 
 def _varlen(mi, **kw):
@@ -146,7 +149,7 @@ def test_attn_fwd_update_validation(mi):
     assert call(Nq=5) == "MIATTN_ERR_GQA_RATIO"
     assert call(pre=3, nxt=-4) == "MIATTN_ERR_MASK"
     assert call(scale=float("nan")) == "MIATTN_ERR_SCALE"
-    assert call(D=160) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=288) == "MIATTN_ERR_UNSUPPORTED"
 
 
 def test_attn_fwd_varlen_update_validation(mi):
@@ -186,6 +189,9 @@ def test_attn_fwd_ext_validation(mi):
     assert call(D=64, Dv=96) == "MIATTN_ERR_SHAPE"               # kD >= vD
     assert call(D=64, Dv=48) == "MIATTN_ERR_UNSUPPORTED"         # pair not built
     assert call(D=128, Dv=64, am=P) == "MIATTN_ERR_UNSUPPORTED"  # Dv < D without a mask tensor
+    # head dims 160..256: V head dim equal, no mask tensor, no dropout
+    assert call(D=256, Dv=128) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=192, Dv=192, am=P) == "MIATTN_ERR_UNSUPPORTED"
 
     def dcall(p, **kw):
         with pytest.raises(mi.MiattnError) as e:
@@ -199,6 +205,7 @@ def test_attn_fwd_ext_validation(mi):
     assert dcall(0.999) == "MIATTN_ERR_DROPOUT"                   # rounds to 256/256
     assert dcall(0.5, am=P) == "MIATTN_ERR_UNSUPPORTED"
     assert dcall(0.5, D=128, Dv=64) == "MIATTN_ERR_UNSUPPORTED"
+    assert dcall(0.5, D=224, Dv=224) == "MIATTN_ERR_UNSUPPORTED"
 
     def vcall(**kw):
         a = dict(mask="causal", prefix=P, D=128, Dv=128)
@@ -279,6 +286,8 @@ def test_mha_self_attn_fwd_validation(mi):
     assert call(N=7) == "MIATTN_ERR_SHAPE"          # 512 is not a multiple of 7
     assert call(N=512) == "MIATTN_ERR_SHAPE"        # more than 256 heads
     assert call(N=16, E=256) == "MIATTN_ERR_UNSUPPORTED"   # D = 16 is not built
+    assert call(N=2, E=512, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"   # D 256: bf16 / fp16 only
+    assert call(N=2, E=512, p=0.1) == "MIATTN_ERR_UNSUPPORTED"        # D 256: no dropout
     assert call(ws=None) == "MIATTN_ERR_WORKSPACE"
     assert call(wsb=need - 1) == "MIATTN_ERR_WORKSPACE"
     assert call(out=P + 2) == "MIATTN_ERR_SHAPE"    # not 16-byte aligned
