@@ -97,9 +97,9 @@ template <> struct Elem<_Float16> {
 // run 4 waves, one per SIMD, so that a wave may hold up to 512 registers (the O
 // accumulators of D 256 alone take 128), on 32-key tiles so that the 4-deep K and V^T
 // rings fit in LDS (about 146 KB at D 256).
-template <int D, int DV>
+template <int D, int DV, bool FOUR = (D > 128)>
 struct Cfg {
-    static constexpr bool BIG = D > 128;
+    static constexpr bool BIG = FOUR;
     static constexpr int NW = BIG ? 4 : 8;            // waves per workgroup
     static constexpr int NT = 64 * NW;                // threads per workgroup
     static constexpr int BM = 32 * NW;                // query rows per workgroup
@@ -157,10 +157,14 @@ __device__ inline unsigned pack_mask(const unsigned (&w)[8])
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
 // masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
 // DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
+template <int D, int DV, bool MASKED, bool DROP>
+using KCfg = Cfg<D, DV, fa_four_waves(D, MASKED || DROP)>;
+
 template <int D, int DV, typename T, bool UPDATE, bool MASKED, bool DROP = false>
-__global__ __launch_bounds__((Cfg<D, DV>::NT)) void fa_fwd_bf16_kernel(FaParams p)
+__global__ __launch_bounds__((KCfg<D, DV, MASKED, DROP>::NT), (KCfg<D, DV, MASKED, DROP>::BIG && D <= 128 ? 2 : 1))
+void fa_fwd_bf16_kernel(FaParams p)
 {
-    using C = Cfg<D, DV>;
+    using C = KCfg<D, DV, MASKED, DROP>;
     constexpr int NT = C::NT, BM = C::BM, BN = C::BN, NKB = C::NKB;
     static_assert(!(C::BIG && (MASKED || DROP)), "the mask tensor and dropout assume 64-key tiles");
     constexpr int PF = MASKED ? 2 : ::miattn::PF;
@@ -609,7 +613,7 @@ template <int D, typename T, bool UPDATE, bool MASKED>
 void launch_d(const FaParams& p, hipStream_t stream)
 {
     hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, D, T, UPDATE, MASKED>), dim3(p.n_slots),
-                       dim3(Cfg<D, D>::NT), 0, stream, p);
+                       dim3(KCfg<D, D, MASKED, false>::NT), 0, stream, p);
 }
 
 template <typename T, bool UPDATE, bool MASKED>
@@ -650,20 +654,21 @@ hipError_t launch_drop(const FaParams& p, int D, hipStream_t stream)
 }
 
 // value head dim below the Q/K head dim (plain forward only)
+template <int D, int DV, typename T>
+void launch_dv_pair(const FaParams& p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, DV, T, false, false>), dim3(p.n_slots),
+                       dim3(KCfg<D, DV, false, false>::NT), 0, stream, p);
+}
+
 template <typename T>
 hipError_t launch_dv(const FaParams& p, int D, int Dv, hipStream_t stream)
 {
-    dim3 grid(p.n_slots), block(NT);
-    if (D == 64 && Dv == 32)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 32, T, false, false>), grid, block, 0, stream, p);
-    else if (D == 96 && Dv == 64)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<96, 64, T, false, false>), grid, block, 0, stream, p);
-    else if (D == 128 && Dv == 64)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 64, T, false, false>), grid, block, 0, stream, p);
-    else if (D == 128 && Dv == 96)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 96, T, false, false>), grid, block, 0, stream, p);
-    else
-        return hipErrorInvalidValue;
+    if (D == 64 && Dv == 32) launch_dv_pair<64, 32, T>(p, stream);
+    else if (D == 96 && Dv == 64) launch_dv_pair<96, 64, T>(p, stream);
+    else if (D == 128 && Dv == 64) launch_dv_pair<128, 64, T>(p, stream);
+    else if (D == 128 && Dv == 96) launch_dv_pair<128, 96, T>(p, stream);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

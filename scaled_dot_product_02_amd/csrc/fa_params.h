@@ -87,7 +87,18 @@ hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t
 
 // Row tile heights, used by the C-ABI layer to size the grids.
 constexpr int kBf16TileM = 256;
-constexpr int kBf16TileMBig = 128;   // the MFMA kernel at head dims above 128 (4 waves)
+constexpr int kBf16TileMBig = 128;   // the MFMA kernel's 4-wave configuration
+
+#ifndef FA_FOUR_WAVE_MIN_D
+#define FA_FOUR_WAVE_MIN_D 129
+#endif
+// Whether the MFMA kernel runs its 4-wave, 32-key-tile configuration (128-row tiles) for
+// head dim D: always above 128; from FA_FOUR_WAVE_MIN_D up for the plain and update
+// instances (the mask-tensor and dropout instances assume 64-key tiles).
+constexpr bool fa_four_waves(int D, bool mask_or_dropout)
+{
+    return D > 128 || (!mask_or_dropout && D >= FA_FOUR_WAVE_MIN_D);
+}
 constexpr int kF32TileM = 64;
 
 }  // namespace miattn

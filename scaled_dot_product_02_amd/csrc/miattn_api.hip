@@ -111,7 +111,8 @@ miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream,
     const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
     const bool mfma = (dtype == MIATTN_BF16 || dtype == MIATTN_F16) && mask_words;
-    const int tile_m = mfma ? (D > 128 ? kBf16TileMBig : kBf16TileM) : kF32TileM;
+    const int tile_m = !mfma ? kF32TileM
+                     : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
     hipError_t e = mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
