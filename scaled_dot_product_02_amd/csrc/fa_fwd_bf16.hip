@@ -136,23 +136,6 @@ __device__ inline float pair_sum(float x)
 // the key order of the P operand taken from the S^T accumulator layout.
 __device__ inline int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// Packs the 8 mask words of one lane and tile (bytes for keys 32b + 8g + 4hf + e, word
-// 4b + g, byte e) into bit 16b + 4g + e: set where the byte is nonzero (masked out).
-__device__ inline unsigned pack_mask(const unsigned (&w)[8])
-{
-    unsigned bits = 0;
-    #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        unsigned x = w[k];
-        x |= x >> 4;
-        x |= x >> 2;
-        x |= x >> 1;                                        // bit 8e: byte e nonzero
-        x &= 0x01010101u;
-        bits |= ((x * 0x01020408u) >> 24 & 0xfu) << (4 * k);  // bit 8e -> bit 24 + e
-    }
-    return bits;
-}
-
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
 // masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
@@ -295,9 +278,10 @@ void fa_fwd_bf16_kernel(FaParams p)
         const int n = __builtin_amdgcn_readfirstlane((int)bytes);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
     };
-    // explicit mask: this lane's row, words of one tile in flight, bits of the current one
+    // explicit mask: this lane's row; the 8 words of the next tile in flight and those of
+    // the current tile (byte e of word 4b + g: key 32b + 8g + 4hf + e of the tile)
     unsigned mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    unsigned mbits = 0;
+    unsigned mcur[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t rmask;
     uint32_t moff = 0;
     if constexpr (MASKED) {
@@ -401,11 +385,12 @@ void fa_fwd_bf16_kernel(FaParams p)
     auto softmax = [&](int t, f32x16 (&s)[NKB], X8 (&pp)[2 * NKB]) {
         const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
         if constexpr (MASKED) {
+            // element i of block b: byte i % 4 of word 4b + i / 4 (one byte-select compare each)
             #pragma unroll
             for (int b = 0; b < NKB; ++b)
                 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if ((mbits >> (16 * b + i)) & 1u) s[b][i] = -INFINITY;
+                    if ((mcur[4 * b + (i >> 2)] >> (8 * (i & 3)) & 0xffu) != 0u) s[b][i] = -INFINITY;
         }
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
@@ -516,7 +501,8 @@ void fa_fwd_bf16_kernel(FaParams p)
     const bool late = C::NW == 8 && wave >= 4;   // one wave per SIMD: no partner to skew against
     auto step = [&](int t, u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
         if constexpr (MASKED) {
-            mbits = pack_mask(mw);             // mask of tile t, read one step earlier
+            #pragma unroll
+            for (int k = 0; k < 8; ++k) mcur[k] = mw[k];   // mask of tile t, read one step earlier
             if (t + 1 < T1) load_mask(t + 1);
         }
         __builtin_amdgcn_s_setprio(3);
