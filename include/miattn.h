@@ -96,9 +96,12 @@ typedef enum {
  *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
  *   dtype: MIATTN_BF16 or MIATTN_F16 (MFMA path: fp32 accumulation, the softmax weights
  *   rounded to the input type for the P V product, RNE output) or MIATTN_F32.
- *   D: 32, 64, 96 or 128 in every dtype; 160, 192, 224 or 256 in bf16 / fp16 (the entry
- *   points below: with Dv = D, no mask tensor and no dropout).  The operator spec allows
- *   1..768; other values -> UNSUPPORTED.
+ *   D: any of 1..768, the operator spec's range (aclnnFlashAttentionVarLenScore 约束说明),
+ *   in every dtype; outside it -> MIATTN_ERR_SHAPE.  The tiled kernels serve 32, 64, 96
+ *   and 128 (and 160, 192, 224, 256 in bf16 / fp16 without a mask tensor or dropout);
+ *   every other head dim and combination runs on a head-dim-general MFMA kernel (the head
+ *   dim split over the waves of a workgroup, partial scores summed in LDS), same results
+ *   to rounding, slower.
  *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
  *   Pass pre_tokens/next_tokens for the band modes; they are ignored otherwise.
@@ -234,8 +237,7 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
  *   arguments, limits and errors as attn_fwd / attn_fwd_varlen.
  *   Dv: head dim of v and out (aclnnFlashAttentionVarLenScore 约束说明: qD == kD >= vD);
  *     v is [B, Nkv, Skv, Dv] / [Tkv, Nkv, Dv] and out [B, Nq, Sq, Dv] / [Tq, Nq, Dv] in the
- *     same layout.  Dv = D always; Dv < D for (D, Dv) in {(64, 32), (96, 64), (128, 64),
- *     (128, 96)} without atten_mask (else MIATTN_ERR_UNSUPPORTED); Dv > D -> MIATTN_ERR_SHAPE.
+ *     same layout.  Any 1 <= Dv <= D (else MIATTN_ERR_SHAPE).
  *   dropout_p, seed, offset: dropout on the probabilities (the dropout_p of the
  *     MultiHeadAttention page and the SDPA-pitfalls blog); the pages name no generator, so
  *     it is defined here: probability (i, j) of query head h in batch entry / sequence b is
@@ -304,8 +306,8 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
  *   NULL.  All of the storage type `dtype`: MIATTN_BF16, MIATTN_F16 or MIATTN_F32.
  *   workspace: DEVICE scratch of at least mha_workspace_bytes(B, S, E, dtype) bytes (q, k, v
  *   and the attention output), owned by the caller; its contents are overwritten.
- *   N divides E with D = E / N in {32, 64, 96, 128} (and 160..256 as attn_fwd, without a
- *   mask or dropout); 1 <= N <= 256; B * S <= 2^31 - 1.
+ *   N divides E with D = E / N <= 768; rows of E elements are whole 16-byte vectors (E a
+ *   multiple of 8 for bf16 / fp16, of 4 for fp32); 1 <= N <= 256; B * S <= 2^31 - 1.
  *   atten_mask: DEVICE uint8 [S, S] or NULL, nonzero = the pair is masked out (the
  *   convention of attn_fwd_ext), with the same alignment rules as there.
  *   dropout_p, seed, offset: as attn_fwd_ext (dropout is not combined with atten_mask).

@@ -104,9 +104,8 @@ miattn_status_t mha_self_attn_fwd(const void* x, const void* w_qkv, const void* 
         E > 32768)
         return MIATTN_ERR_SHAPE;
     const int64_t D = E / N;
-    const bool big = D == 160 || D == 192 || D == 224 || D == 256;   // attention kernel limits
-    if (D != 32 && D != 64 && D != 96 && D != 128 && !big) return MIATTN_ERR_UNSUPPORTED;
-    if (big && (dtype == MIATTN_F32 || atten_mask || dropout_p > 0.f)) return MIATTN_ERR_UNSUPPORTED;
+    // head dims of the attention operator; rows of whole 16-byte vectors for the bias fill
+    if (D > 768 || (E * eb) % 16 != 0) return MIATTN_ERR_SHAPE;
     const int64_t need = mha_workspace_bytes(B, S, E, dtype);
     if (!workspace || need < 0 || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
     if (!aligned16(workspace) || !aligned16(out) || (b_qkv && !aligned16(b_qkv)) ||

@@ -50,12 +50,25 @@ miattn_status_t check_mask(int mask, int64_t pre, int64_t next, FaParams& p)
 
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-// head dims with a built attention kernel (every dtype)
+// head dims of the tiled kernels in every dtype (the sparse kernel: these only)
 bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 
-// larger head dims, built for the MFMA kernel only: bf16 / fp16, V head dim equal, no mask
-// tensor and no dropout
+// larger head dims of the tiled MFMA kernel: bf16 / fp16, V head dim equal, no mask tensor
+// and no dropout
 bool big_head_dim(int64_t D) { return D == 160 || D == 192 || D == 224 || D == 256; }
+
+// Whether one of the tiled kernels serves this forward; every other valid one runs on the
+// head-dim-general kernel.
+bool tiled_forward(int64_t D, int64_t Dv, int dtype, bool update, bool amask, bool drop)
+{
+    if (head_dim_built(D)) {
+        if (Dv == D) return true;
+        const bool pair = (D == 64 && Dv == 32) || (D == 96 && Dv == 64) || (D == 128 && Dv == 64) ||
+                          (D == 128 && Dv == 96);
+        return pair && !update && !amask && !drop;
+    }
+    return big_head_dim(D) && Dv == D && dtype != MIATTN_F32 && !amask && !drop;
+}
 
 // Dropout probability p -> byte threshold round(256 p) and the scale of kept probabilities;
 // p must be finite in [0, 1) with threshold < 256.  Threshold 0 is no dropout.
@@ -72,17 +85,10 @@ miattn_status_t set_dropout(FaParams& p, float prob, uint64_t seed, uint32_t off
     return MIATTN_OK;
 }
 
-// (Q/K head dim, V head dim) pairs with a built kernel; a smaller V head dim only for the
-// plain forward (no fused update, no mask tensor)
-miattn_status_t check_head_dims(int64_t D, int64_t Dv, bool update, bool amask)
+// V head dim: 1..D (the varlen operator: kD >= vD); D itself is checked against 1..768
+miattn_status_t check_head_dims(int64_t D, int64_t Dv)
 {
-    if (Dv < 1 || Dv > D) return MIATTN_ERR_SHAPE;   // the varlen operator: kD >= vD
-    if (big_head_dim(D)) return Dv == D && !amask ? MIATTN_OK : MIATTN_ERR_UNSUPPORTED;
-    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
-    if (Dv == D) return MIATTN_OK;
-    const bool pair = (D == 64 && Dv == 32) || (D == 96 && Dv == 64) || (D == 128 && Dv == 64) ||
-                      (D == 128 && Dv == 96);
-    return pair && !update && !amask ? MIATTN_OK : MIATTN_ERR_UNSUPPORTED;
+    return Dv < 1 || Dv > D ? MIATTN_ERR_SHAPE : MIATTN_OK;
 }
 
 miattn_status_t check_dtype_fa(int dtype)
@@ -111,11 +117,14 @@ miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream,
     const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
     const bool mfma = (dtype == MIATTN_BF16 || dtype == MIATTN_F16) && mask_words;
-    const int tile_m = !mfma ? kF32TileM
+    const bool tiled = tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr, p.amask != nullptr, p.drop_thr != 0);
+    const int tile_m = !tiled ? fa_wide_tile_m(dtype, p.Dv)
+                     : !mfma ? kF32TileM
                      : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
-    hipError_t e = mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
+    hipError_t e = !tiled ? launch_fa_fwd_wide(p, (int)D, dtype, stream)
+                 : mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
                         : launch_fa_fwd_f32(p, (int)D, dtype, stream);
     return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
@@ -172,7 +181,7 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
         return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
+    st = check_head_dims(D, Dv);
     if (st != MIATTN_OK) return st;
     p.Dv = (int32_t)Dv;
     st = set_dropout(p, dropout_p, seed, offset);
@@ -181,7 +190,6 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     p.amask = atten_mask;
     p.amask_ld = Skv;
     if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
-    if (big_head_dim(D) && (dtype == MIATTN_F32 || p.drop_thr)) return MIATTN_ERR_UNSUPPORTED;
 
     const Strides sq = strides_of(layout, B, Nq, Sq, D), skv = strides_of(layout, B, Nkv, Skv, D);
     const Strides so = strides_of(layout, B, Nq, Sq, Dv), sv = strides_of(layout, B, Nkv, Skv, Dv);
@@ -229,7 +237,7 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
         return MIATTN_ERR_MASK;   // a prefix goes with the causal modes only
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    st = check_head_dims(D, Dv, prev_out != nullptr, atten_mask != nullptr);
+    st = check_head_dims(D, Dv);
     if (st != MIATTN_OK) return st;
     p.Dv = (int32_t)Dv;
     st = set_dropout(p, dropout_p, seed, offset);
@@ -238,7 +246,6 @@ miattn_status_t fwd_varlen(const void* q, const void* k, const void* v,
     p.amask = atten_mask;
     p.amask_ld = max_seqlen_kv;
     if (p.drop_thr && (prev_out || atten_mask || Dv != D)) return MIATTN_ERR_UNSUPPORTED;
-    if (big_head_dim(D) && (dtype == MIATTN_F32 || p.drop_thr)) return MIATTN_ERR_UNSUPPORTED;
 
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.smax = softmax_max; p.ssum = softmax_sum;

@@ -81,7 +81,6 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, out=None) == "MIATTN_ERR_NULL"
     assert _fwd(mi, dtype=9) == "MIATTN_ERR_DTYPE"
     assert _fwd(mi, dtype="f64") == "MIATTN_ERR_DTYPE"          # fp64 is the sparse op's only
-    assert _fwd(mi, dtype="f16", D=80) == "MIATTN_ERR_UNSUPPORTED"   # fp16 takes the bf16 head dims
     assert _fwd(mi, layout=7) == "MIATTN_ERR_LAYOUT"
     assert _fwd(mi, B=0) == "MIATTN_ERR_SHAPE"
     assert _fwd(mi, Sq=0) == "MIATTN_ERR_SHAPE"
@@ -97,11 +96,7 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, scale=-0.1) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, scale=float("nan")) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, scale=float("inf")) == "MIATTN_ERR_SCALE"
-    assert _fwd(mi, D=80) == "MIATTN_ERR_UNSUPPORTED"           # in spec, not built (32/64/96/128 are)
-    assert _fwd(mi, D=1) == "MIATTN_ERR_UNSUPPORTED"
-    assert _fwd(mi, D=288) == "MIATTN_ERR_UNSUPPORTED"
-    assert _fwd(mi, D=160, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"   # 160..256: bf16 / fp16 only
-    assert _fwd(mi, D=256, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"
+    assert _fwd(mi, D=0) == "MIATTN_ERR_SHAPE"
 
 
 def _varlen(mi, **kw):
@@ -127,7 +122,7 @@ def test_attn_fwd_varlen_validation(mi):
     assert _varlen(mi, Nq=8, Nkv=3) == "MIATTN_ERR_GQA_RATIO"
     assert _varlen(mi, mask="band", pre=-5, nxt=4) == "MIATTN_ERR_MASK"
     assert _varlen(mi, scale=0.0) == "MIATTN_ERR_SCALE"
-    assert _varlen(mi, D=48) == "MIATTN_ERR_UNSUPPORTED"
+    assert _varlen(mi, D=769) == "MIATTN_ERR_SHAPE"
     assert _varlen(mi, dtype=3) == "MIATTN_ERR_DTYPE"
 
 
@@ -149,7 +144,7 @@ def test_attn_fwd_update_validation(mi):
     assert call(Nq=5) == "MIATTN_ERR_GQA_RATIO"
     assert call(pre=3, nxt=-4) == "MIATTN_ERR_MASK"
     assert call(scale=float("nan")) == "MIATTN_ERR_SCALE"
-    assert call(D=288) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=769) == "MIATTN_ERR_SHAPE"
 
 
 def test_attn_fwd_varlen_update_validation(mi):
@@ -166,7 +161,7 @@ def test_attn_fwd_varlen_update_validation(mi):
     assert call(B=0) == "MIATTN_ERR_SHAPE"
     assert call(mq=101) == "MIATTN_ERR_SHAPE"
     assert call(mask=7) == "MIATTN_ERR_MASK"
-    assert call(D=100) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=0) == "MIATTN_ERR_SHAPE"
 
 
 def test_attn_fwd_ext_validation(mi):
@@ -184,14 +179,10 @@ def test_attn_fwd_ext_validation(mi):
     assert call(mask="band_br", pre=2, nxt=-3) == "MIATTN_ERR_MASK"      # empty band
     assert call(mask="band", pre=4, nxt=0, prefix=P) == "MIATTN_ERR_MASK"  # prefix: causal only
     assert call(mask="none", prefix=P) == "MIATTN_ERR_MASK"
-    assert call(D=80, am=P) == "MIATTN_ERR_UNSUPPORTED"
     assert call(dtype="f64", am=P) == "MIATTN_ERR_DTYPE"
     assert call(D=64, Dv=96) == "MIATTN_ERR_SHAPE"               # kD >= vD
-    assert call(D=64, Dv=48) == "MIATTN_ERR_UNSUPPORTED"         # pair not built
-    assert call(D=128, Dv=64, am=P) == "MIATTN_ERR_UNSUPPORTED"  # Dv < D without a mask tensor
-    # head dims 160..256: V head dim equal, no mask tensor, no dropout
-    assert call(D=256, Dv=128) == "MIATTN_ERR_UNSUPPORTED"
-    assert call(D=192, Dv=192, am=P) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=64, Dv=0) == "MIATTN_ERR_SHAPE"
+    assert call(D=769, Dv=64) == "MIATTN_ERR_SHAPE"
 
     def dcall(p, **kw):
         with pytest.raises(mi.MiattnError) as e:
@@ -205,7 +196,6 @@ def test_attn_fwd_ext_validation(mi):
     assert dcall(0.999) == "MIATTN_ERR_DROPOUT"                   # rounds to 256/256
     assert dcall(0.5, am=P) == "MIATTN_ERR_UNSUPPORTED"
     assert dcall(0.5, D=128, Dv=64) == "MIATTN_ERR_UNSUPPORTED"
-    assert dcall(0.5, D=224, Dv=224) == "MIATTN_ERR_UNSUPPORTED"
 
     def vcall(**kw):
         a = dict(mask="causal", prefix=P, D=128, Dv=128)
@@ -216,7 +206,7 @@ def test_attn_fwd_ext_validation(mi):
                                       P, stream=0)
         return mi.STATUS[e.value.status]
     assert vcall(mask="band") == "MIATTN_ERR_MASK"
-    assert vcall(D=48, Dv=48) == "MIATTN_ERR_UNSUPPORTED"
+    assert vcall(D=770, Dv=48) == "MIATTN_ERR_SHAPE"
     assert vcall(Dv=0) == "MIATTN_ERR_SHAPE"
 
 
@@ -285,9 +275,8 @@ def test_mha_self_attn_fwd_validation(mi):
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(N=7) == "MIATTN_ERR_SHAPE"          # 512 is not a multiple of 7
     assert call(N=512) == "MIATTN_ERR_SHAPE"        # more than 256 heads
-    assert call(N=16, E=256) == "MIATTN_ERR_UNSUPPORTED"   # D = 16 is not built
-    assert call(N=2, E=512, dtype="f32") == "MIATTN_ERR_UNSUPPORTED"   # D 256: bf16 / fp16 only
-    assert call(N=2, E=512, p=0.1) == "MIATTN_ERR_UNSUPPORTED"        # D 256: no dropout
+    assert call(N=1, E=1024) == "MIATTN_ERR_SHAPE"  # head dim above 768
+    assert call(N=3, E=771) == "MIATTN_ERR_SHAPE"   # rows of 1542 bytes: not 16-byte multiples
     assert call(ws=None) == "MIATTN_ERR_WORKSPACE"
     assert call(wsb=need - 1) == "MIATTN_ERR_WORKSPACE"
     assert call(out=P + 2) == "MIATTN_ERR_SHAPE"    # not 16-byte aligned
