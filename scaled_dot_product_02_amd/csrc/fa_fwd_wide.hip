@@ -5,17 +5,20 @@
 //
 // Same operation, batches, masks, statistics, fused update and dropout as the other
 // kernels.  A workgroup of 8 waves owns BM query rows (32 for fp32 and for V head dims
-// above 512, else 64) and walks 32-key tiles, but splits the head dims, not the rows, across
-// its waves:
-//   * wave w contracts S^T = K Q^T over its own slice of the Q/K head dim (16 KC columns,
-//     zero past D) on the matrix cores, with Q held in registers and K read from global
-//     memory (L2) straight into MFMA operand layout;
-//   * the eight partial score tiles meet in LDS; each wave then owns BM / 8 rows: it sums
-//     the partials, applies scale and masks, and runs the online-softmax step (running
-//     max, rescale factor, exponentials, running sum) and writes P and the factor back;
-//   * wave w accumulates O^T = V^T P^T for its slice of the V head dim (32 VB columns).
+// above 512, else 64) and walks 32-key tiles, splitting the head dims across its waves:
+//   * for S^T = K Q^T the waves form RB row blocks of 32 rows x 8 / RB slices of the Q/K
+//     head dim (zero past D); each contracts its slice on the matrix cores, with its Q rows
+//     held in registers and K read from global memory (L2) straight into MFMA operand
+//     layout;
+//   * the partial score tiles meet in LDS; each wave then owns BM / 8 rows: it sums the
+//     partials, applies scale and masks, and runs the online-softmax step (running max,
+//     rescale factor, exponentials, running sum) and writes P and the factor back;
+//   * wave w accumulates O^T = V^T P^T for all BM rows over its slice of the V head dim
+//     (32 VB columns).  bf16 / fp16 stage that slice in LDS from 16-byte loads, one tile
+//     ahead, and read it back transposed (ds_read_b64_tr_b16) as the A operand.
 // Two barriers per tile.  bf16 / fp16 use v_mfma_f32_32x32x16 with P rounded to the input
-// type (as the tiled MFMA kernel); fp32 uses v_mfma_f32_32x32x2f32 with P kept in fp32.
+// type (as the tiled MFMA kernel); fp32 uses v_mfma_f32_32x32x2f32 with P kept in fp32 and
+// V^T fragments read from global memory.
 #include "fa_common.h"
 
 namespace miattn {
@@ -23,6 +26,9 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NW = 8;          // waves per workgroup
 constexpr int NT = 64 * NW;
@@ -79,9 +85,20 @@ __device__ inline typename Frag<T>::v8 load_frag(const T* x, int n, bool vec)
 // operands and accumulators of a wave within 256 registers), else two.
 constexpr int wide_row_blocks(bool f32, int VB) { return f32 || VB == 3 ? 1 : 2; }
 
-// T: input / output type.  KC: 16-column steps of the Q/K head dim per wave (the workgroup
-// covers 128 KC >= D); VB: 32-column blocks of the V head dim per wave (256 VB >= Dv).
-// flags: 1 = Q and K rows allow vector loads, 2 = output rows allow 4-element stores.
+// ds_read_b64_tr_b16 over four rows of 16-bit elements: lane l, slot e receives element
+// l % 4 of the 8-byte block read by lane 16 (l / 16) + 4 e + (l % 16) / 4.  The V tile of a
+// wave sits in LDS as [key][dv]; lane r reads the four dv 16 ((r / 16) % 2) + 4 (r % 4) ..
+// + 3 of key (r % 16) / 4 (+ 4 for the second read), so lane l ends up with
+// V[key 8 (l / 32) + e][dv l % 32] for e = 0..7: the A operand of O^T += V^T P^T.
+__device__ inline i16x4 ds_read_tr16(const void* lds)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds);
+}
+
+// T: input / output type.  KC: the workgroup covers 128 KC >= D columns of the Q/K head
+// dim; VB: 32-column blocks of the V head dim per wave (256 VB >= Dv).
+// flags: 1 = Q and K rows allow vector loads, 2 = output rows allow 4-element stores,
+// 4 = V rows allow 8-element vector loads.
 template <typename T, int KC, int VB>
 __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, int flags)
 {
@@ -92,12 +109,31 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     constexpr int LPR = 64 / RPW;                // lanes per softmax row
     constexpr int KPL = BN / LPR;                // keys per lane in the softmax
     constexpr int PS = Frag<T>::PS;
-    constexpr int DS = 16 * KC, DVS = 32 * VB;
+    // for S^T = K Q^T the waves split into RG row groups (of RBW 32-row blocks) x NDS
+    // slices of the Q/K head dim (16 KQ columns each); for O^T = V^T P^T into NW slices of
+    // the V head dim.  Head dims up to 256 split the rows too (RG = RB), which halves the
+    // partial-score tiles in LDS so that two workgroups fit a CU; larger ones keep every
+    // row block in each wave, so that K is read once per workgroup.
+    constexpr int RG = KC <= 2 ? RB : 1;
+    constexpr int RBW = RB / RG;
+    constexpr int NDS = NW / RG;
+    constexpr int KQ = KC * RG;
+    constexpr int DS = 16 * KQ, DVS = 32 * VB;
+    // 16-bit types stage each wave's V slice in LDS ([key][dv], row stride VSS) from 16-byte
+    // loads and read it back transposed; fp32 reads V^T fragments from global memory
+    constexpr bool TR = sizeof(T) == 2;
+    constexpr int VSS = DVS + 8;
+    constexpr int VCH = DVS / 8;                 // 16-byte chunks per key of a wave's slice
+    constexpr int VU = TR ? BN * VCH / 64 : 1;   // chunks per lane per tile (= 2 VB)
+    // V buffers: two (the next tile's slice loaded and stored during this one) where LDS
+    // allows; one for VB = 1, which keeps the workgroup within half the LDS (two per CU)
+    constexpr int NB = VB == 1 ? 1 : 2;
 
-    __shared__ __attribute__((aligned(16))) float red[NW][BM][RS];
+    __shared__ __attribute__((aligned(16))) float red[NDS][BM][RS];
     __shared__ __attribute__((aligned(16))) T ps[BM][PS];
     __shared__ float alpha_s[BM];
     __shared__ float wfin[2][BM];
+    __shared__ __attribute__((aligned(16))) T vs[NB][TR ? NW : 1][TR ? BN : 1][TR ? VSS : 8];
 
     const TileCoord tc = decode_tile(p, blockIdx.x, BM);
     if (!tc.live) return;
@@ -105,7 +141,7 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     const int col = lane & 31, hi = lane >> 5;
     const int i0 = tc.r0, i1 = tc.r1;
     const int Dv = p.Dv;
-    const bool vec_qk = flags & 1, vec_o = flags & 2;
+    const bool vec_qk = flags & 1, vec_o = flags & 2, vec_v = flags & 4;
 
     const T* qg = (const T*)p.q + (int64_t)tc.b * p.q_sb + tc.q0 * p.q_ss + (int64_t)tc.h * p.q_sh;
     const T* kg = (const T*)p.k + (int64_t)tc.b * p.k_sb + tc.kv0 * p.k_ss + (int64_t)tc.kvh * p.k_sh;
@@ -117,25 +153,27 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     int kv_lo, kv_hi;
     key_range(bd, i0, i1, tc.len_kv, kv_lo, kv_hi);
 
-    // this wave's head-dim slices; waves past the end of one skip that contraction
-    const int d0 = w * DS, dv0 = w * DVS;
-    const int nq = (D + DS - 1) / DS;            // waves holding part of the Q/K head dim
+    // this wave's row block and head-dim slices; waves past the end of one skip that
+    // contraction
+    const int rg = w / NDS, ds = w % NDS;
+    const int d0 = ds * DS, dv0 = w * DVS;
+    const int nq = (D + DS - 1) / DS;            // slices holding part of the Q/K head dim
     const bool qk_on = d0 < D, pv_on = dv0 < Dv;
     const int dlane = d0 + 8 * hi;               // first of the lane's 8 head-dim columns
 
-    v8 qf[RB][KC];
+    v8 qf[RBW][KQ];
     #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int qi = i0 + 32 * rb + col;
+    for (int r = 0; r < RBW; ++r) {
+        const int qi = i0 + 32 * (rg * RBW + r) + col;
         #pragma unroll
-        for (int c = 0; c < KC; ++c)
-            qf[rb][c] = qk_on && qi < i1 ? load_frag(qg + (int64_t)qi * p.q_ss + dlane + 16 * c, D - dlane - 16 * c, vec_qk)
-                                         : load_frag(qg, 0, false);
+        for (int c = 0; c < KQ; ++c)
+            qf[r][c] = qk_on && qi < i1 ? load_frag(qg + (int64_t)qi * p.q_ss + dlane + 16 * c, D - dlane - 16 * c, vec_qk)
+                                        : load_frag(qg, 0, false);
     }
-    auto load_k = [&](int j0, v8 (&kf)[KC]) {
+    auto load_k = [&](int j0, v8 (&kf)[KQ]) {
         const int j = j0 + col;
         #pragma unroll
-        for (int c = 0; c < KC; ++c)
+        for (int c = 0; c < KQ; ++c)
             kf[c] = qk_on && j < tc.len_kv ? load_frag(kg + (int64_t)j * p.k_ss + dlane + 16 * c, D - dlane - 16 * c, vec_qk)
                                            : load_frag(kg, 0, false);
     };
@@ -155,31 +193,71 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     const uint8_t* arow = mrow ? p.amask + (int64_t)sqi * p.amask_ld : nullptr;
     float m_run = -INFINITY, l_run = 0.f;
 
+    // V slice of the tile at key j0 (16-bit types): chunk u of the lane = key u / VCH, dims
+    // 8 (u % VCH) .. + 7 of the wave's slice; only this wave reads its slice, so its LDS
+    // writes need no barrier
+    u32x4 vst[VU];
+    auto load_v = [&](int j0) {
+        #pragma unroll
+        for (int i = 0; i < VU; ++i) {
+            const int u = lane + 64 * i, j = j0 + u / VCH, dv = dv0 + 8 * (u % VCH);
+            const T* src = vg + (int64_t)j * p.v_ss + dv;
+            vst[i] = u32x4{0u, 0u, 0u, 0u};
+            if (pv_on && j < tc.len_kv && dv < Dv) {
+                if (vec_v) {
+                    vst[i] = *(const u32x4*)src;
+                } else {
+                    T x[8];
+                    #pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = dv + e < Dv ? src[e] : (T)0.f;
+                    vst[i] = *(const u32x4*)x;
+                }
+            }
+        }
+    };
+    auto store_v = [&](int buf) {
+        #pragma unroll
+        for (int i = 0; i < VU; ++i) {
+            const int u = lane + 64 * i;
+            *(u32x4*)&vs[buf][w][u / VCH][8 * (u % VCH)] = vst[i];
+        }
+    };
+
     const int jfirst = (kv_lo / BN) * BN;
-    v8 kf[KC];
+    v8 kf[KQ];
     load_k(jfirst, kf);
+    if constexpr (TR && NB == 2) {
+        load_v(jfirst);
+        store_v(0);
+    }
     for (int j0 = jfirst; j0 < kv_hi; j0 += BN) {
-        // partial S^T over this wave's head-dim slice -> red[w][row][key]
+        const int buf = NB == 2 ? ((j0 - jfirst) / BN) & 1 : 0;
+        if constexpr (TR) {
+            if (NB == 1) load_v(j0);
+            else if (j0 + BN < kv_hi) load_v(j0 + BN);
+        }
+        // partial S^T of the wave's row blocks over its head-dim slice -> red[ds][row][key]
         if (qk_on) {
             #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
+            for (int r = 0; r < RBW; ++r) {
                 f32x16 s;
                 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[r] = 0.f;
+                for (int x = 0; x < 16; ++x) s[x] = 0.f;
                 #pragma unroll
-                for (int c = 0; c < KC; ++c) s = Frag<T>::mma(kf[c], qf[rb][c], s);
+                for (int c = 0; c < KQ; ++c) s = Frag<T>::mma(kf[c], qf[r][c], s);
                 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    *(f32x4*)&red[w][32 * rb + col][8 * jj + 4 * hi] =
+                    *(f32x4*)&red[ds][32 * (rg * RBW + r) + col][8 * jj + 4 * hi] =
                         f32x4{s[4 * jj], s[4 * jj + 1], s[4 * jj + 2], s[4 * jj + 3]};
             }
             if (j0 + BN < kv_hi) load_k(j0 + BN, kf);
         }
         __syncthreads();
 
-        // V^T fragments of this tile (consumed after the softmax): lane holds
+        // fp32: V^T fragments of this tile (consumed after the softmax): lane holds
         // V[key 16 kc + 8 hi + e][dv0 + 32 vb + col]
-        v8 vf[VB][2];
+        v8 vf[TR ? 1 : VB][2];
+        if constexpr (!TR)
         #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
             #pragma unroll
@@ -236,6 +314,12 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
             m_run = m_new;
             if (lane % LPR == 0) alpha_s[srow] = alpha;
         }
+        // this tile's V slice (one buffer), or the next tile's into the other buffer; the
+        // last reader of either, this wave's own PV, came earlier in program order
+        if constexpr (TR) {
+            if (NB == 1) store_v(0);
+            else if (j0 + BN < kv_hi) store_v(buf ^ 1);
+        }
         __syncthreads();
 
         // O^T += V^T P^T over this wave's V head-dim slice
@@ -249,7 +333,19 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
                 for (int kc = 0; kc < 2; ++kc) {
                     const v8 pf = *(const v8*)&ps[32 * rb + col][16 * kc + 8 * hi];
                     #pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) o[vb][rb] = Frag<T>::mma(vf[vb][kc], pf, o[vb][rb]);
+                    for (int vb = 0; vb < VB; ++vb) {
+                        v8 a;
+                        if constexpr (TR) {
+                            const int key = 16 * kc + 8 * hi + ((lane & 15) >> 2);
+                            const int dv = 32 * vb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                            const i16x4 lo = ds_read_tr16(&vs[buf][w][key][dv]);
+                            const i16x4 up = ds_read_tr16(&vs[buf][w][key + 4][dv]);
+                            a = __builtin_bit_cast(v8, i16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+                        } else {
+                            a = vf[vb][kc];
+                        }
+                        o[vb][rb] = Frag<T>::mma(a, pf, o[vb][rb]);
+                    }
                 }
             }
         }
@@ -360,7 +456,8 @@ hipError_t launch_fa_fwd_wide(const FaParams& p, int D, int dtype, hipStream_t s
 {
     if (D < 1 || D > 768 || p.Dv < 1 || p.Dv > D) return hipErrorInvalidValue;
     const int flags = (D % 8 == 0 && aligned16(p.q) && aligned16(p.k) ? 1 : 0) |
-                      (p.Dv % 4 == 0 && aligned16(p.out) && (!p.prev_out || aligned16(p.prev_out)) ? 2 : 0);
+                      (p.Dv % 4 == 0 && aligned16(p.out) && (!p.prev_out || aligned16(p.prev_out)) ? 2 : 0) |
+                      (p.Dv % 8 == 0 && aligned16(p.v) ? 4 : 0);
     switch (dtype) {
     case 0: return launch_type<float>(p, D, flags, stream);
     case 1: return launch_type<__bf16>(p, D, flags, stream);
