@@ -19,6 +19,7 @@ Also measured in the same run (reported under "secondary"):
   * sparse_csr_attn on the CSR workload (B 2, N 8, S 4096, D 64, band 128 + 64 random), in
     fp32 and in fp64 (same pattern and draws);
   * head dim 256: dense causal bf16, S 8192, N 16 (4-wave workgroups, 32-key tiles);
+  * head dim 768: dense causal bf16, S 4096, N 16 (the head-dim-general kernel);
   * the multi-head self-attention module (mha_self_attn_fwd) at its defaults, embed 512 and
     8 heads, on B 8 x S 4096 bf16 in eval mode (projections + attention flops).
 
@@ -441,6 +442,28 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(d2tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(d2tf / PEAK_BF16_TFLOPS, 4)}}
         del dq, dk, dv_, do_
+
+        # head dim 768, the operator's largest, on the head-dim-general kernel (head dims split
+        # across the waves of a workgroup): dense causal bf16, S 4096, N 16
+        Sw, Nw, Dw = 4096, 16, 768
+        gw = torch.Generator(device=dev); gw.manual_seed(0)
+        wq_, wk_, wv_ = (torch.randn((1, Nw, Sw, Dw), device=dev, generator=gw).to(torch.bfloat16)
+                         for _ in range(3))
+        wo_ = torch.empty_like(wq_)
+        wflops = 4.0 * Dw * Nw * (Sw * (Sw + 1) // 2)
+
+        def step_d768():
+            mi.attn_fwd(wq_, wk_, wv_, wo_, None, None, 1, Nw, Nw, Sw, Sw, Dw, "bf16", "BNSD",
+                        1 / math.sqrt(Dw), "causal", stream=stream.cuda_stream)
+
+        wms = time_launches(step_d768, 10, 2, stream)
+        wtf = wflops / (wms * 1e-3) / 1e12
+        sec["attn_fwd_head_dim_768"] = {
+            "workload": "dense_causal_bf16_b1n16s4096d768", "ms_per_launch": round(wms, 4),
+            "flop_per_launch": wflops,
+            "roofline": {"bound": "mfma", "achieved": round(wtf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(wtf / PEAK_BF16_TFLOPS, 4)}}
+        del wq_, wk_, wv_, wo_
 
         # the multi-head self-attention module at its defaults (embed 512, 8 heads), eval
         # mode: two rocBLAS projections around the attention kernel
