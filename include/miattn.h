@@ -94,8 +94,9 @@ typedef enum {
  *   q    [B, Nq,  Sq,  D] in `layout`;   k, v [B, Nkv, Skv, D] in `layout`;
  *   out  [B, Nq,  Sq,  D] in `layout` (same dtype as q);
  *   softmax_max, softmax_sum: fp32 [B, Nq, Sq] contiguous, or NULL.
- *   dtype: MIATTN_BF16 or MIATTN_F16 (MFMA path: fp32 accumulation, the softmax weights
- *   rounded to the input type for the P V product, RNE output) or MIATTN_F32.
+ *   dtype: MIATTN_BF16 or MIATTN_F16 (fp32 accumulation, the softmax weights rounded to
+ *   the input type for the P V product, RNE output) or MIATTN_F32 (fp32 matrix-core
+ *   products, softmax weights kept in fp32); all on the matrix cores.
  *   D: any of 1..768, the operator spec's range (aclnnFlashAttentionVarLenScore 约束说明),
  *   in every dtype; outside it -> MIATTN_ERR_SHAPE.  The tiled kernels serve 32, 64, 96
  *   and 128 (and 160, 192, 224, 256 in bf16 / fp16 without a mask tensor or dropout);
@@ -230,11 +231,11 @@ miattn_status_t attn_fwd_varlen_update(const void* q, const void* k, const void*
  *     positions, top-left), on top of the mask mode and the prefix; it is shared by all
  *     batch entries / sequences and heads.  The page forbids rows that are entirely masked;
  *     here such a row gives the empty result (out 0, max -inf, sum 0).
- *   bf16 / fp16 with atten_mask run on the matrix cores like attn_fwd when the mask pointer
+ *   bf16 / fp16 with atten_mask run on the tiled kernel like attn_fwd when the mask pointer
  *   is 4-byte aligned, its row length (Skv, resp. max_seqlen_kv) a multiple of 4 and its
- *   size under 2^31 bytes; otherwise (and for fp32) the forward runs in fp32 arithmetic on
- *   the vector ALUs (inputs widened on load, output rounded to the input type).  Other
- *   arguments, limits and errors as attn_fwd / attn_fwd_varlen.
+ *   size under 2^31 bytes; otherwise on the head-dim-general kernel (byte reads of the
+ *   mask), same results to rounding.  Other arguments, limits and errors as attn_fwd /
+ *   attn_fwd_varlen.
  *   Dv: head dim of v and out (aclnnFlashAttentionVarLenScore 约束说明: qD == kD >= vD);
  *     v is [B, Nkv, Skv, Dv] / [Tkv, Nkv, Dv] and out [B, Nq, Sq, Dv] / [Tq, Nq, Dv] in the
  *     same layout.  Any 1 <= Dv <= D (else MIATTN_ERR_SHAPE).

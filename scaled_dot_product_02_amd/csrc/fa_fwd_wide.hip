@@ -1,7 +1,8 @@
 // Attention forward for any head dims 1 <= Dv <= D <= 768 in every dtype: the path for
-// the (D, Dv) pairs and feature combinations that the tiled kernels are not built for
-// (the operator of "aclnnFlashAttentionVarLenScore" allows head dims 1..768 with the V head
-// dim at most the Q/K one; those kernels cover 32..256 in steps of 32).
+// fp32 inputs, and for bf16 / fp16 at the (D, Dv) pairs and feature combinations that the
+// tiled kernel is not built for (the operator of "aclnnFlashAttentionVarLenScore" allows
+// head dims 1..768 with the V head dim at most the Q/K one; the tiled kernel covers 32..256
+// in steps of 32).
 //
 // Same operation, batches, masks, statistics, fused update and dropout as the other
 // kernels.  A workgroup of 8 waves owns BM query rows (32 for fp32 and for V head dims

@@ -38,7 +38,7 @@ struct FaParams {
     const int64_t* prefix;      // device [B] or null: keys j < prefix[b] are seen by every row
                                 // (only with pre unbounded, so the visible keys stay a range)
     const uint8_t* amask;       // device [Sq][Skv] bytes or null: nonzero = masked out,
-                                // sequence-local positions (VALU kernel only)
+                                // sequence-local positions
     int64_t amask_ld;           // row stride of amask
     uint32_t drop_thr;          // dropout: a probability is dropped when its byte < drop_thr
     float drop_scale;           // 256 / (256 - drop_thr), applied to the kept ones
@@ -79,9 +79,6 @@ struct SparseParams {
 // the MFMA forward for bf16 (f16 = false) or fp16 (f16 = true) inputs; both forwards
 // merge into p.prev_* when p.prev_out is set
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
-// the VALU forward: fp32 inputs (dtype 0), or any input type (0, 1 = bf16, 2 = fp16) with
-// an explicit mask (p.amask)
-hipError_t launch_fa_fwd_f32(const FaParams& p, int D, int dtype, hipStream_t stream);
 // the head-dim-general forward: any 1 <= p.Dv <= D <= 768, every dtype and feature; rows per
 // workgroup fa_wide_tile_m(dtype, p.Dv)
 hipError_t launch_fa_fwd_wide(const FaParams& p, int D, int dtype, hipStream_t stream);
@@ -103,6 +100,5 @@ constexpr bool fa_four_waves(int D, bool mask_or_dropout)
 {
     return D > 128 || (!mask_or_dropout && D >= FA_FOUR_WAVE_MIN_D);
 }
-constexpr int kF32TileM = 64;
 
 }  // namespace miattn

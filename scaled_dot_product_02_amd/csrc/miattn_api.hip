@@ -57,17 +57,18 @@ bool head_dim_built(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 12
 // and no dropout
 bool big_head_dim(int64_t D) { return D == 160 || D == 192 || D == 224 || D == 256; }
 
-// Whether one of the tiled kernels serves this forward; every other valid one runs on the
-// head-dim-general kernel.
+// Whether the tiled MFMA kernel serves this forward (bf16 / fp16); every other valid one,
+// fp32 included, runs on the head-dim-general kernel.
 bool tiled_forward(int64_t D, int64_t Dv, int dtype, bool update, bool amask, bool drop)
 {
+    if (dtype != MIATTN_BF16 && dtype != MIATTN_F16) return false;
     if (head_dim_built(D)) {
         if (Dv == D) return true;
         const bool pair = (D == 64 && Dv == 32) || (D == 96 && Dv == 64) || (D == 128 && Dv == 64) ||
                           (D == 128 && Dv == 96);
         return pair && !update && !amask && !drop;
     }
-    return big_head_dim(D) && Dv == D && dtype != MIATTN_F32 && !amask && !drop;
+    return big_head_dim(D) && Dv == D && !amask && !drop;
 }
 
 // Dropout probability p -> byte threshold round(256 p) and the scale of kept probabilities;
@@ -112,20 +113,18 @@ miattn_status_t size_grid(FaParams& p, int64_t max_len_q, int tile_m)
 
 miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
 {
-    // an explicit mask stays on the matrix cores when its rows are 4-byte aligned words
-    // (read as 32-bit buffer loads with 32-bit offsets); otherwise it takes the VALU kernel
+    // an explicit mask stays on the tiled kernel when its rows are 4-byte aligned words
+    // (read as 32-bit buffer loads with 32-bit offsets); otherwise it takes the general one
     const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
-    const bool mfma = (dtype == MIATTN_BF16 || dtype == MIATTN_F16) && mask_words;
-    const bool tiled = tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr, p.amask != nullptr, p.drop_thr != 0);
+    const bool tiled = mask_words && tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr,
+                                                   p.amask != nullptr, p.drop_thr != 0);
     const int tile_m = !tiled ? fa_wide_tile_m(dtype, p.Dv)
-                     : !mfma ? kF32TileM
                      : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
-    hipError_t e = !tiled ? launch_fa_fwd_wide(p, (int)D, dtype, stream)
-                 : mfma ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
-                        : launch_fa_fwd_f32(p, (int)D, dtype, stream);
+    hipError_t e = tiled ? launch_fa_fwd_bf16(p, (int)D, dtype == MIATTN_F16, stream)
+                         : launch_fa_fwd_wide(p, (int)D, dtype, stream);
     return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 

@@ -1,7 +1,9 @@
 """GPU parity of the mask modes against the CPU fp64 oracle's explicit visibility matrices:
 bottom-right causal and band (attn_fwd, attn_fwd_varlen, attn_fwd_update), the prefix
 (attn_fwd_varlen_ext / attn_fwd_ext), and an explicit mask tensor (any dtype; rows of
-whole 4-byte words on the matrix cores for bf16 / fp16, other rows on the vector ALUs).  Sizes span several tiles with ragged ends; Sq > Skv gives empty rows.
+whole 4-byte words on the tiled kernel for bf16 / fp16, other rows and fp32 on the
+head-dim-general kernel).  Sizes span several tiles with ragged ends; Sq > Skv gives empty
+rows.
 """
 import math
 
@@ -81,7 +83,7 @@ def test_dense_prefix(mi, dtype, mask, align):
 @pytest.mark.parametrize("Skv", [150, 152])
 def test_dense_explicit_mask(mi, dtype, D, mask, pre, nxt, Skv):
     """Mask rows of 152 bytes (4-byte words) run on the matrix cores for bf16 / fp16; rows
-    of 150 bytes take the vector-ALU kernel."""
+    of 150 bytes take the head-dim-general kernel."""
     Sq = 200
     w = synthetic.dense_inputs(83, 2, 4, 2, Sq, Skv, D, dtype, "BSH")
     rng = np.random.default_rng(84)
