@@ -20,6 +20,7 @@ Also measured in the same run (reported under "secondary"):
     fp32 and in fp64 (same pattern and draws);
   * head dim 256: dense causal bf16, S 8192, N 16 (4-wave workgroups, 32-key tiles);
   * head dim 768: dense causal bf16, S 4096, N 16 (the head-dim-general kernel);
+  * fp32 inputs: dense causal, S 4096, N 16, D 128 (fp32 matrix-core products);
   * the multi-head self-attention module (mha_self_attn_fwd) at its defaults, embed 512 and
     8 heads, on B 8 x S 4096 bf16 in eval mode (projections + attention flops).
 
@@ -47,7 +48,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector ALUs and matrix cores alike)
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
 PROBES_LIB = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn_probes.so")
 PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_varlen_causal_gqa_t33064_pmc.json")
@@ -464,6 +465,27 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(wtf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(wtf / PEAK_BF16_TFLOPS, 4)}}
         del wq_, wk_, wv_, wo_
+
+        # fp32 inputs (the general kernel's fp32 matrix-core path): dense causal, S 4096,
+        # N 16, D 128
+        Sf, Nf, Df = 4096, 16, 128
+        gf = torch.Generator(device=dev); gf.manual_seed(0)
+        fq, fk, fv = (torch.randn((1, Nf, Sf, Df), device=dev, generator=gf) for _ in range(3))
+        fo = torch.empty_like(fq)
+        fflops = 4.0 * Df * Nf * (Sf * (Sf + 1) // 2)
+
+        def step_f32():
+            mi.attn_fwd(fq, fk, fv, fo, None, None, 1, Nf, Nf, Sf, Sf, Df, "f32", "BNSD",
+                        1 / math.sqrt(Df), "causal", stream=stream.cuda_stream)
+
+        fms = time_launches(step_f32, 10, 2, stream)
+        ftf = fflops / (fms * 1e-3) / 1e12
+        sec["attn_fwd_fp32"] = {
+            "workload": "dense_causal_f32_b1n16s4096d128", "ms_per_launch": round(fms, 4),
+            "flop_per_launch": fflops,
+            "roofline": {"bound": "mfma", "achieved": round(ftf, 2), "peak": PEAK_F32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ftf / PEAK_F32_TFLOPS, 4)}}
+        del fq, fk, fv, fo
 
         # the multi-head self-attention module at its defaults (embed 512, 8 heads), eval
         # mode: two rocBLAS projections around the attention kernel
