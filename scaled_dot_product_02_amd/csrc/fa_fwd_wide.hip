@@ -5,8 +5,8 @@
 // in steps of 32).
 //
 // Same operation, batches, masks, statistics, fused update and dropout as the other
-// kernels.  A workgroup of 8 waves owns BM query rows (32 for fp32 and for V head dims
-// above 512, else 64) and walks 32-key tiles, splitting the head dims across its waves:
+// kernels.  A workgroup of 8 waves owns BM query rows (32 for fp32, 64 for bf16 / fp16)
+// and walks 32-key tiles, splitting the head dims across its waves:
 //   * for S^T = K Q^T the waves form RB row blocks of 32 rows x 8 / RB slices of the Q/K
 //     head dim (zero past D); each contracts its slice on the matrix cores, with its Q rows
 //     held in registers and K read from global memory (L2) straight into MFMA operand
@@ -82,9 +82,9 @@ __device__ inline typename Frag<T>::v8 load_frag(const T* x, int n, bool vec)
     return r;
 }
 
-// 32-row blocks per workgroup: one for fp32 and for V head dims above 512 (to keep the
-// operands and accumulators of a wave within 256 registers), else two.
-constexpr int wide_row_blocks(bool f32, int VB) { return f32 || VB == 3 ? 1 : 2; }
+// 32-row blocks per workgroup: one for fp32 (to keep the operands and accumulators of a
+// wave within 256 registers), else two.
+constexpr int wide_row_blocks(bool f32) { return f32 ? 1 : 2; }
 
 // ds_read_b64_tr_b16 over four rows of 16-bit elements: lane l, slot e receives element
 // l % 4 of the 8-byte block read by lane 16 (l / 16) + 4 e + (l % 16) / 4.  The V tile of a
@@ -104,7 +104,7 @@ template <typename T, int KC, int VB>
 __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, int flags)
 {
     typedef typename Frag<T>::v8 v8;
-    constexpr int RB = wide_row_blocks(sizeof(T) == 4, VB);   // 32-row blocks per workgroup
+    constexpr int RB = wide_row_blocks(sizeof(T) == 4);   // 32-row blocks per workgroup
     constexpr int BM = 32 * RB;
     constexpr int RPW = BM / NW;                 // softmax rows per wave
     constexpr int LPR = 64 / RPW;                // lanes per softmax row
@@ -126,9 +126,10 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     constexpr int VSS = DVS + 8;
     constexpr int VCH = DVS / 8;                 // 16-byte chunks per key of a wave's slice
     constexpr int VU = TR ? BN * VCH / 64 : 1;   // chunks per lane per tile (= 2 VB)
-    // V buffers: two (the next tile's slice loaded and stored during this one) where LDS
-    // allows; one for VB = 1, which keeps the workgroup within half the LDS (two per CU)
-    constexpr int NB = VB == 1 ? 1 : 2;
+    // V buffers: two (the next tile's slice loaded and stored during this one) for VB = 2;
+    // one for VB = 1, which keeps the workgroup within half the LDS (two per CU), and for
+    // VB = 3, where two would not fit beside the partial-score tiles
+    constexpr int NB = VB == 2 ? 2 : 1;
 
     __shared__ __attribute__((aligned(16))) float red[NDS][BM][RS];
     __shared__ __attribute__((aligned(16))) T ps[BM][PS];
@@ -450,7 +451,7 @@ bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
 
 }  // namespace
 
-int fa_wide_tile_m(int dtype, int Dv) { return 32 * wide_row_blocks(dtype == 0, (Dv + 255) / 256); }
+int fa_wide_tile_m(int dtype) { return 32 * wide_row_blocks(dtype == 0); }
 
 // dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the C-ABI enum values)
 hipError_t launch_fa_fwd_wide(const FaParams& p, int D, int dtype, hipStream_t stream)

@@ -80,9 +80,9 @@ struct SparseParams {
 // merge into p.prev_* when p.prev_out is set
 hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t stream);
 // the head-dim-general forward: any 1 <= p.Dv <= D <= 768, every dtype and feature; rows per
-// workgroup fa_wide_tile_m(dtype, p.Dv)
+// workgroup fa_wide_tile_m(dtype)
 hipError_t launch_fa_fwd_wide(const FaParams& p, int D, int dtype, hipStream_t stream);
-int fa_wide_tile_m(int dtype, int Dv);
+int fa_wide_tile_m(int dtype);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream);
 

@@ -119,7 +119,7 @@ miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream,
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
     const bool tiled = mask_words && tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr,
                                                    p.amask != nullptr, p.drop_thr != 0);
-    const int tile_m = !tiled ? fa_wide_tile_m(dtype, p.Dv)
+    const int tile_m = !tiled ? fa_wide_tile_m(dtype)
                      : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
     if (st != MIATTN_OK) return st;
