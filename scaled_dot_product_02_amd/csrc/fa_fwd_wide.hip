@@ -15,8 +15,9 @@
 //     partials, applies scale and masks, and runs the online-softmax step (running max,
 //     rescale factor, exponentials, running sum) and writes P and the factor back;
 //   * wave w accumulates O^T = V^T P^T for all BM rows over its slice of the V head dim
-//     (32 VB columns).  bf16 / fp16 stage that slice in LDS from 16-byte loads, one tile
-//     ahead, and read it back transposed (ds_read_b64_tr_b16) as the A operand.
+//     (32 VB columns).  bf16 / fp16 stage that slice in LDS from 16-byte loads issued at
+//     the start of the tile (for VB = 2 a tile ahead, into a second buffer) and read it
+//     back transposed (ds_read_b64_tr_b16) as the A operand.
 // Two barriers per tile.  bf16 / fp16 use v_mfma_f32_32x32x16 with P rounded to the input
 // type (as the tiled MFMA kernel); fp32 uses v_mfma_f32_32x32x2f32 with P kept in fp32 and
 // V^T fragments read from global memory.
