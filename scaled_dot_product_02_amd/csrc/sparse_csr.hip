@@ -63,7 +63,13 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
     const T scale_log2 = sizeof(T) == 8 ? (T)p.scale_log2_d : (T)p.scale_log2;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t total = (int64_t)p.B * p.N * p.S;
-    const int64_t row = (int64_t)blockIdx.x * (NT / 64) + wave;
+    // workgroups go to the 8 XCDs round-robin (id mod 8); XCD x takes the x-th eighth of
+    // the row blocks in order, so that the rows resident on one XCD are consecutive rows of
+    // one slice and share its K/V rows (the band, and the slice as a whole) in that XCD's L2
+    const int64_t nblk = (total + NT / 64 - 1) / (NT / 64);
+    const int64_t per = (nblk + 7) / 8;
+    const int64_t blk = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    const int64_t row = blk * (NT / 64) + wave;
     const bool valid = row < total;
     if (valid)
         for (int d = lane; d < D; d += 64) qs[wave][d] = q[row * D + d];
@@ -146,7 +152,7 @@ template <typename T>
 hipError_t launch_t(const SparseParams& p, int D, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.N * p.S;
-    dim3 grid((unsigned)((rows + NT / 64 - 1) / (NT / 64))), block(NT);
+    dim3 grid((unsigned)(((rows + NT / 64 - 1) / (NT / 64) + 7) / 8 * 8)), block(NT);
     switch (D) {
     case 32: hipLaunchKernelGGL((sparse_csr_kernel<T, 32>), grid, block, 0, stream, p); break;
     case 64: hipLaunchKernelGGL((sparse_csr_kernel<T, 64>), grid, block, 0, stream, p); break;
