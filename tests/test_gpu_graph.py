@@ -66,3 +66,46 @@ def test_graph_capture_varlen_forward_and_merge(mi):
             assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.int16) if want.dtype == torch.bfloat16 else want), rep
     assert np.isfinite(out.float().cpu().numpy()).all()
+
+
+def test_graph_capture_general_kernel(mi):
+    """The head-dim-general kernel (fp32 at D 128, and bf16 at D 200 with a smaller V head
+    dim) captured into a graph: every replay equals the eager run bit for bit."""
+    lengths = [150, 0, 1, 65, 33]
+    wf = synthetic.varlen_inputs(402, Nq=4, Nkv=2, D=128, dtype="f32", lengths_q=lengths)
+    wb = synthetic.varlen_inputs(403, Nq=4, Nkv=2, D=200, dtype="bf16", lengths_q=lengths)
+    T = wf["Tq"]
+    qf, kf, vf = (dev(wf[x], "f32") for x in ("q", "k", "v"))
+    qb, kb, vb = (dev(wb[x], "bf16") for x in ("q", "k", "v"))
+    vb = vb[..., :120].contiguous()
+    cu = torch.from_numpy(wf["cu_q"]).to("cuda:0")
+    of, ob = torch.empty_like(qf), torch.empty((T, 4, 120), dtype=torch.bfloat16, device="cuda:0")
+    mf, lf, mb, lb = (torch.empty((4, T), device="cuda:0") for _ in range(4))
+    side = torch.cuda.Stream()
+
+    def work():
+        s = torch.cuda.current_stream()
+        mi.attn_fwd_varlen(qf, kf, vf, of, mf, lf, cu, cu, wf["B"], T, T, 150, 150, 4, 2, 128,
+                           "f32", 1 / math.sqrt(128), "causal", stream=s)
+        mi.attn_fwd_varlen_ext(qb, kb, vb, ob, mb, lb, cu, cu, wb["B"], T, T, 150, 150, 4, 2, 200,
+                               120, "bf16", 1 / math.sqrt(200), "band", 30, 5, None, None, stream=s)
+
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (of, mf, lf, ob, mb, lb)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        work()
+    for rep in range(3):
+        for t in (of, ob):
+            t.fill_(float("nan"))
+        for t in (mf, lf, mb, lb):
+            t.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((of, mf, lf, ob, mb, lb), eager):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), rep
+    assert np.isfinite(of.cpu().numpy()).all()
