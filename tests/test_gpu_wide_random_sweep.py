@@ -1,4 +1,4 @@
-"""A seeded random sweep of the head-dim-general forward against the CPU fp64 oracle: each
+"""A seeded random sweep (150 cases) of the head-dim-general forward against the CPU fp64 oracle: each
 case draws Q/K and V head dims (1 <= Dv <= D <= 768, odd sizes included, dims the tiled
 kernels serve excluded so every case runs on the general kernel), dtype, GQA ratio, dense
 layout or packed batch (zero lengths included), a mask mode with random band widths and,
@@ -17,7 +17,7 @@ from gpu_utils import check_out, check_stats, dev, empty_like_storage, host_valu
 pytestmark = pytest.mark.gpu
 
 BIG = 1 << 40
-N_CASES = 60
+N_CASES = 150
 TILED = {32, 64, 96, 128, 160, 192, 224, 256}
 
 
