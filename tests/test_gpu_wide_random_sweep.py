@@ -1,9 +1,9 @@
-"""A seeded random sweep (150 cases) of the head-dim-general forward against the CPU fp64 oracle: each
-case draws Q/K and V head dims (1 <= Dv <= D <= 768, odd sizes included, dims the tiled
-kernels serve excluded so every case runs on the general kernel), dtype, GQA ratio, dense
-layout or packed batch (zero lengths included), a mask mode with random band widths and,
-for some cases, an explicit mask tensor.  The oracle sees each mask as an explicit
-visibility matrix (oracle.keep_band, pinned against np.tril and torch's SDPA)."""
+"""A seeded random sweep (150 cases) of the head-dim-general forward against the CPU fp64
+oracle: each case draws Q/K and V head dims (1 <= Dv <= D <= 768, odd sizes included, dims
+the tiled kernels serve excluded so every case runs on the general kernel), dtype, GQA
+ratio, dense layout or packed batch (zero lengths included), a mask mode with random band
+widths and, for some cases, an explicit mask tensor.  The oracle sees each mask as an
+explicit visibility matrix (oracle.keep_band, pinned against np.tril and torch's SDPA)."""
 import math
 
 import numpy as np
