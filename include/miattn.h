@@ -82,6 +82,9 @@ typedef enum {
     MIATTN_MASK_BAND_BR = 4
 } miattn_mask_t;
 
+/* Kernels a dense forward may run on (attn_fwd_route). */
+typedef enum { MIATTN_KERNEL_TILED = 1, MIATTN_KERNEL_GENERAL = 2 } miattn_kernel_t;
+
 /*
  * attn_fwd - dense attention forward over a batch of equal-length sequences.
  *
@@ -103,7 +106,11 @@ typedef enum {
  *   every other head dim and combination runs on a head-dim-general MFMA kernel (the head
  *   dim split over the waves of a workgroup, partial scores summed in LDS), same results
  *   to rounding, slower.
- *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, Sq, Skv >= 1 with B*Sq and B*Skv <= 2^31.
+ *   Ranges: B >= 1, 1 <= Nq, Nkv <= 256, 1 <= Sq, Skv <= 2^30 with B*Sq and
+ *   B*Skv <= 2^31.  Shapes whose K / V row stride is too large for the tiled kernels'
+ *   32-bit tile offsets (64 rows x stride x element size >= 2^31 bytes: the SBH layout
+ *   with B*Nkv*D >= 2^24 in bf16 / fp16) run on the head-dim-general kernel, which indexes
+ *   in 64 bits; attn_fwd_route reports the choice.
  *   scale: finite and > 0 (callers pass 1/sqrt(D)).
  *   Pass pre_tokens/next_tokens for the band modes; they are ignored otherwise.
  *   Returns MIATTN_OK or an error status; nothing is enqueued on error.
@@ -269,6 +276,20 @@ miattn_status_t attn_fwd_varlen_ext(const void* q, const void* k, const void* v,
                                        const int64_t* prefix, const uint8_t* atten_mask,
                                        float dropout_p, uint64_t seed, uint32_t offset,
                                        void* stream);
+
+/*
+ * attn_fwd_route - which kernel a dense forward with these arguments runs on, without any
+ * HIP call (a query for callers and tests of the routing that attn_fwd_ext and
+ * attn_fwd_update apply; the routing is a property of this implementation, not of the
+ * pages).  Arguments as attn_fwd_ext; update != 0 asks about attn_fwd_update; atten_mask
+ * is only inspected for its alignment, never read.
+ *   Returns MIATTN_KERNEL_TILED or MIATTN_KERNEL_GENERAL, or minus the status the forward
+ *   would return for these arguments (e.g. -MIATTN_ERR_SHAPE).
+ */
+int32_t attn_fwd_route(int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                       int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout,
+                       miattn_mask_t mask, const uint8_t* atten_mask, float dropout_p,
+                       int32_t update);
 
 /*
  * sparse_csr_attn - CSR-sparse attention (Paddle "sparse_attention": formula, parameters

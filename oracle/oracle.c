@@ -233,13 +233,17 @@ int oracle_attn_keep(const double* q, const double* k, const double* v, double* 
 }
 
 /*
- * Merge of two partial results of the same queries over disjoint key sets, in the order
- * the ring-attention update page states it: take the larger max, rescale each partial
- * sum by exp(own max - new max), add the sums, and weight each partial output by its
- * rescaled sum over the new sum.
+ * Merge of two partial results of the same queries over disjoint key sets (the update of
+ * "npu_ring_attention_update对外接口"), written from the log-sum-exp identity rather than
+ * in that page's step order: a partial (o_i, m_i, l_i) stands for keys whose softmax
+ * weights sum to Z_i = l_i e^{m_i}, i.e. log|Z_i| = m_i + ln|l_i| (the sign of l_i is kept,
+ * so that the page's example with arbitrary, even negative, sums is covered).  The union of
+ * the keys has Z = Z_1 + Z_2, taken as a signed log-add-exp; each partial output enters
+ * with weight Z_i / Z; the union's max is max(m_1, m_2) and its sum l = Z e^{-max}.
  *   o1, o2, out [B][N][S][D]; m1, l1, m2, l2, mo, lo [B][N][S]; contiguous fp64.
  * Reading for an all-empty pair (both max = -inf, where the plain formula divides 0/0):
- * out = 0, max = -inf, sum = 0.
+ * out = 0, max = -inf, sum = 0.  A pair whose sums are both 0 has no weight at all and
+ * gives out = 0, sum = 0 with the larger max.
  */
 int oracle_merge(const double* o1, const double* m1, const double* l1,
                  const double* o2, const double* m2, const double* l2,
@@ -251,20 +255,27 @@ int oracle_merge(const double* o1, const double* m1, const double* l1,
     int nt = pick_threads(nthreads);
 #pragma omp parallel for num_threads(nt) schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        double m = m1[r] > m2[r] ? m1[r] : m2[r];
-        if (m == -INFINITY) {
-            mo[r] = -INFINITY;
+        const double m = m1[r] > m2[r] ? m1[r] : m2[r];
+        /* log|Z_i| and sign of Z_i; an empty partial (sum 0) has log|Z_i| = -inf */
+        const double a1 = l1[r] == 0.0 ? -INFINITY : m1[r] + log(fabs(l1[r]));
+        const double a2 = l2[r] == 0.0 ? -INFINITY : m2[r] + log(fabs(l2[r]));
+        const double g1 = l1[r] < 0.0 ? -1.0 : 1.0, g2 = l2[r] < 0.0 ? -1.0 : 1.0;
+        const double amax = a1 > a2 ? a1 : a2;
+        if (m == -INFINITY || amax == -INFINITY) {
+            mo[r] = m;
             lo[r] = 0.0;
             for (int64_t d = 0; d < D; ++d) out[r * D + d] = 0.0;
             continue;
         }
-        double s1 = l1[r] * exp(m1[r] - m);
-        double s2 = l2[r] * exp(m2[r] - m);
-        double l = s1 + s2;
-        double w1 = s1 / l, w2 = s2 / l;
+        /* Z = Z_1 + Z_2 = e^{amax} (g1 e^{a1 - amax} + g2 e^{a2 - amax}) */
+        const double rel = g1 * exp(a1 - amax) + g2 * exp(a2 - amax);
+        const double gz = rel < 0.0 ? -1.0 : 1.0;
+        const double az = amax + log(fabs(rel));             /* log|Z| */
+        const double w1 = g1 * gz * exp(a1 - az);              /* Z_1 / Z */
+        const double w2 = g2 * gz * exp(a2 - az);              /* Z_2 / Z */
         for (int64_t d = 0; d < D; ++d) out[r * D + d] = o1[r * D + d] * w1 + o2[r * D + d] * w2;
         mo[r] = m;
-        lo[r] = l;
+        lo[r] = gz * exp(az - m);
     }
     return 0;
 }

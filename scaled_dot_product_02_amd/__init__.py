@@ -32,9 +32,11 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
 
+KERNELS = {1: "tiled", 2: "general"}
+
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-           "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
-           "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str")
+           "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
+           "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -53,6 +55,8 @@ _lib.attn_fwd_ext.argtypes = ([_P] * 6 + [_I64] * 7 + [_E, _E, _F, _E, _I64, _I6
                               + [_F, _U64, _U32, _P])
 _lib.attn_fwd_varlen_ext.argtypes = ([_P] * 8 + [_I64] * 9 + [_E, _F, _E, _I64, _I64, _P, _P]
                                      + [_F, _U64, _U32, _P])
+_lib.attn_fwd_route.argtypes = [_I64] * 7 + [_E, _E, _E, _P, _F, ctypes.c_int32]
+_lib.attn_fwd_route.restype = ctypes.c_int32
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
 _lib.mha_workspace_bytes.argtypes = [_I64] * 3 + [_E]
@@ -106,8 +110,9 @@ def _host_ints(x):
     return None
 
 
-def _check_cu(cu, B, T, name):
-    """Cumulative END offsets: B entries, non-decreasing from >= 0, last = T."""
+def _check_cu(cu, B, T, max_len, name):
+    """Cumulative END offsets: B entries, non-decreasing from >= 0, last = T, and no
+    sequence longer than max_len (the kernels cover max_len rows of each sequence)."""
     h = _host_ints(cu)
     if h is None:
         return
@@ -115,6 +120,10 @@ def _check_cu(cu, B, T, name):
     if len(h) < B or (B and (h[0] < 0 or np.any(np.diff(h[:B]) < 0) or h[B - 1] != T)):
         raise ValueError(f"{name}: cumulative lengths must be {B} non-decreasing end offsets "
                          f"ending at {T}")
+    longest = int(np.max(np.diff(np.concatenate([[0], h[:B]])))) if B else 0
+    if longest > max_len:
+        raise ValueError(f"{name}: a sequence of {longest} rows exceeds the max_seqlen "
+                         f"argument {max_len}")
 
 
 def _check_csr(offset, columns, nnz, B, N, S):
@@ -153,8 +162,8 @@ def attn_fwd_varlen(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu_seq
                     B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask,
                     pre_tokens=0, next_tokens=0, stream=None):
     if _metadata_checks():
-        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
-        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
+        _check_cu(cu_seqlens_q, B, Tq, max_seqlen_q, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, max_seqlen_kv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                 _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
                                 B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D,
@@ -177,8 +186,8 @@ def attn_fwd_varlen_update(q, k, v, prev_out, prev_max, prev_sum, out, out_max, 
                            max_seqlen_kv, Nq, Nkv, D, dtype, scale, mask, pre_tokens=0,
                            next_tokens=0, stream=None):
     if _metadata_checks():
-        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
-        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
+        _check_cu(cu_seqlens_q, B, Tq, max_seqlen_q, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, max_seqlen_kv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen_update(_ptr(q), _ptr(k), _ptr(v), _ptr(prev_out),
                                        _ptr(prev_max), _ptr(prev_sum), _ptr(out), _ptr(out_max),
                                        _ptr(out_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
@@ -203,8 +212,8 @@ def attn_fwd_varlen_ext(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu
                            mask, pre_tokens=0, next_tokens=0, prefix=None, atten_mask=None,
                            dropout_p=0.0, seed=0, offset=0, stream=None):
     if _metadata_checks():
-        _check_cu(cu_seqlens_q, B, Tq, "cu_seqlens_q")
-        _check_cu(cu_seqlens_kv, B, Tkv, "cu_seqlens_kv")
+        _check_cu(cu_seqlens_q, B, Tq, max_seqlen_q, "cu_seqlens_q")
+        _check_cu(cu_seqlens_kv, B, Tkv, max_seqlen_kv, "cu_seqlens_kv")
     _check(_lib.attn_fwd_varlen_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_max),
                                        _ptr(softmax_sum), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
                                        B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv, D, Dv,
@@ -212,6 +221,18 @@ def attn_fwd_varlen_ext(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu
                                        pre_tokens, next_tokens, _ptr(prefix), _ptr(atten_mask),
                                        dropout_p, seed, offset, _stream(stream)),
            "attn_fwd_varlen_ext")
+
+
+def attn_fwd_route(B, Nq, Nkv, Sq, Skv, D, Dv, dtype, layout, mask, atten_mask=None,
+                   dropout_p=0.0, update=False) -> str:
+    """Which kernel a dense forward with these arguments runs on ("tiled" or "general");
+    no HIP call.  Raises MiattnError with the status the forward would return."""
+    r = _lib.attn_fwd_route(B, Nq, Nkv, Sq, Skv, D, Dv, _enum(dtype, DTYPES),
+                            _enum(layout, LAYOUTS), _enum(mask, MASKS), _ptr(atten_mask),
+                            dropout_p, int(bool(update)))
+    if r < 0:
+        raise MiattnError(-r, "attn_fwd_route")
+    return KERNELS[r]
 
 
 def attn_lse_merge(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, out_max,

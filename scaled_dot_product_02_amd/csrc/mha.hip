@@ -113,6 +113,11 @@ miattn_status_t mha_self_attn_fwd(const void* x, const void* w_qkv, const void* 
         return MIATTN_ERR_SHAPE;   // the bias rows and the filled outputs move in 16-byte vectors
     if (!(dropout_p >= 0.f && dropout_p < 1.f)) return MIATTN_ERR_DROPOUT;
     if (dropout_p > 0.f && atten_mask) return MIATTN_ERR_UNSUPPORTED;
+    // every check of the attention call (dropout rounding, head dims, mask and dropout
+    // combination) runs here, before the first launch, so that an error enqueues nothing
+    const int32_t route = attn_fwd_route(B, N, N, S, S, D, D, dtype, MIATTN_BSND,
+                                         MIATTN_MASK_NONE, atten_mask, dropout_p, 0);
+    if (route < 0) return (miattn_status_t)(-route);
 
     const hipStream_t st = (hipStream_t)stream;
     const int64_t M = B * S, plane = M * E * eb;

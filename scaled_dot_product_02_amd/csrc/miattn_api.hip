@@ -10,6 +10,8 @@ using namespace miattn;
 namespace {
 
 constexpr int64_t kTokensClamp = int64_t(1) << 40;  // |pre|, |next| beyond this change nothing
+// Longest dense sequence: positions, tile bounds and key indices are 32-bit in the kernels
+constexpr int64_t kMaxLen = int64_t(1) << 30;
 
 struct Strides { int64_t sb, ss, sh; };
 
@@ -111,14 +113,26 @@ miattn_status_t size_grid(FaParams& p, int64_t max_len_q, int tile_m)
     return MIATTN_OK;
 }
 
-miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
+// Whether a validated forward runs on the tiled MFMA kernel (else the general one).
+bool use_tiled(const FaParams& p, int dtype, int64_t D)
 {
     // an explicit mask stays on the tiled kernel when its rows are 4-byte aligned words
     // (read as 32-bit buffer loads with 32-bit offsets); otherwise it takes the general one
     const bool mask_words = !p.amask || ((uintptr_t)p.amask % 4 == 0 && p.amask_ld % 4 == 0 &&
                                          (int64_t)p.Sq * p.amask_ld < (int64_t(1) << 31));
-    const bool tiled = mask_words && tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr,
-                                                   p.amask != nullptr, p.drop_thr != 0);
+    // the tiled kernel addresses a key tile through a buffer descriptor whose byte range
+    // (64 rows of K or V) and per-lane offsets are 32-bit; larger row strides (the SBH
+    // layout with B * Nkv * D >= 2^24 elements) take the general kernel, which indexes in
+    // 64 bits
+    const int64_t esz = dtype == MIATTN_F32 ? 4 : 2;
+    const bool tile_fits = 64 * esz * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (int64_t(1) << 31);
+    return mask_words && tile_fits &&
+           tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr, p.amask != nullptr, p.drop_thr != 0);
+}
+
+miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
+{
+    const bool tiled = use_tiled(p, dtype, D);
     const int tile_m = !tiled ? fa_wide_tile_m(dtype)
                      : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
@@ -156,15 +170,16 @@ const char* miattn_status_str(miattn_status_t s)
 
 namespace {
 
-// Dense forward; with prev_out set, the partial result is merged into the prior.
-miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
-                          const void* prev_out, const float* prev_max, const float* prev_sum,
-                          void* out, float* softmax_max, float* softmax_sum,
-                          int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
-                          int64_t Dv, int dtype, int layout, float scale,
-                          int mask, int64_t pre_tokens, int64_t next_tokens,
-                          const int64_t* prefix, const uint8_t* atten_mask,
-                          float dropout_p, uint64_t seed, uint32_t offset, void* stream)
+// Validation and launch parameters of a dense forward (no HIP call); with prev_out set,
+// the partial result is merged into the prior.
+miattn_status_t prepare_dense(FaParams& p, const void* q, const void* k, const void* v,
+                              const void* prev_out, const float* prev_max, const float* prev_sum,
+                              void* out, float* softmax_max, float* softmax_sum,
+                              int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv,
+                              int64_t D, int64_t Dv, int dtype, int layout, float scale,
+                              int mask, int64_t pre_tokens, int64_t next_tokens,
+                              const int64_t* prefix, const uint8_t* atten_mask,
+                              float dropout_p, uint64_t seed, uint32_t offset)
 {
     if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
     miattn_status_t st = check_dtype_fa(dtype);
@@ -172,9 +187,10 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     if (!layout_ok(layout)) return MIATTN_ERR_LAYOUT;
     if (B < 1 || Nq < 1 || Nkv < 1 || Sq < 1 || Skv < 1 || D < 1) return MIATTN_ERR_SHAPE;
     if (Nq > 256 || Nkv > 256 || D > 768) return MIATTN_ERR_SHAPE;
+    if (Sq > kMaxLen || Skv > kMaxLen) return MIATTN_ERR_SHAPE;
     if (B * Sq > (int64_t(1) << 31) || B * Skv > (int64_t(1) << 31)) return MIATTN_ERR_SHAPE;
     if (Nq % Nkv != 0) return MIATTN_ERR_GQA_RATIO;
-    FaParams p{};
+    p = FaParams{};
     st = check_mask(mask, pre_tokens, next_tokens, p);
     if (st != MIATTN_OK) return st;
     if (prefix && mask != MIATTN_MASK_CAUSAL && mask != MIATTN_MASK_CAUSAL_BR)
@@ -205,6 +221,24 @@ miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
     p.Sq = (int32_t)Sq; p.Skv = (int32_t)Skv;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
+    return MIATTN_OK;
+}
+
+miattn_status_t fwd_dense(const void* q, const void* k, const void* v,
+                          const void* prev_out, const float* prev_max, const float* prev_sum,
+                          void* out, float* softmax_max, float* softmax_sum,
+                          int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                          int64_t Dv, int dtype, int layout, float scale,
+                          int mask, int64_t pre_tokens, int64_t next_tokens,
+                          const int64_t* prefix, const uint8_t* atten_mask,
+                          float dropout_p, uint64_t seed, uint32_t offset, void* stream)
+{
+    FaParams p;
+    const miattn_status_t st = prepare_dense(p, q, k, v, prev_out, prev_max, prev_sum, out,
+                                             softmax_max, softmax_sum, B, Nq, Nkv, Sq, Skv, D, Dv,
+                                             dtype, layout, scale, mask, pre_tokens, next_tokens,
+                                             prefix, atten_mask, dropout_p, seed, offset);
+    if (st != MIATTN_OK) return st;
     return launch_fa(p, dtype, D, (hipStream_t)stream, Sq);
 }
 
@@ -353,6 +387,24 @@ miattn_status_t attn_fwd_varlen_ext(const void* q, const void* k, const void* v,
                       cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, max_seqlen_q, max_seqlen_kv, Nq, Nkv,
                       D, Dv, dtype, scale, mask, pre_tokens, next_tokens, prefix, atten_mask,
                       dropout_p, seed, offset, stream);
+}
+
+int32_t attn_fwd_route(int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
+                       int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout,
+                       miattn_mask_t mask, const uint8_t* atten_mask, float dropout_p,
+                       int32_t update)
+{
+    // the same validation and routing as attn_fwd_ext / attn_fwd_update; the data pointers
+    // are stand-ins that are never dereferenced
+    char dummy[16];
+    float* fs = (float*)dummy;
+    FaParams p;
+    const miattn_status_t st = prepare_dense(
+        p, dummy, dummy, dummy, update ? dummy : nullptr, update ? fs : nullptr,
+        update ? fs : nullptr, dummy, fs, fs, B, Nq, Nkv, Sq, Skv, D, Dv, dtype, layout, 1.f,
+        mask, 0, 0, nullptr, atten_mask, dropout_p, 0, 0);
+    if (st != MIATTN_OK) return -(int32_t)st;
+    return use_tiled(p, dtype, D) ? MIATTN_KERNEL_TILED : MIATTN_KERNEL_GENERAL;
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

@@ -23,8 +23,9 @@ def _declared():
 def test_header_declares_every_entry_point():
     d = _declared()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
-                 "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_lse_merge", "sparse_csr_attn",
-                 "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str"):
+                 "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
+                 "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd",
+                 "miattn_status_str"):
         assert name in d, d
 
 
@@ -97,6 +98,41 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, scale=float("nan")) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, scale=float("inf")) == "MIATTN_ERR_SCALE"
     assert _fwd(mi, D=0) == "MIATTN_ERR_SHAPE"
+    assert _fwd(mi, Sq=1 << 31) == "MIATTN_ERR_SHAPE"          # positions are 32-bit inside
+    assert _fwd(mi, Skv=(1 << 30) + 1) == "MIATTN_ERR_SHAPE"
+
+
+def test_attn_fwd_route_large_sbh_stride(mi):
+    """The tiled kernel addresses a 64-key tile with 32-bit buffer offsets; a K / V row
+    stride of 64 x stride x 2 bytes >= 2^31 (SBH with B * Nkv * D >= 2^24 in bf16) must take
+    the 64-bit general kernel, not a wrapped descriptor."""
+    r = mi.attn_fwd_route
+    # S 64, B 16384, N 8, D 128 SBH: row stride 2^24 elements = 2^25 bytes; 64 rows = 2^31
+    assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "general"
+    assert r(16384, 8, 8, 64, 64, 128, 128, "f16", "SBH", "none") == "general"
+    assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "none", update=True) == "general"
+    # one batch entry fewer stays below the bound: the tiled kernel
+    assert r(16383, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "tiled"
+    # the same sizes in the other layouts keep small row strides
+    for lay in ("BNSD", "BSND", "BSH"):
+        assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", lay, "causal") == "tiled"
+    # GQA: the K / V stride counts the kv heads only
+    assert r(16384, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "general"
+    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "tiled"
+    # other routes: fp32 and head dims outside the tiled set, mask tensors by alignment
+    assert r(1, 4, 4, 100, 100, 128, 128, "f32", "BNSD", "none") == "general"
+    assert r(1, 4, 4, 100, 100, 80, 80, "bf16", "BNSD", "none") == "general"
+    assert r(1, 4, 4, 100, 100, 256, 256, "bf16", "BNSD", "causal") == "tiled"
+    assert r(1, 4, 4, 100, 128, 128, 128, "bf16", "BNSD", "causal", atten_mask=P) == "tiled"
+    assert r(1, 4, 4, 100, 130, 128, 128, "bf16", "BNSD", "causal", atten_mask=P) == "general"
+    assert r(1, 4, 4, 100, 128, 128, 128, "bf16", "BNSD", "causal", atten_mask=P + 1) == "general"
+    # invalid arguments report the forward's status
+    with pytest.raises(mi.MiattnError) as e:
+        r(1, 6, 4, 100, 100, 128, 128, "bf16", "BNSD", "none")
+    assert mi.STATUS[e.value.status] == "MIATTN_ERR_GQA_RATIO"
+    with pytest.raises(mi.MiattnError) as e:
+        r(1, 4, 4, 1 << 31, 100, 128, 128, "bf16", "BNSD", "none")
+    assert mi.STATUS[e.value.status] == "MIATTN_ERR_SHAPE"
 
 
 def _varlen(mi, **kw):
@@ -282,6 +318,8 @@ def test_mha_self_attn_fwd_validation(mi):
     assert call(out=P + 2) == "MIATTN_ERR_SHAPE"    # not 16-byte aligned
     assert call(bq=P + 8) == "MIATTN_ERR_SHAPE"
     assert call(p=1.0) == "MIATTN_ERR_DROPOUT"
+    assert call(p=0.999) == "MIATTN_ERR_DROPOUT"    # in [0, 1) but rounds to 256/256: rejected
+                                                    # before the projections are enqueued
     assert call(p=0.1, mask=P) == "MIATTN_ERR_UNSUPPORTED"   # dropout with a mask tensor
 
 
@@ -302,6 +340,16 @@ def test_host_metadata_checks(mi, monkeypatch):
         with pytest.raises(ValueError):
             mi.attn_fwd_varlen(P, P, P, P, None, None, cu, cu, 3, 6, 6, 4, 4, 2, 2, 64, "bf16",
                                0.1, "causal", stream=0)
+    cu = torch.tensor([3, 4, 6], dtype=torch.int64)           # valid, longest sequence 3
+    with pytest.raises(ValueError, match="max_seqlen"):
+        mi.attn_fwd_varlen(P, P, P, P, None, None, cu, cu, 3, 6, 6, 2, 3, 2, 2, 64, "bf16",
+                           0.1, "causal", stream=0)
+    with pytest.raises(ValueError, match="max_seqlen"):
+        mi.attn_fwd_varlen_ext(P, P, P, P, None, None, cu, cu, 3, 6, 6, 3, 2, 2, 2, 64, 64,
+                               "bf16", 0.1, "causal", stream=0)
+    with pytest.raises(ValueError, match="max_seqlen"):
+        mi.attn_fwd_varlen_update(P, P, P, P, P, P, P, P, P, cu, cu, 3, 6, 6, 2, 2, 2, 2, 64,
+                                  "bf16", 0.1, "causal", stream=0)
     off = torch.tensor([[[0, 2, 1, 3]]], dtype=torch.int32)  # non-decreasing violated
     col = torch.zeros((1, 1, 4), dtype=torch.int32)
     with pytest.raises(ValueError):

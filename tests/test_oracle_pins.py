@@ -451,15 +451,18 @@ def test_merge_closed_forms_on_random_stats():
     out_same, _, _ = oracle.merge(o1, m1, l1, o1, m2, l2)
     ok = np.abs(l) > 1e-3
     assert np.max(np.abs(out_same - o1)[ok]) < 1e-9
+    # the oracle forms the merge through logarithms (log-sum-exp identity), so identities
+    # hold to a few ulp of the values involved rather than bit for bit
     out_eq, m_eq, l_eq = oracle.merge(o1, m1, l1, o2, m1, l2)
-    assert np.max(np.abs(l_eq - (l1 + l2))) < 1e-15
+    assert np.max(np.abs(l_eq - (l1 + l2))) < 1e-13
     lpos1, lpos2 = np.abs(l1) + 0.1, np.abs(l2) + 0.1
     out_eq, _, _ = oracle.merge(o1, m1, lpos1, o2, m1, lpos2)
     want = (lpos1[..., None] * o1 + lpos2[..., None] * o2) / (lpos1 + lpos2)[..., None]
     assert np.max(np.abs(out_eq - want)) < 1e-12
     empty_m, empty_l = np.full((B, N, S), -np.inf), np.zeros((B, N, S))
     o, mm, ll = oracle.merge(o1, m1, lpos1, np.zeros_like(o2), empty_m, empty_l)
-    assert np.array_equal(o, o1) and np.array_equal(mm, m1) and np.array_equal(ll, lpos1)
+    assert np.array_equal(o, o1) and np.array_equal(mm, m1)
+    assert np.max(np.abs(ll / lpos1 - 1)) < 8 * 2.0 ** -52
     o, mm, ll = oracle.merge(o1, empty_m, empty_l, o2, empty_m, empty_l)
     assert np.all(o == 0) and np.all(mm == -np.inf) and np.all(ll == 0)
 
@@ -528,8 +531,10 @@ def test_update_with_empty_prior_is_plain_attention():
     want = oracle.attn(q, k, v, 0.7, "band", 2, 1)
     got = oracle.attn_update(q, k, v, np.zeros_like(q), np.full((1, 2, 9), -np.inf),
                              np.zeros((1, 2, 9)), 0.7, "band", 2, 1)
-    for g, w in zip(got, want):
-        assert np.array_equal(g, w)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    ok = want[2] > 0   # the sum passes through log and exp: a few ulp
+    assert np.array_equal(got[2][~ok], want[2][~ok])
+    assert np.max(np.abs(got[2][ok] / want[2][ok] - 1)) < 8 * 2.0 ** -52
 
 
 # ------------------------------------------------------------------------------------
