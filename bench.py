@@ -7,6 +7,8 @@ fp32 accumulation, causal per sequence, all inputs resident in HBM before timing
 The metric counts 4 * D * Nq * (visible (query, key) pairs) flops per step.
 
 Also measured in the same run (reported under "secondary"):
+  * the two small dense workloads: fp32 BNSD [1, 1, 128, 64] and bf16 BNSD [8, 8, 128, 64]
+    (the SDPA blog's test shape), no mask; both are launch-latency bound;
   * the same forward with fp16 storage (same lengths and draws; 2.5 PFLOP/s fp16 peak);
   * the same forward with bottom-right causal plus a prefix of L/3 keys per sequence;
   * the same forward with dropout 0.1 on the probabilities;
@@ -29,7 +31,9 @@ measured_peaks: the dense bf16 MFMA rate of the chip and the bandwidth of a plai
 roofline also states its fraction of the measured ceiling beside the datasheet one.
 
 cpu_baseline: the CPU fp64 oracle (untuned) on a bounded sample of the same workload
-(all sequences, the first --cpu-heads query heads), timed on this host's cores.
+(all sequences, the first --cpu-heads query heads), timed on this host's cores; under
+"per_workload" the oracle timed on each of the other workloads (the small dense ones also
+on one thread), with the CPU model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -48,7 +52,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector ALUs and matrix cores alike)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (packed vector ALUs and matrix cores alike)
+PEAK_F32_VALU_TFLOPS = 78.6  # fp32 vector ALUs without packed instructions (not built here)
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
 PROBES_LIB = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn_probes.so")
 PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_varlen_causal_gqa_t33064_pmc.json")
@@ -86,7 +91,21 @@ def load_probes():
     lib.miattn_probe_mfma_bf16_flops.argtypes = [I32, I32]
     lib.miattn_probe_mfma_bf16_flops.restype = I64
     lib.miattn_probe_stream_r2w1.argtypes = [P, P, P, I64, P]
+    lib.miattn_probe_l2_gather.argtypes = [P, I32, I32, I32, P, P]
+    lib.miattn_probe_l2_gather_bytes.argtypes = [I32, I32]
+    lib.miattn_probe_l2_gather_bytes.restype = I64
     return lib
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_launches(fn, steps: int, warmup: int, stream):
@@ -102,6 +121,56 @@ def time_launches(fn, steps: int, warmup: int, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per launch
+
+
+def cpu_baselines(oracle, synthetic, threads: int) -> dict:
+    """The oracle (as it stands) timed on each workload other than the metric one: the two
+    small dense ones whole (also on one thread), the ring merge whole plus its full causal
+    forward on a sample of heads, and the CSR workload whole."""
+    import numpy as np
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    res = {}
+    for wname, dt_ in (("dense_f32_b1n1s128d64", "f32"), ("dense_bf16_b8n8s128d64", "bf16")):
+        w = synthetic.make(wname)
+        qv, kv, vv = (synthetic.storage_values(w[x], dt_) for x in ("q", "k", "v"))
+        fl = 4.0 * w["B"] * w["Nq"] * w["Sq"] * w["Skv"] * w["D"]
+        t1 = min(timed(lambda: oracle.attn(qv, kv, vv, 1 / math.sqrt(w["D"]), "none", threads=1))
+                 for _ in range(3))
+        tn = min(timed(lambda: oracle.attn(qv, kv, vv, 1 / math.sqrt(w["D"]), "none",
+                                           threads=threads)) for _ in range(3))
+        res[wname] = {"flop": fl, "seconds_1_thread": round(t1, 6),
+                      f"seconds_{threads}_threads": round(tn, 6),
+                      "tflops_1_thread": round(fl / t1 / 1e12, 6),
+                      f"tflops_{threads}_threads": round(fl / tn / 1e12, 6)}
+    # ring merge: the merge of two partials over all of S 8192, N 32, D 128 (random partials
+    # of that shape), and the full causal forward over the first 4 of 32 heads
+    rng = np.random.default_rng(0)
+    S, N, Dm = 8192, 32, 128
+    o1, o2 = (rng.standard_normal((1, N, S, Dm)) for _ in range(2))
+    m1, m2 = (rng.standard_normal((1, N, S)) for _ in range(2))
+    l1, l2 = (rng.uniform(1, 100, (1, N, S)) for _ in range(2))
+    tm = timed(lambda: oracle.merge(o1, m1, l1, o2, m2, l2, threads=threads))
+    mbytes = 3 * S * N * Dm * 2 + 6 * N * S * 4
+    hs = 4
+    qf, kf, vf = (rng.standard_normal((1, hs, S, Dm)) for _ in range(3))
+    tf = timed(lambda: oracle.attn(qf, kf, vf, 1 / math.sqrt(Dm), "causal", threads=threads))
+    ffl = 4.0 * Dm * hs * (S * (S + 1) // 2)
+    res["ring_merge_sbh_bf16_s8192_n32_d128"] = {
+        "merge_seconds": round(tm, 4), "merge_gbs_of_bf16_bytes": round(mbytes / tm / 1e9, 3),
+        "causal_forward_sample": f"heads 0..{hs - 1} of {N}", "forward_flop": ffl,
+        "forward_seconds": round(tf, 3), "forward_tflops": round(ffl / tf / 1e12, 5)}
+    ws = synthetic.make("csr_sparse_f32_b2n8s4096d64")
+    sfl = 4.0 * ws["B"] * ws["N"] * ws["nnz"] * ws["D"]
+    ts = timed(lambda: oracle.sparse(ws["q"], ws["k"], ws["v"], ws["offset"], ws["columns"],
+                                     1 / math.sqrt(ws["D"]), threads=threads))
+    res["csr_sparse_f32_b2n8s4096d64"] = {"flop": sfl, "seconds": round(ts, 4),
+                                          "tflops": round(sfl / ts / 1e12, 5)}
+    return res
 
 
 def main():
@@ -219,6 +288,44 @@ def main():
     # ---------------- secondary: fp16 forward, merge and sparse ----------------
     if not args.no_secondary:
         sec = {}
+        # the two small dense workloads (fp32 [1, 1, 128, 64] on the fp32 matrix-core path,
+        # bf16 [8, 8, 128, 64] on the tiled kernel): far too small to fill the chip, so the
+        # time per launch is launch latency; also timed as a captured graph of 100 launches
+        for wname, dt_, peak in (("dense_f32_b1n1s128d64", "f32", PEAK_F32_TFLOPS),
+                                 ("dense_bf16_b8n8s128d64", "bf16", PEAK_BF16_TFLOPS)):
+            ws_ = synthetic.make(wname)
+            sB, sN, sS, sD = ws_["B"], ws_["Nq"], ws_["Sq"], ws_["D"]
+            tq, tk, tv = up(ws_["q"], dt_), up(ws_["k"], dt_), up(ws_["v"], dt_)
+            to = torch.empty_like(tq)
+            tm = torch.empty((sB, sN, sS), dtype=torch.float32, device=dev)
+            tl = torch.empty_like(tm)
+            sflop = 4.0 * sB * sN * sS * sS * sD
+
+            def small_step(tq=tq, tk=tk, tv=tv, to=to, tm=tm, tl=tl, sB=sB, sN=sN, sS=sS, sD=sD,
+                           dt_=dt_):
+                mi.attn_fwd(tq, tk, tv, to, tm, tl, sB, sN, sN, sS, sS, sD, dt_, "BNSD",
+                            1 / math.sqrt(sD), "none", 0, 0, stream.cuda_stream)
+
+            sms_ = time_launches(small_step, 200, 20, stream)
+            gstream = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(gstream):
+                small_step()   # settles the stream before capture
+                gstream.synchronize()
+                with torch.cuda.graph(graph, stream=gstream):
+                    for _ in range(100):
+                        mi.attn_fwd(tq, tk, tv, to, tm, tl, sB, sN, sN, sS, sS, sD, dt_, "BNSD",
+                                    1 / math.sqrt(sD), "none", 0, 0, gstream.cuda_stream)
+            gms_ = time_launches(graph.replay, 10, 2, stream) / 100
+            stf_ = sflop / (gms_ * 1e-3) / 1e12
+            sec[wname] = {
+                "workload": wname, "flop_per_launch": sflop,
+                "us_per_launch": round(sms_ * 1e3, 2),
+                "us_per_launch_in_graph": round(gms_ * 1e3, 2),
+                "roofline": {"bound": "latency", "achieved": round(stf_, 3), "peak": peak,
+                             "unit": "TFLOP/s", "frac": round(stf_ / peak, 5)}}
+            del graph, tq, tk, tv, to, tm, tl
+
         wh = synthetic.varlen_inputs(0, Nq, Nkv, D, "f16", B=B)   # same lengths, fp16 storage
         hq, hk, hv = (torch.from_numpy(np.ascontiguousarray(wh[x]).view(np.float16)).to(dev)
                       for x in ("q", "k", "v"))
@@ -401,11 +508,42 @@ def main():
         sflops = 4.0 * sB * sN * nnz * sD
         sbytes = 4 * 4 * sB * sN * sS * sD + 4 * sB * sN * (nnz + sS + 1)
         stf = sflops / (sms * 1e-3) / 1e12
+
+        # measured ceiling of the sparse kernel's access: random 256-byte row gathers from a
+        # 2 MiB region per XCD (the K and V of one (b, n) slice in fp32), held in L2
+        rows_log2 = 13   # 8192 rows of 256 B = 2 MiB per region
+        gtab = torch.randint(0, 1 << 30, (8 << rows_log2, 64), dtype=torch.int32, device=dev)
+        gblocks, giters = 8 * torch.cuda.get_device_properties(0).multi_processor_count, 512
+        gout = torch.empty(gblocks * 256, dtype=torch.int32, device=dev)
+
+        def gather_probe():
+            rc = probes.miattn_probe_l2_gather(gtab.data_ptr(), rows_log2, gblocks, giters,
+                                               gout.data_ptr(), stream.cuda_stream)
+            if rc:
+                raise RuntimeError(f"gather probe launch failed ({rc})")
+
+        gpms = time_launches(gather_probe, 10, 3, stream)
+        gather_gbs = probes.miattn_probe_l2_gather_bytes(gblocks, giters) / (gpms * 1e-3) / 1e9
+        result["measured_peaks"]["l2_gather_gbs"] = round(gather_gbs, 1)
+        result["measured_peaks"]["l2_gather_method"] = (
+            f"{gblocks} workgroups x 4 waves, random 256-byte rows (16 B a lane) from 2 MiB per "
+            "XCD, 8 rows in flight per 16 lanes")
+        del gtab, gout
+
+        def sparse_roofline(seconds, elem):
+            # every stored entry gathers one K row and one V row of D elements
+            gathered = 2.0 * sB * sN * nnz * sD * elem
+            ach = gathered / seconds / 1e9
+            return {"bound": "l2_gather", "achieved": round(ach, 1), "peak": round(gather_gbs, 1),
+                    "unit": "GB/s", "frac": round(ach / gather_gbs, 4),
+                    "gathered_bytes": gathered}
+
         sec["sparse_csr_attn"] = {
             "workload": "csr_sparse_f32_b2n8s4096d64", "us_per_launch": round(sms * 1e3, 2),
             "tflops": round(stf, 3), "gbs_algorithmic": round(sbytes / (sms * 1e-3) / 1e9, 1),
-            "roofline": {"bound": "alu", "achieved": round(stf, 3), "peak": PEAK_F32_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(stf / PEAK_F32_TFLOPS, 4)}}
+            "roofline": sparse_roofline(sms * 1e-3, 4),
+            "alu": {"achieved": round(stf, 3), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(stf / PEAK_F32_VALU_TFLOPS, 4)}}
         # the same CSR workload with fp64 inputs and arithmetic
         wd = synthetic.sparse_inputs(0, sB, sN, sS, sD, band=128, n_random=64, dtype="f64")
         dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(wd[x])).to(dev) for x in ("q", "k", "v"))
@@ -420,8 +558,9 @@ def main():
         sec["sparse_csr_attn_f64"] = {
             "workload": "csr_sparse_f64_b2n8s4096d64", "us_per_launch": round(dms * 1e3, 2),
             "tflops": round(dtf, 3),
-            "roofline": {"bound": "alu", "achieved": round(dtf, 3), "peak": 78.6,
-                         "unit": "TFLOP/s", "frac": round(dtf / 78.6, 4)}}
+            "roofline": sparse_roofline(dms * 1e-3, 8),
+            "alu": {"achieved": round(dtf, 3), "peak": 78.6, "unit": "TFLOP/s",
+                    "frac": round(dtf / 78.6, 4)}}
 
         # head dim 256 (4-wave workgroups, 32-key tiles): dense causal bf16, S 8192, N 16
         Sd, Nd, Dd = 8192, 16, 256
@@ -535,7 +674,9 @@ def main():
             "value": round(sflops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"all {B} sequences x query heads 0..{hs - 1} of {Nq} "
-                      f"({sflops / 1e9:.1f} GFLOP fp64, {dt:.1f} s wall)"}
+                      f"({sflops / 1e9:.1f} GFLOP fp64, {dt:.1f} s wall)",
+            "cpu_model": cpu_model(),
+            "per_workload": cpu_baselines(oracle, synthetic, threads)}
 
     print(json.dumps(result), flush=True)
 

@@ -4,8 +4,9 @@
  * Measurement aids for the roofline figures of the benchmark, not part of the attention
  * library: the dense bf16 matrix-core rate of the whole chip (back-to-back
  * v_mfma_f32_32x32x16_bf16 on independent accumulators, with random operands: the chip
- * clocks lower on random data than on constant operands) and the bandwidth of a plain
- * streaming pass that reads two arrays and writes one.  The caller times the launches
+ * clocks lower on random data than on constant operands), the bandwidth of a plain
+ * streaming pass that reads two arrays and writes one, and the rate of random 256-byte row
+ * gathers from a table that each XCD's L2 holds (the access of the CSR-sparse kernel).  The caller times the launches
  * (e.g. with events on `stream`); the functions only enqueue work.  All pointers are device
  * pointers owned by the caller.  Each returns 0 on success or the HIP error code.
  */
@@ -28,6 +29,16 @@ int64_t miattn_probe_mfma_bf16_flops(int32_t blocks, int32_t iters);
 /* o[i] = a[i] ^ b[i] over `bytes` bytes (a multiple of 16; 16-byte aligned pointers), with
  * non-temporal 16-byte loads and stores: 3 * bytes of HBM traffic. */
 int miattn_probe_stream_r2w1(const void* a, const void* b, void* o, int64_t bytes, void* stream);
+
+/* Random row gathers: table holds 8 regions (one per XCD) of 2^rows_log2 rows of 256 bytes
+ * (8 * 2^rows_log2 * 256 bytes, 16-byte aligned; 1 <= rows_log2 <= 20); workgroup b reads
+ * region b % 8.  blocks of 256 threads; iters (a multiple of 8) 16-byte loads per thread,
+ * one 256-byte row per 16 lanes per step.  out: uint32 [blocks * 256]. */
+int miattn_probe_l2_gather(const void* table, int32_t rows_log2, int32_t blocks, int32_t iters,
+                           uint32_t* out, void* stream);
+
+/* bytes gathered by one miattn_probe_l2_gather launch: blocks * 256 * iters * 16. */
+int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
 // Peak probes of the running GPU, declared in include/miattn_probes.h: the dense bf16 MFMA
-// rate of the chip and the bandwidth of a plain 2-read / 1-write stream.  They give the
-// benchmark measured ceilings beside the datasheet ones.
+// rate of the chip, the bandwidth of a plain 2-read / 1-write stream, and the rate of
+// random 256-byte row gathers from an L2-resident table.  They give the benchmark measured
+// ceilings beside the datasheet ones.
 #include <hip/hip_runtime.h>
 
 #include "miattn_probes.h"
@@ -68,6 +69,29 @@ __global__ __launch_bounds__(kThreads) void stream_r2w1(const u32x4* a, const u3
         __builtin_nontemporal_store(__builtin_nontemporal_load(a + i) ^ __builtin_nontemporal_load(b + i), o + i);
 }
 
+// Random 256-byte row gathers from a table resident in L2: workgroup b reads region b % 8
+// (the XCD that the round-robin dispatch places it on), 2^rows_log2 rows of 256 bytes.
+// Each group of 16 lanes fetches one row per step (16 bytes a lane), eight rows in flight
+// per group before any is used, like the dependent gathers of a CSR row.
+__global__ __launch_bounds__(kThreads) void l2_gather(const u32x4* table, int rows_log2, int iters,
+                                                      unsigned* out)
+{
+    const unsigned mask = (1u << rows_log2) - 1u;
+    const u32x4* base = table + ((int64_t)(blockIdx.x & 7) << rows_log2) * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 15;
+    const unsigned key = ((blockIdx.x * (kThreads / 64) + wave) * 4u + (lane >> 4)) * 0x9e3779b9u;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < iters; i += 8) {
+        u32x4 x[8];
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = base[(int64_t)(mix32(key + (unsigned)(i + u)) & mask) * 16 + sub];
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= x[u];
+    }
+    out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +116,22 @@ int miattn_probe_stream_r2w1(const void* a, const void* b, void* o, int64_t byte
     hipLaunchKernelGGL(stream_r2w1, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                        (hipStream_t)stream, (const u32x4*)a, (const u32x4*)b, (u32x4*)o, n);
     return (int)hipGetLastError();
+}
+
+int miattn_probe_l2_gather(const void* table, int32_t rows_log2, int32_t blocks, int32_t iters,
+                           uint32_t* out, void* stream)
+{
+    if (!table || !out || rows_log2 < 1 || rows_log2 > 20 || blocks < 1 || iters < 8 || iters % 8)
+        return (int)hipErrorInvalidValue;
+    if ((uintptr_t)table % 16) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(l2_gather, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4*)table, rows_log2, iters, (unsigned*)out);
+    return (int)hipGetLastError();
+}
+
+int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters)
+{
+    return (int64_t)blocks * kThreads * iters * 16;
 }
 
 }  // extern "C"

@@ -81,6 +81,18 @@ def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 LAYOUTS = ("BNSD", "BSND", "BSH", "SBH")
 
 
+def device_normal(shape, seed: int, dtype: str, device: str = "cuda:0"):
+    """N(0, 1) draws made on the device (torch's counter-based generator, seeded), stored in
+    `dtype`: for inputs of several GiB that the host would take long to draw and upload.
+    Returns a torch tensor; its values reach the oracle by reading back the stored bits."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(tdt)
+
+
 def storage_shape(layout: str, B: int, N: int, S: int, D: int):
     if layout == "BNSD":
         return (B, N, S, D)

@@ -42,7 +42,8 @@ def test_probe_library_exports_its_declared_symbols():
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "miattn_probes.h")).read(), flags=re.S)
     declared = set(re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", src, re.M))
     assert declared == {"miattn_probe_mfma_bf16", "miattn_probe_mfma_bf16_flops",
-                        "miattn_probe_stream_r2w1"}
+                        "miattn_probe_stream_r2w1", "miattn_probe_l2_gather",
+                        "miattn_probe_l2_gather_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -55,6 +56,13 @@ def test_probe_library_exports_its_declared_symbols():
     probes.miattn_probe_stream_r2w1.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_void_p]
     assert probes.miattn_probe_stream_r2w1(256, 256, 256, 24, None) != 0   # not a multiple of 16
     assert probes.miattn_probe_stream_r2w1(None, 256, 256, 32, None) != 0
+    probes.miattn_probe_l2_gather_bytes.restype = ctypes.c_int64
+    probes.miattn_probe_l2_gather_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert probes.miattn_probe_l2_gather_bytes(3, 16) == 3 * 256 * 16 * 16
+    probes.miattn_probe_l2_gather.argtypes = ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p])
+    assert probes.miattn_probe_l2_gather(256, 13, 8, 12, 256, None) != 0   # iters % 8
+    assert probes.miattn_probe_l2_gather(256, 21, 8, 16, 256, None) != 0   # rows_log2 > 20
 
 
 @pytest.fixture(scope="module")

@@ -1,7 +1,8 @@
 """GPU parity at the edges of the accepted argument ranges: a packed batch of T = 2^20 tokens
 (the varlen operator's bound of 1M tokens, read as 2^20), the library's largest batch of 2048
-sequences, 256 query heads (the operator's bound on N), and a single-head sequence of 131,072
-keys.  Sampled rows are checked against the oracle, each computed from its own visible keys."""
+sequences, 256 query heads (the operator's bound on N), a single-head sequence of 131,072
+keys, and SBH batches whose row stride crosses the tiled kernel's 32-bit tile range.
+Sampled rows are checked against the oracle, each computed from its own visible keys."""
 import math
 
 import numpy as np
@@ -98,3 +99,29 @@ def test_single_head_131072_keys(mi):
                                  1 / math.sqrt(128), "none")
         check_out(go[:, :, i:i + 1], wo, "bf16", f"row {i}")
         check_stats(gm[:, :, i:i + 1], gl[:, :, i:i + 1], wm, wl)
+
+
+@pytest.mark.parametrize("B,route", [(16383, "tiled"), (32768, "general")])
+def test_sbh_row_stride_beyond_32_bit_tiles(mi, B, route):
+    """SBH bf16, S 64, N 8, D 128: the K / V row stride is B * 1024 elements.  At B 32768 a
+    64-row tile spans 2^32 bytes, past the tiled kernel's 32-bit buffer range, so the call
+    must run on the general kernel (64-bit indexing); just below the bound it stays tiled.
+    Sampled batch entries (every head) against the oracle."""
+    S, N, D = 64, 8, 128
+    assert mi.attn_fwd_route(B, N, N, S, S, D, D, "bf16", "SBH", "causal") == route
+    q = synthetic.device_normal((S, B, N * D), 116, "bf16")
+    k = synthetic.device_normal((S, B, N * D), 117, "bf16")
+    v = synthetic.device_normal((S, B, N * D), 118, "bf16")
+    out = torch.full_like(q, float("nan"))
+    m, l = nan_stats((B, N, S)), nan_stats((B, N, S))
+    scale = 1 / math.sqrt(D)
+    mi.attn_fwd(q, k, v, out, m, l, B, N, N, S, S, D, "bf16", "SBH", scale, "causal")
+    torch.cuda.synchronize()
+    for b in (0, 1, B // 2 + 7, B - 1):
+        # the stored bits of batch entry b, read back: (S, N*D) -> (1, N, S, D)
+        pick = lambda t: host_values(t[:, b]).reshape(S, N, D).transpose(1, 0, 2)[None]
+        wo, wm, wl = oracle.attn(pick(q), pick(k), pick(v), scale, "causal")
+        check_out(pick(out), wo, "bf16", f"batch entry {b}")
+        check_stats(host_values(m[b])[None], host_values(l[b])[None], wm, wl)
+    del q, k, v, out
+    torch.cuda.empty_cache()
