@@ -68,7 +68,8 @@ typedef enum {
     MIATTN_ERR_SCALE = 9,       /* scale is not a finite positive number */
     MIATTN_ERR_DROPOUT = 10,    /* dropout_p is not in [0, 1) (or rounds to 256/256) */
     MIATTN_ERR_BLAS = 11,       /* a rocBLAS call (handle creation or GEMM) failed */
-    MIATTN_ERR_WORKSPACE = 12   /* the workspace is NULL or smaller than required */
+    MIATTN_ERR_WORKSPACE = 12,  /* the workspace is NULL or smaller than required */
+    MIATTN_ERR_SCRATCH = 13     /* larger than the static scratch of a no-allocation entry point */
 } miattn_status_t;
 
 /* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
@@ -344,6 +345,33 @@ miattn_status_t mha_self_attn_fwd(const void* x, const void* w_qkv, const void* 
                                   int64_t B, int64_t S, int64_t E, int64_t N,
                                   miattn_dtype_t dtype, const uint8_t* atten_mask,
                                   float dropout_p, uint64_t seed, uint32_t offset, void* stream);
+
+/*
+ * mha_self_attn_fwd_noalloc - mha_self_attn_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same module and arguments without the workspace; it allocates nothing:
+ *   - q, k, v and the attention output live in a static device array of
+ *     MIATTN_MHA_SCRATCH_BYTES that each GPU the library runs on holds until the process
+ *     ends (the first call on a device only looks up that device's copy);
+ *   - the projections run on this library's own GEMM kernel (fp32 accumulation, the bias
+ *     added in fp32 before the one rounding to the storage type), not rocBLAS, so outputs
+ *     can differ from mha_self_attn_fwd's by the rounding of a different summation order.
+ * Limit: mha_workspace_bytes(B, S, E, dtype) <= MIATTN_MHA_SCRATCH_BYTES, else
+ * MIATTN_ERR_SCRATCH (bf16: B * S * E <= 8 Mi elements).  x, w_qkv, w_out and out must be
+ * 16-byte aligned.  Other arguments, limits and errors as mha_self_attn_fwd; errors are
+ * reported before any work is enqueued, except MIATTN_ERR_LAUNCH.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on a GPU (on
+ * different streams, or from different threads) race and must be serialized by the
+ * caller; nothing in the array needs to start at zero (each call overwrites what it reads).
+ */
+#define MIATTN_MHA_SCRATCH_BYTES (64ll << 20)
+
+miattn_status_t mha_self_attn_fwd_noalloc(const void* x, const void* w_qkv, const void* b_qkv,
+                                          const void* w_out, const void* b_out, void* out,
+                                          int64_t B, int64_t S, int64_t E, int64_t N,
+                                          miattn_dtype_t dtype, const uint8_t* atten_mask,
+                                          float dropout_p, uint64_t seed, uint32_t offset,
+                                          void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* miattn_status_str(miattn_status_t status);

@@ -27,7 +27,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 STATUS = {0: "MIATTN_OK", 1: "MIATTN_ERR_NULL", 2: "MIATTN_ERR_SHAPE", 3: "MIATTN_ERR_DTYPE",
           4: "MIATTN_ERR_LAYOUT", 5: "MIATTN_ERR_GQA_RATIO", 6: "MIATTN_ERR_MASK",
           7: "MIATTN_ERR_UNSUPPORTED", 8: "MIATTN_ERR_LAUNCH", 9: "MIATTN_ERR_SCALE",
-          10: "MIATTN_ERR_DROPOUT", 11: "MIATTN_ERR_BLAS", 12: "MIATTN_ERR_WORKSPACE"}
+          10: "MIATTN_ERR_DROPOUT", 11: "MIATTN_ERR_BLAS", 12: "MIATTN_ERR_WORKSPACE",
+          13: "MIATTN_ERR_SCRATCH"}
+MHA_SCRATCH_BYTES = 64 << 20   # MIATTN_MHA_SCRATCH_BYTES
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
@@ -36,7 +38,8 @@ KERNELS = {1: "tiled", 2: "general"}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
            "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
-           "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd", "miattn_status_str")
+           "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd",
+           "mha_self_attn_fwd_noalloc", "miattn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -62,9 +65,10 @@ _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
 _lib.mha_workspace_bytes.argtypes = [_I64] * 3 + [_E]
 _lib.mha_workspace_bytes.restype = ctypes.c_int64
 _lib.mha_self_attn_fwd.argtypes = [_P] * 7 + [_I64] * 5 + [_E, _P, _F, _U64, _U32, _P]
+_lib.mha_self_attn_fwd_noalloc.argtypes = [_P] * 6 + [_I64] * 4 + [_E, _P, _F, _U64, _U32, _P]
 for _f in (_lib.attn_fwd, _lib.attn_fwd_varlen, _lib.attn_fwd_update, _lib.attn_fwd_varlen_update,
            _lib.attn_fwd_ext, _lib.attn_fwd_varlen_ext, _lib.attn_lse_merge,
-           _lib.sparse_csr_attn, _lib.mha_self_attn_fwd):
+           _lib.sparse_csr_attn, _lib.mha_self_attn_fwd, _lib.mha_self_attn_fwd_noalloc):
     _f.restype = ctypes.c_int
 _lib.miattn_status_str.argtypes = [ctypes.c_int]
 _lib.miattn_status_str.restype = ctypes.c_char_p
@@ -265,6 +269,15 @@ def mha_self_attn_fwd(x, w_qkv, b_qkv, w_out, b_out, out, workspace, workspace_b
                                   _ptr(out), _ptr(workspace), workspace_bytes, B, S, E, N,
                                   _enum(dtype, DTYPES), _ptr(atten_mask), dropout_p, seed,
                                   offset, _stream(stream)), "mha_self_attn_fwd")
+
+
+def mha_self_attn_fwd_noalloc(x, w_qkv, b_qkv, w_out, b_out, out, B, S, E, N, dtype,
+                              atten_mask=None, dropout_p=0.0, seed=0, offset=0, stream=None):
+    _check(_lib.mha_self_attn_fwd_noalloc(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_out),
+                                          _ptr(b_out), _ptr(out), B, S, E, N,
+                                          _enum(dtype, DTYPES), _ptr(atten_mask), dropout_p,
+                                          seed, offset, _stream(stream)),
+           "mha_self_attn_fwd_noalloc")
 
 
 from .mha import MultiHeadAttention  # noqa: E402  (the module form of mha_self_attn_fwd)

@@ -25,7 +25,7 @@ def test_header_declares_every_entry_point():
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
                  "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
                  "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd",
-                 "miattn_status_str"):
+                 "mha_self_attn_fwd_noalloc", "miattn_status_str"):
         assert name in d, d
 
 
@@ -331,8 +331,32 @@ def test_mha_self_attn_fwd_validation(mi):
     assert call(p=0.1, mask=P) == "MIATTN_ERR_UNSUPPORTED"   # dropout with a mask tensor
 
 
+def test_mha_self_attn_fwd_noalloc_validation(mi):
+    def call(**kw):
+        a = dict(x=P, wq=P, bq=P, wo=P, bo=P, out=P, B=2, S=16, E=512, N=8, dtype="bf16",
+                 mask=None, p=0.0)
+        a.update(kw)
+        with pytest.raises(mi.MiattnError) as e:
+            mi.mha_self_attn_fwd_noalloc(a["x"], a["wq"], a["bq"], a["wo"], a["bo"], a["out"],
+                                         a["B"], a["S"], a["E"], a["N"], a["dtype"],
+                                         atten_mask=a["mask"], dropout_p=a["p"], stream=0)
+        return mi.STATUS[e.value.status]
+    assert call(x=None) == "MIATTN_ERR_NULL"
+    assert call(out=None) == "MIATTN_ERR_NULL"
+    assert call(dtype="f64") == "MIATTN_ERR_DTYPE"
+    assert call(N=7) == "MIATTN_ERR_SHAPE"
+    assert call(x=P + 4) == "MIATTN_ERR_SHAPE"       # 16-byte aligned operands
+    assert call(p=0.999) == "MIATTN_ERR_DROPOUT"
+    assert call(p=0.1, mask=P) == "MIATTN_ERR_UNSUPPORTED"
+    # the static scratch holds 4 planes of B*S*E elements: 64 MiB = 8 Mi bf16 elements each
+    # ... of the four planes, i.e. B*S*E <= 8 Mi in bf16 and 4 Mi in fp32
+    assert mi.MHA_SCRATCH_BYTES == 64 << 20
+    assert call(B=1, S=(8 << 20) // 512 + 1) == "MIATTN_ERR_SCRATCH"
+    assert call(B=1, S=(4 << 20) // 512 + 1, dtype="f32") == "MIATTN_ERR_SCRATCH"
+
+
 def test_status_strings(mi):
-    for code in range(13):
+    for code in range(14):
         assert mi.status_str(code) and mi.status_str(code) != "unknown status"
     assert mi.status_str(99) == "unknown status"
 
