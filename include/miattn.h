@@ -84,7 +84,11 @@ typedef enum {
 } miattn_mask_t;
 
 /* Kernels a dense forward may run on (attn_fwd_route). */
-typedef enum { MIATTN_KERNEL_TILED = 1, MIATTN_KERNEL_GENERAL = 2 } miattn_kernel_t;
+typedef enum {
+    MIATTN_KERNEL_TILED = 1,      /* the tiled MFMA kernel, one workgroup per query tile */
+    MIATTN_KERNEL_GENERAL = 2,    /* the head-dim-general kernel */
+    MIATTN_KERNEL_PERSISTENT = 3  /* the tiled kernel's persistent causal form */
+} miattn_kernel_t;
 
 /*
  * attn_fwd - dense attention forward over a batch of equal-length sequences.

@@ -34,7 +34,7 @@ DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "f64": 3}
 LAYOUTS = {"BNSD": 0, "BSND": 1, "BSH": 2, "SBH": 3}
 MASKS = {"none": 0, "causal": 1, "band": 2, "causal_br": 3, "band_br": 4}
 
-KERNELS = {1: "tiled", 2: "general"}
+KERNELS = {1: "tiled", 2: "general", 3: "persistent"}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
            "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
@@ -229,8 +229,9 @@ def attn_fwd_varlen_ext(q, k, v, out, softmax_max, softmax_sum, cu_seqlens_q, cu
 
 def attn_fwd_route(B, Nq, Nkv, Sq, Skv, D, Dv, dtype, layout, mask, atten_mask=None,
                    dropout_p=0.0, update=False) -> str:
-    """Which kernel a dense forward with these arguments runs on ("tiled" or "general");
-    no HIP call.  Raises MiattnError with the status the forward would return."""
+    """Which kernel a dense forward with these arguments runs on ("tiled", "general" or
+    "persistent"); no HIP call.  Raises MiattnError with the status the forward would
+    return."""
     r = _lib.attn_fwd_route(B, Nq, Nkv, Sq, Skv, D, Dv, _enum(dtype, DTYPES),
                             _enum(layout, LAYOUTS), _enum(mask, MASKS), _ptr(atten_mask),
                             dropout_p, int(bool(update)))

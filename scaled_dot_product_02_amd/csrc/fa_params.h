@@ -46,6 +46,7 @@ struct FaParams {
     uint32_t drop_offset;       // fourth counter word
     float scale;                // softmax scale
     float scale_log2;           // scale * log2(e)
+    int32_t persist_hpi;        // persistent kernel: query heads per work item (1, 2, 4, 8)
 };
 
 struct MergeParams {
@@ -82,9 +83,22 @@ hipError_t launch_fa_fwd_bf16(const FaParams& p, int D, bool f16, hipStream_t st
 // the head-dim-general forward: any 1 <= p.Dv <= D <= 768, every dtype and feature; rows per
 // workgroup fa_wide_tile_m(dtype)
 hipError_t launch_fa_fwd_wide(const FaParams& p, int D, int dtype, hipStream_t stream);
+// the persistent causal forward (bf16 / fp16, head dim 64 or 128): p.n_slots workgroups
+// (one per CU) walk the work items; p.persist_hpi = fa_persist_heads_per_item(p.group)
+hipError_t launch_fa_fwd_persist(const FaParams& p, int D, bool f16, hipStream_t stream);
+// query heads of one GQA group that a persistent work item covers: the largest power of two
+// dividing the group size, at most 8
+int fa_persist_heads_per_item(int group);
 int fa_wide_tile_m(int dtype);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream);
+
+// Longest packed batch (sequences) of the persistent kernel, whose workgroups sort the
+// sequence lengths in LDS.
+constexpr int kPersistMaxSeq = 512;
+// the most work items one workgroup of the persistent kernel may own at head dim D (its
+// item records live in LDS)
+int fa_persist_max_items(int D);
 
 // Row tile heights, used by the C-ABI layer to size the grids.
 constexpr int kBf16TileM = 256;

@@ -1,6 +1,9 @@
 // C ABI of the attention-forward library: argument validation, layout strides, grid
 // sizing and launches on the caller's stream.  Declared in include/miattn.h.
 #include <math.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "miattn.h"
 #include "fa_params.h"
@@ -130,9 +133,59 @@ bool use_tiled(const FaParams& p, int dtype, int64_t D)
            tiled_forward(D, p.Dv, dtype, p.prev_out != nullptr, p.amask != nullptr, p.drop_thr != 0);
 }
 
+// Compute units of the current device (the persistent kernel runs one workgroup per CU),
+// queried once per device.
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// MIATTN_PERSIST=0 in the environment turns the persistent kernel off (the tiled kernel
+// then takes its forwards), for comparisons; read at every call.
+bool persist_enabled()
+{
+    const char* e = getenv("MIATTN_PERSIST");
+    return !(e && e[0] == '0' && e[1] == 0);
+}
+
+// Whether a forward that the tiled kernel would serve runs on the persistent one: causal
+// (either alignment) without a prefix, mask tensor, dropout or prior, head dim 64 or 128
+// with V of the same head dim, packed batches of at most kPersistMaxSeq sequences.
+bool use_persistent(const FaParams& p, int64_t D, int64_t Tq, int n_wg)
+{
+    if (D != 64 && D != 128) return false;
+    if (p.Dv != D || p.prev_out || p.amask || p.drop_thr || p.prefix) return false;
+    if (p.pre != kTokensClamp || p.next != 0) return false;
+    if (p.cu_q && p.B > kPersistMaxSeq) return false;
+    // items: sum over sequences of their query tiles, times the head groups; packed
+    // batches have at most Tq / rows + B tiles.  Each workgroup lists its items in LDS.
+    const int64_t hpi = fa_persist_heads_per_item(p.group);
+    const int64_t rows = 256 / hpi;
+    const int64_t tiles = p.cu_q ? (Tq + rows - 1) / rows + p.B : p.B * ((p.Sq + rows - 1) / rows);
+    const int64_t items = tiles * (p.Nq / hpi);
+    if (n_wg < 1 || items >= (int64_t(1) << 30) || (items + n_wg - 1) / n_wg > fa_persist_max_items((int)D))
+        return false;
+    return persist_enabled();
+}
+
 miattn_status_t launch_fa(FaParams& p, int dtype, int64_t D, hipStream_t stream, int64_t max_len_q)
 {
     const bool tiled = use_tiled(p, dtype, D);
+    const int n = tiled ? cu_count() : 0;
+    if (tiled && use_persistent(p, D, p.cu_q ? p.st_sh : 0, n)) {
+        p.persist_hpi = fa_persist_heads_per_item(p.group);
+        p.n_slots = n;
+        return launch_fa_fwd_persist(p, (int)D, dtype == MIATTN_F16, stream) == hipSuccess
+                   ? MIATTN_OK : MIATTN_ERR_LAUNCH;
+    }
     const int tile_m = !tiled ? fa_wide_tile_m(dtype)
                      : fa_four_waves((int)D, p.amask != nullptr || p.drop_thr != 0) ? kBf16TileMBig : kBf16TileM;
     miattn_status_t st = size_grid(p, max_len_q, tile_m);
@@ -405,7 +458,9 @@ int32_t attn_fwd_route(int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t S
         update ? fs : nullptr, dummy, fs, fs, B, Nq, Nkv, Sq, Skv, D, Dv, dtype, layout, 1.f,
         mask, 0, 0, nullptr, atten_mask, dropout_p, 0, 0);
     if (st != MIATTN_OK) return -(int32_t)st;
-    return use_tiled(p, dtype, D) ? MIATTN_KERNEL_TILED : MIATTN_KERNEL_GENERAL;
+    if (!use_tiled(p, dtype, D)) return MIATTN_KERNEL_GENERAL;
+    // the routing is decided for a device of 256 compute units (this query makes no HIP call)
+    return use_persistent(p, D, 0, 256) ? MIATTN_KERNEL_PERSISTENT : MIATTN_KERNEL_TILED;
 }
 
 miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, const float* prev_sum,

@@ -110,6 +110,29 @@ def test_attn_fwd_validation(mi):
     assert _fwd(mi, Skv=(1 << 30) + 1) == "MIATTN_ERR_SHAPE"
 
 
+def test_attn_fwd_route_persistent(mi, monkeypatch):
+    """Causal bf16 / fp16 forwards at head dim 64 or 128 without a prefix, mask tensor,
+    dropout or prior run on the persistent kernel while every workgroup's items fit its
+    LDS list; MIATTN_PERSIST=0 sends them to the tiled kernel."""
+    r = mi.attn_fwd_route
+    for mask in ("causal", "causal_br"):
+        for dt in ("bf16", "f16"):
+            for D in (64, 128):
+                assert r(2, 32, 8, 4096, 4096, D, D, dt, "BNSD", mask) == "persistent"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "none") == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "band") == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 64, "bf16", "BNSD", "causal") == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", dropout_p=0.1) == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", update=True) == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "f32", "BNSD", "causal") == "general"
+    # at most 319 items per workgroup at head dim 128 (256 workgroups): 256 heads of one
+    # kv head each (256-row items) x 319 query tiles fit, 320 do not
+    assert r(1, 256, 256, 319 * 256, 319 * 256, 128, 128, "bf16", "BNSD", "causal") == "persistent"
+    assert r(1, 256, 256, 320 * 256, 320 * 256, 128, 128, "bf16", "BNSD", "causal") == "tiled"
+    monkeypatch.setenv("MIATTN_PERSIST", "0")
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal") == "tiled"
+
+
 def test_attn_fwd_route_large_sbh_stride(mi):
     """The tiled kernel addresses a 64-key tile with 32-bit buffer offsets; a K / V row
     stride of 64 x stride x 2 bytes >= 2^31 (SBH with B * Nkv * D >= 2^24 in bf16) must take
@@ -119,18 +142,19 @@ def test_attn_fwd_route_large_sbh_stride(mi):
     assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "general"
     assert r(16384, 8, 8, 64, 64, 128, 128, "f16", "SBH", "none") == "general"
     assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "none", update=True) == "general"
-    # one batch entry fewer stays below the bound: the tiled kernel
-    assert r(16383, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "tiled"
+    # one batch entry fewer stays below the bound: the tiled kernel (or its persistent form)
+    assert r(16383, 8, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") != "general"
     # the same sizes in the other layouts keep small row strides
     for lay in ("BNSD", "BSND", "BSH"):
-        assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", lay, "causal") == "tiled"
+        assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", lay, "causal") != "general"
     # GQA: the K / V stride counts the kv heads only
     assert r(16384, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "general"
-    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "tiled"
+    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "persistent"
     # other routes: fp32 and head dims outside the tiled set, mask tensors by alignment
     assert r(1, 4, 4, 100, 100, 128, 128, "f32", "BNSD", "none") == "general"
     assert r(1, 4, 4, 100, 100, 80, 80, "bf16", "BNSD", "none") == "general"
     assert r(1, 4, 4, 100, 100, 256, 256, "bf16", "BNSD", "causal") == "tiled"
+    assert r(1, 4, 4, 100, 100, 96, 96, "bf16", "BNSD", "causal") == "tiled"
     assert r(1, 4, 4, 100, 128, 128, 128, "bf16", "BNSD", "causal", atten_mask=P) == "tiled"
     assert r(1, 4, 4, 100, 130, 128, 128, "bf16", "BNSD", "causal", atten_mask=P) == "general"
     assert r(1, 4, 4, 100, 128, 128, 128, "bf16", "BNSD", "causal", atten_mask=P + 1) == "general"

@@ -1,0 +1,173 @@
+"""GPU parity of the persistent causal forward (one workgroup per CU walking a static list of
+work items of R rows x HPI query heads).
+
+Every case runs twice through the C ABI, once on the persistent kernel and once with
+MIATTN_PERSIST=0 on the tiled kernel, and the two results must be identical bit for bit:
+each output row is computed by the same per-row arithmetic in both (the same key tiles in
+the same order, the same lazy rescale), only the grouping of rows into workgroups and the
+schedule differ.  The cases that only this path has (GQA groups packed into one item,
+items that see no key, many sequences, both causal alignments) are also compared with the
+CPU fp64 oracle at the tolerances of tests/gpu_utils.py.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_utils import check_out, check_stats, dev, empty_like_storage, host_values, nan_stats
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mi():
+    import scaled_dot_product_02_amd as m
+    return m
+
+
+def _both(run):
+    """run() on the persistent kernel and on the tiled one."""
+    os.environ.pop("MIATTN_PERSIST", None)
+    a = run()
+    os.environ["MIATTN_PERSIST"] = "0"
+    try:
+        b = run()
+    finally:
+        os.environ.pop("MIATTN_PERSIST", None)
+    return a, b
+
+
+def _varlen_run(mi, w, mask="causal"):
+    dt = w["dtype"]
+    q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
+    cq = torch.from_numpy(w["cu_q"]).to("cuda:0")
+    ck = torch.from_numpy(w["cu_kv"]).to("cuda:0")
+    mq = max(1, int(w["lengths_q"].max()))
+    mk = max(1, int(w["lengths_kv"].max()))
+    scale = 1 / math.sqrt(w["D"])
+
+    def run():
+        out = empty_like_storage(q.shape, dt)
+        m, l = nan_stats((w["Nq"], w["Tq"])), nan_stats((w["Nq"], w["Tq"]))
+        mi.attn_fwd_varlen(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"], mq, mk,
+                           w["Nq"], w["Nkv"], w["D"], dt, scale, mask)
+        torch.cuda.synchronize()
+        return host_values(out), host_values(m), host_values(l)
+    return run
+
+
+def _assert_identical(a, b, what):
+    for x, y, name in zip(a, b, ("out", "softmax_max", "softmax_sum")):
+        assert np.array_equal(x, y, equal_nan=False), f"{what}: {name} differs from the tiled kernel"
+
+
+def _oracle_varlen(w, mask):
+    q, k, v = (synthetic.storage_values(w[x], w["dtype"]) for x in ("q", "k", "v"))
+    if mask == "causal":
+        return oracle.attn_varlen(q, k, v, w["cu_q"], w["cu_kv"], 1 / math.sqrt(w["D"]), "causal")
+    return oracle.attn_varlen_keep(
+        q, k, v, w["cu_q"], w["cu_kv"],
+        lambda b, sq, sk: oracle.keep_band(sq, sk, 1 << 62, 0, "bottom_right"), 1 / math.sqrt(w["D"]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_full_workload_matches_tiled_bit_for_bit(mi, dtype):
+    """The 16-sequence packed causal GQA workload (T = 33,064, Nq 32, Nkv 8, D 128)."""
+    w = synthetic.varlen_inputs(0, Nq=32, Nkv=8, D=128, dtype=dtype, B=16)
+    assert mi.attn_fwd_route(1, 32, 8, 4096, 4096, 128, 128, dtype, "BSND", "causal") == "persistent"
+    a, b = _both(_varlen_run(mi, w))
+    _assert_identical(a, b, f"full workload {dtype}")
+
+
+@pytest.mark.parametrize("Nq,Nkv", [(8, 8), (8, 4), (8, 2), (8, 1), (16, 1), (6, 2), (12, 2), (24, 8)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", ["causal", "causal_br"])
+def test_gqa_packing_against_oracle_and_tiled(mi, Nq, Nkv, D, mask):
+    """GQA ratios 1, 2, 4, 8, 16, 3, 6, 3 (heads per item 1, 2, 4, 8, 8, 1, 2, 1); query and
+    key lengths that differ per sequence, with zeros on either side (items without a key)."""
+    lq = [300, 0, 1, 129, 64, 517, 2, 65, 190]
+    lk = [300, 40, 0, 200, 64, 400, 2, 65, 3]
+    w = synthetic.varlen_inputs(400 + Nq + 10 * Nkv + D, Nq=Nq, Nkv=Nkv, D=D, dtype="bf16",
+                                lengths_q=lq, lengths_kv=lk)
+    a, b = _both(_varlen_run(mi, w, mask))
+    _assert_identical(a, b, f"Nq {Nq} Nkv {Nkv} D {D} {mask}")
+    wo, wm, wl = _oracle_varlen(w, mask)
+    check_out(a[0], wo, "bf16", f"Nq {Nq} Nkv {Nkv} D {D} {mask}")
+    check_stats(a[1], a[2], wm, wl)
+
+
+def test_512_sequences(mi):
+    """The largest packed batch the persistent kernel takes (its workgroups sort the
+    sequence lengths in LDS), lengths 0..300."""
+    rng = np.random.default_rng(410)
+    lengths = rng.integers(0, 301, size=512)
+    w = synthetic.varlen_inputs(411, Nq=4, Nkv=1, D=64, dtype="f16", lengths_q=lengths)
+    a, b = _both(_varlen_run(mi, w))
+    _assert_identical(a, b, "512 sequences")
+    wo, wm, wl = _oracle_varlen(w, "causal")
+    check_out(a[0], wo, "f16")
+    check_stats(a[1], a[2], wm, wl)
+
+
+def test_513_sequences_take_the_tiled_kernel(mi):
+    """One sequence more than the persistent kernel sorts: the tiled kernel serves it, with
+    the same result."""
+    rng = np.random.default_rng(412)
+    lengths = rng.integers(0, 70, size=513)
+    w = synthetic.varlen_inputs(413, Nq=2, Nkv=2, D=128, dtype="bf16", lengths_q=lengths)
+    a, b = _both(_varlen_run(mi, w))
+    _assert_identical(a, b, "513 sequences")
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "SBH", "BSND"])
+@pytest.mark.parametrize("Nq,Nkv", [(4, 4), (8, 2)])
+def test_dense_batches(mi, layout, Nq, Nkv):
+    """Dense causal batches (every sequence the same length): 3 x 700 queries over 700 keys
+    top-left, and 3 x 300 queries over 700 keys bottom-right."""
+    for Sq, Skv, mask in ((700, 700, "causal"), (300, 700, "causal_br")):
+        w = synthetic.dense_inputs(420 + Sq + Nq, 3, Nq, Nkv, Sq, Skv, 128, "bf16", layout)
+        q, k, v = dev(w["q"], "bf16"), dev(w["k"], "bf16"), dev(w["v"], "bf16")
+
+        def run():
+            out = empty_like_storage(q.shape, "bf16")
+            m, l = nan_stats((3, Nq, Sq)), nan_stats((3, Nq, Sq))
+            mi.attn_fwd(q, k, v, out, m, l, 3, Nq, Nkv, Sq, Skv, 128, "bf16", layout,
+                        1 / math.sqrt(128), mask)
+            torch.cuda.synchronize()
+            return host_values(out), host_values(m), host_values(l)
+        a, b = _both(run)
+        _assert_identical(a, b, f"dense {layout} {Sq}x{Skv} {mask}")
+        qo, ko, vo = (synthetic.to_bnsd(synthetic.storage_values(w[x], "bf16"), layout, n)
+                      for x, n in (("q", Nq), ("k", Nkv), ("v", Nkv)))
+        keep = oracle.keep_band(Sq, Skv, 1 << 62, 0, "bottom_right" if mask == "causal_br" else "top_left")
+        wo, wm, wl = oracle.attn_keep(qo, ko, vo, keep, 1 / math.sqrt(128))
+        check_out(synthetic.to_bnsd(a[0], layout, Nq), wo, "bf16", f"dense {layout} {mask}")
+        check_stats(a[1], a[2], wm, wl)
+
+
+def test_stats_may_be_null_and_outputs_stay_in_bounds(mi):
+    """NULL statistics on the persistent path, and canaries around the output buffer."""
+    w = synthetic.varlen_inputs(430, Nq=8, Nkv=2, D=128, dtype="bf16", lengths_q=[333, 64, 1])
+    q, k, v = (dev(w[x], "bf16") for x in ("q", "k", "v"))
+    cq = torch.from_numpy(w["cu_q"]).to("cuda:0")
+    pad = 8192
+    buf = torch.full((q.numel() + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    out = buf[pad:pad + q.numel()].view(q.shape)
+    mi.attn_fwd_varlen(q, k, v, out, None, None, cq, cq, 3, w["Tq"], w["Tq"], 333, 333, 8, 2, 128,
+                       "bf16", 1 / math.sqrt(128), "causal")
+    torch.cuda.synchronize()
+    hb = host_values(buf)
+    assert np.all(hb[:pad] == 7.0) and np.all(hb[pad + q.numel():] == 7.0)
+    wo, _, _ = _oracle_varlen(w, "causal")
+    check_out(host_values(out), wo, "bf16")
+
+
+def test_deterministic(mi):
+    w = synthetic.varlen_inputs(431, Nq=16, Nkv=4, D=128, dtype="bf16", lengths_q=[1000, 333, 77, 2048])
+    run = _varlen_run(mi, w)
+    a, b = run(), run()
+    _assert_identical(a, b, "repeat")
