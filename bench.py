@@ -54,14 +54,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (packed vector ALUs and matrix cores alike)
 PEAK_F32_VALU_TFLOPS = 78.6  # fp32 vector ALUs without packed instructions (not built here)
-KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "fa_fwd_bf16.hip")
 PROBES_LIB = os.path.join(ROOT, "scaled_dot_product_02_amd", "libmiattn_probes.so")
-PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_varlen_causal_gqa_t33064_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_persist_varlen_causal_gqa_t33064_pmc.json")
+# the kernel that serves the metric launch (bf16, D 128, 4 query heads per work item, packed)
+METRIC_KERNEL = "fa_fwd_persist_kernel<128, __bf16, 4, true>"
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("fa_fwd_bf16.hip", "fa_common.h", "fa_params.h"):
+    for name in ("fa_fwd_persist.hip", "fa_mfma.h", "fa_params.h"):
         with open(os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -261,7 +262,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes": alg_bytes,
-                     "kernel": "fa_fwd_bf16_kernel<128, __bf16, false>"},
+                     "kernel": METRIC_KERNEL},
     }
 
     # ---------------- measured ceilings: dense bf16 MFMA rate of the chip ----------------
