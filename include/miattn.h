@@ -55,7 +55,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums below are int-sized.  In C++ they take int as their fixed underlying type, so
+ * that every int a caller passes is a value of the type and the entry points can reject an
+ * unknown one (without a fixed type a C++ enum holds only the range of its enumerators). */
+#ifdef __cplusplus
+#define MIATTN_ENUM enum : int
+#else
+#define MIATTN_ENUM enum
+#endif
+
+typedef MIATTN_ENUM {
     MIATTN_OK = 0,
     MIATTN_ERR_NULL = 1,        /* a required pointer is NULL */
     MIATTN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
@@ -73,9 +82,9 @@ typedef enum {
 } miattn_status_t;
 
 /* MIATTN_F64 is taken by sparse_csr_attn only (the Paddle page lists float32 and float64). */
-typedef enum { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2, MIATTN_F64 = 3 } miattn_dtype_t;
-typedef enum { MIATTN_BNSD = 0, MIATTN_BSND = 1, MIATTN_BSH = 2, MIATTN_SBH = 3 } miattn_layout_t;
-typedef enum {
+typedef MIATTN_ENUM { MIATTN_F32 = 0, MIATTN_BF16 = 1, MIATTN_F16 = 2, MIATTN_F64 = 3 } miattn_dtype_t;
+typedef MIATTN_ENUM { MIATTN_BNSD = 0, MIATTN_BSND = 1, MIATTN_BSH = 2, MIATTN_SBH = 3 } miattn_layout_t;
+typedef MIATTN_ENUM {
     MIATTN_MASK_NONE = 0,
     MIATTN_MASK_CAUSAL = 1,
     MIATTN_MASK_BAND = 2,
@@ -84,7 +93,7 @@ typedef enum {
 } miattn_mask_t;
 
 /* Kernels a dense forward may run on (attn_fwd_route). */
-typedef enum {
+typedef MIATTN_ENUM {
     MIATTN_KERNEL_TILED = 1,      /* the tiled MFMA kernel, one workgroup per query tile */
     MIATTN_KERNEL_GENERAL = 2,    /* the head-dim-general kernel */
     MIATTN_KERNEL_PERSISTENT = 3  /* the tiled kernel's persistent causal form */

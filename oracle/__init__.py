@@ -18,7 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c to load (the sanitizer build of the CPU test run)
+_BUILT = os.path.join(_HERE, "liboracle.so")
+_LIB = os.environ.get("ORACLE_LIB") or _BUILT
 
 MASKS = {"none": 0, "causal": 1, "band": 2}
 _lib = None
@@ -27,10 +29,10 @@ _lib = None
 def build() -> str:
     """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-           "-o", _LIB + ".tmp", _SRC, "-lm"]
+           "-o", _BUILT + ".tmp", _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(_BUILT + ".tmp", _BUILT)
+    return _BUILT
 
 
 def _load():
@@ -38,6 +40,8 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB):
+        if "ORACLE_LIB" in os.environ:
+            raise ImportError(f"ORACLE_LIB={_LIB} does not exist")
         build()
     lib = ctypes.CDLL(_LIB)
     P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double

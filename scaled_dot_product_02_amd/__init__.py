@@ -7,7 +7,8 @@ integers or None; enum arguments accept the C values or their names ("bf16", "SB
 MiattnError.  All computation runs in the HIP kernels of libmiattn.so; there is no
 fallback: importing this package fails if the library has not been built.  With
 MIATTN_CHECK=1 the device metadata (cumulative lengths, CSR rows) is copied back and
-validated before the call (a debugging aid that synchronizes).
+validated before the call (a debugging aid that synchronizes).  MIATTN_LIB names another
+build of the same library to load (the sanitizer build of the CPU test run).
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmiattn.so")
+LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_HERE, "libmiattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

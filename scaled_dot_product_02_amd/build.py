@@ -36,10 +36,17 @@ def _run(cmd, what: str, verbose: bool) -> None:
         raise RuntimeError(f"hipcc failed building {what}")
 
 
-def _hipcc(out: str, srcs, verbose: bool, libs=()) -> None:
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host pass only (the device code is
+# built exactly as in the normal library); the runtime is clang's shared one.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _hipcc(out: str, srcs, verbose: bool, libs=(), extra=(), link_extra=()) -> None:
     """Compile each source to an object in parallel, then link the shared library."""
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-             "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS]
+             "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra]
     with tempfile.TemporaryDirectory(prefix="miattn_build_") as tmp:
         objs = [os.path.join(tmp, f"{i}_{os.path.basename(src)}.o") for i, src in enumerate(srcs)]
         jobs = [([HIPCC, *flags, "-c", "-o", o, src], os.path.basename(src))
@@ -48,7 +55,8 @@ def _hipcc(out: str, srcs, verbose: bool, libs=()) -> None:
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
             for f in [pool.submit(_run, cmd, what, verbose) for cmd, what in jobs]:
                 f.result()
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp", *objs, *libs],
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", out + ".tmp",
+              *objs, *libs],
              os.path.basename(out), verbose)
     os.replace(out + ".tmp", out)
 
@@ -62,5 +70,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """The same library with the host code under ASan + UBSan, written to out_dir (for the
+    CPU test run under sanitizers; load it with MIATTN_LIB and preload clang's ASan runtime)."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libmiattn_san.so")
+    _hipcc(out, sources(), verbose, libs=("-L/opt/rocm/lib", "-lrocblas"), extra=HOST_SANITIZE,
+           link_extra=("-fsanitize=address,undefined", "-shared-libasan"))
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    if len(sys.argv) == 3 and sys.argv[1] == "--sanitize":
+        print(build_sanitized(sys.argv[2], verbose=True))
+    else:
+        print(build(verbose=True))

@@ -29,6 +29,22 @@ def test_header_declares_every_entry_point():
         assert name in d, d
 
 
+def test_header_compiles_as_c_and_cxx(tmp_path):
+    """The header is usable from C (C11, pedantic) and C++; its enums are int-sized in both."""
+    src = tmp_path / "use.c"
+    src.write_text('#include "miattn.h"\n'
+                   '_Static_assert(sizeof(miattn_dtype_t) == sizeof(int), "enum size");\n'
+                   'int main(void) { miattn_mask_t m = MIATTN_MASK_CAUSAL; return (int)m - 1; }\n')
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                    os.path.dirname(HEADER), "-fsyntax-only", str(src)], check=True)
+    cxx = tmp_path / "use.cc"
+    cxx.write_text('#include "miattn.h"\n'
+                   'static_assert(sizeof(miattn_dtype_t) == sizeof(int), "enum size");\n'
+                   'int main() { miattn_dtype_t d = (miattn_dtype_t)9; return (int)d == 9 ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-I",
+                    os.path.dirname(HEADER), "-fsyntax-only", str(cxx)], check=True)
+
+
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
