@@ -531,18 +531,42 @@ def main():
             "XCD, 8 rows in flight per 16 lanes")
         del gtab, gout
 
-        def sparse_roofline(seconds, elem):
-            # every stored entry gathers one K row and one V row of D elements
-            gathered = 2.0 * sB * sN * nnz * sD * elem
+        def sparse_split(dtype_):
+            """Entries whose K / V rows the kernel reads from its LDS window (the keys before
+            the end of each 64-row block, sparse_csr_window) and entries it gathers from
+            global memory, and the rows the window copies take (coalesced)."""
+            W = mi.sparse_csr_window(sD, dtype_)
+            off_, col_ = ws["offset"].reshape(-1, sS + 1), ws["columns"].reshape(-1, nnz)
+            in_w, copied = 0, 0
+            r1_blocks = np.minimum(sS, np.arange(64, sS + 64, 64))
+            copied = int(np.sum(r1_blocks - np.maximum(0, r1_blocks - W))) * off_.shape[0]
+            for sl in range(off_.shape[0]):
+                n_ = int(off_[sl, -1])
+                rows_ = np.repeat(np.arange(sS), np.diff(off_[sl]))
+                r1 = np.minimum(sS, (rows_ // 64 + 1) * 64)
+                c_ = col_[sl, :n_]
+                in_w += int(np.count_nonzero((c_ >= np.maximum(0, r1 - W)) & (c_ < r1)))
+            return W, in_w, copied
+
+        def sparse_roofline(seconds, elem, split):
+            # every stored entry reads one K row and one V row of D elements: from the LDS
+            # window or, for the rest, gathered from global memory (L2); the bound is the
+            # latter against the measured random-row gather rate
+            W, in_w, copied = split
+            total = sB * sN * nnz
+            gathered = 2.0 * (total - in_w) * sD * elem
             ach = gathered / seconds / 1e9
             return {"bound": "l2_gather", "achieved": round(ach, 1), "peak": round(gather_gbs, 1),
                     "unit": "GB/s", "frac": round(ach / gather_gbs, 4),
-                    "gathered_bytes": gathered}
+                    "gathered_bytes": gathered, "window_keys": W,
+                    "entries_from_lds_window": in_w, "entries_total": total,
+                    "window_copy_bytes": 2.0 * copied * sD * elem,
+                    "row_bytes_all_entries": 2.0 * total * sD * elem}
 
         sec["sparse_csr_attn"] = {
             "workload": "csr_sparse_f32_b2n8s4096d64", "us_per_launch": round(sms * 1e3, 2),
             "tflops": round(stf, 3), "gbs_algorithmic": round(sbytes / (sms * 1e-3) / 1e9, 1),
-            "roofline": sparse_roofline(sms * 1e-3, 4),
+            "roofline": sparse_roofline(sms * 1e-3, 4, sparse_split("f32")),
             "alu": {"achieved": round(stf, 3), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(stf / PEAK_F32_VALU_TFLOPS, 4)}}
         # the same CSR workload with fp64 inputs and arithmetic
@@ -559,7 +583,7 @@ def main():
         sec["sparse_csr_attn_f64"] = {
             "workload": "csr_sparse_f64_b2n8s4096d64", "us_per_launch": round(dms * 1e3, 2),
             "tflops": round(dtf, 3),
-            "roofline": sparse_roofline(dms * 1e-3, 8),
+            "roofline": sparse_roofline(dms * 1e-3, 8, sparse_split("f64")),
             "alu": {"achieved": round(dtf, 3), "peak": 78.6, "unit": "TFLOP/s",
                     "frac": round(dtf / 78.6, 4)}}
 

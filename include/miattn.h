@@ -297,8 +297,10 @@ miattn_status_t attn_fwd_varlen_ext(const void* q, const void* k, const void* v,
  * attn_fwd_update apply; the routing is a property of this implementation, not of the
  * pages).  Arguments as attn_fwd_ext; update != 0 asks about attn_fwd_update; atten_mask
  * is only inspected for its alignment, never read.
- *   Returns MIATTN_KERNEL_TILED or MIATTN_KERNEL_GENERAL, or minus the status the forward
- *   would return for these arguments (e.g. -MIATTN_ERR_SHAPE).
+ *   Returns MIATTN_KERNEL_TILED, MIATTN_KERNEL_PERSISTENT or MIATTN_KERNEL_GENERAL, or
+ *   minus the status the forward would return for these arguments (e.g. -MIATTN_ERR_SHAPE).
+ *   The environment variable MIATTN_PERSIST=0 turns the persistent route off (the tiled
+ *   kernel then serves those calls, with identical results).
  */
 int32_t attn_fwd_route(int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t Skv, int64_t D,
                        int64_t Dv, miattn_dtype_t dtype, miattn_layout_t layout,
@@ -316,13 +318,27 @@ int32_t attn_fwd_route(int64_t B, int64_t Nq, int64_t Nkv, int64_t Sq, int64_t S
  *   q, k, v, out: fp32 or fp64 [B, N, S, D] (BNSD) contiguous (all arithmetic in that type;
  *   the fp64 path uses `scale` widened to double);
  *   csr_offset: DEVICE int32 [B, N, S+1];  csr_columns: DEVICE int32 [B, N, nnz];
- *   dtype: MIATTN_F32 or MIATTN_F64 (bf16/fp16 -> UNSUPPORTED).  D in {32, 64, 96, 128}.
- *   nnz >= 0.
+ *   dtype: MIATTN_F32 or MIATTN_F64 (bf16/fp16 -> UNSUPPORTED).  Any head dim 1 <= D <= 768
+ *   (the page bounds none; 768 is the dense entry points' limit); D > 768 -> SHAPE.
+ *   nnz >= 0.  Entries whose column lies among the keys just before a block of 64 rows
+ *   are read from a copy in LDS, the rest gathered from global memory: a banded pattern
+ *   runs fastest, any pattern runs.
  */
 miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, void* out,
                                 const int32_t* csr_offset, const int32_t* csr_columns,
                                 int64_t nnz, int64_t B, int64_t N, int64_t S, int64_t D,
                                 miattn_dtype_t dtype, float scale, void* stream);
+
+/*
+ * sparse_csr_window - how many keys sparse_csr_attn serves from LDS: rows are taken in
+ * blocks of 64 ([64 j, 64 j + 64) of each slice, the last one ragged), and an entry of a row
+ * in a block that ends at row r1 (exclusive) is read from the LDS copy when its column lies
+ * in [max(0, r1 - W), r1), W the value returned; every other entry is gathered from global
+ * memory.  For 16-byte aligned K, V and out (the value may be larger for unaligned ones).
+ * A property of this implementation (for measurement), not of the Paddle page.
+ *   Returns W >= 1, or minus the status sparse_csr_attn would return for this D and dtype.
+ */
+int32_t sparse_csr_window(int64_t D, miattn_dtype_t dtype);
 
 /*
  * mha_self_attn_fwd - forward of the multi-head self-attention module of the page "flash

@@ -39,7 +39,7 @@ KERNELS = {1: "tiled", 2: "general", 3: "persistent"}
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
            "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
-           "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd",
+           "sparse_csr_attn", "sparse_csr_window", "mha_workspace_bytes", "mha_self_attn_fwd",
            "mha_self_attn_fwd_noalloc", "miattn_status_str")
 
 
@@ -63,6 +63,8 @@ _lib.attn_fwd_route.argtypes = [_I64] * 7 + [_E, _E, _E, _P, _F, ctypes.c_int32]
 _lib.attn_fwd_route.restype = ctypes.c_int32
 _lib.attn_lse_merge.argtypes = [_P] * 9 + [_I64] * 4 + [_E, _E, _P]
 _lib.sparse_csr_attn.argtypes = [_P] * 6 + [_I64] * 5 + [_E, _F, _P]
+_lib.sparse_csr_window.argtypes = [_I64, _E]
+_lib.sparse_csr_window.restype = ctypes.c_int32
 _lib.mha_workspace_bytes.argtypes = [_I64] * 3 + [_E]
 _lib.mha_workspace_bytes.restype = ctypes.c_int64
 _lib.mha_self_attn_fwd.argtypes = [_P] * 7 + [_I64] * 5 + [_E, _P, _F, _U64, _U32, _P]
@@ -256,6 +258,15 @@ def sparse_csr_attn(q, k, v, out, csr_offset, csr_columns, nnz, B, N, S, D, dtyp
     _check(_lib.sparse_csr_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(csr_offset),
                                 _ptr(csr_columns), nnz, B, N, S, D, _enum(dtype, DTYPES),
                                 scale, _stream(stream)), "sparse_csr_attn")
+
+
+def sparse_csr_window(D, dtype) -> int:
+    """Keys before the end of each 64-row block that sparse_csr_attn reads from LDS (no HIP
+    call).  Raises MiattnError with the status sparse_csr_attn would return."""
+    r = _lib.sparse_csr_window(D, _enum(dtype, DTYPES))
+    if r < 0:
+        raise MiattnError(-r, "sparse_csr_window")
+    return r
 
 
 def mha_workspace_bytes(B, S, E, dtype) -> int:

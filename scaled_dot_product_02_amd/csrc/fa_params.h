@@ -71,7 +71,7 @@ struct SparseParams {
     const int32_t* offset;
     const int32_t* columns;
     int64_t nnz;
-    int32_t B, N, S;
+    int32_t B, N, S, D;
     float scale_log2;
     double scale_log2_d;        // the same in double precision (fp64 inputs)
 };
@@ -91,7 +91,14 @@ hipError_t launch_fa_fwd_persist(const FaParams& p, int D, bool f16, hipStream_t
 int fa_persist_heads_per_item(int group);
 int fa_wide_tile_m(int dtype);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
-hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream);
+// the CSR kernel; aligned16: K, V and out are 16-byte aligned (vector row accesses)
+hipError_t launch_sparse_csr(const SparseParams& p, bool f64, bool aligned16, hipStream_t stream);
+// whether the CSR kernel takes head dim D (1..768; fp64 at 768 still fits its LDS)
+bool sparse_head_dim_fits(int D, bool f64);
+// keys of the CSR kernel's LDS window (the keys before the end of each block of
+// kSparseRowBlock rows that it reads from LDS instead of global memory)
+int sparse_window_keys(int D, bool f64, bool aligned16);
+constexpr int kSparseRowBlock = 64;
 
 // Longest packed batch (sequences) of the persistent kernel, whose workgroups sort the
 // sequence lengths in LDS.

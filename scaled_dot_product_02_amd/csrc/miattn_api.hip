@@ -487,6 +487,16 @@ miattn_status_t attn_lse_merge(const void* prev_out, const float* prev_max, cons
     return launch_lse_merge(p, dtype, (hipStream_t)stream) == hipSuccess ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 
+int32_t sparse_csr_window(int64_t D, miattn_dtype_t dtype)
+{
+    if (dtype != MIATTN_F32 && dtype != MIATTN_F64)
+        return -(int32_t)((dtype == MIATTN_BF16 || dtype == MIATTN_F16) ? MIATTN_ERR_UNSUPPORTED
+                                                                        : MIATTN_ERR_DTYPE);
+    if (D < 1 || D > 768) return -(int32_t)MIATTN_ERR_SHAPE;
+    if (!sparse_head_dim_fits((int)D, dtype == MIATTN_F64)) return -(int32_t)MIATTN_ERR_UNSUPPORTED;
+    return sparse_window_keys((int)D, dtype == MIATTN_F64, true);
+}
+
 miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, void* out,
                                 const int32_t* csr_offset, const int32_t* csr_columns,
                                 int64_t nnz, int64_t B, int64_t N, int64_t S, int64_t D,
@@ -500,14 +510,16 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
     if (S >= (int64_t(1) << 31) - 1 || nnz >= (int64_t(1) << 31) || B * N * S >= (int64_t(1) << 33))
         return MIATTN_ERR_SHAPE;
     if (!scale_ok(scale)) return MIATTN_ERR_SCALE;
-    if (!head_dim_built(D)) return MIATTN_ERR_UNSUPPORTED;
+    if (!sparse_head_dim_fits((int)D, dtype == MIATTN_F64)) return MIATTN_ERR_UNSUPPORTED;
     SparseParams p{};
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.offset = csr_offset; p.columns = csr_columns; p.nnz = nnz;
-    p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S;
+    p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S; p.D = (int32_t)D;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.scale_log2_d = (double)scale * 1.4426950408889634074;
-    return launch_sparse_csr(p, (int)D, dtype == MIATTN_F64, (hipStream_t)stream) == hipSuccess
+    // vector reads of K / V rows and vector stores of output rows
+    const bool aligned16 = (((uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) == 0;
+    return launch_sparse_csr(p, dtype == MIATTN_F64, aligned16, (hipStream_t)stream) == hipSuccess
                ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }
 

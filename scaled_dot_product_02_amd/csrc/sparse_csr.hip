@@ -1,39 +1,81 @@
-// CSR-sparse attention, fp32 or fp64 (Paddle "sparse_attention": formula, parameters,
-// example; the page lists float32 and float64 inputs).  All arithmetic is in the input type.
+// CSR-sparse attention, fp32 or fp64, any head dim 1..768 (Paddle "sparse_attention":
+// formula, parameters, example; the page lists float32 and float64 inputs and puts no
+// bound on the head dim).  All arithmetic is in the input type.
 //
 // Row i of slice (b, n) attends to the key rows listed in
-// columns[b][n][offset[b][n][i] .. offset[b][n][i+1]).  One wave per query row:
+// columns[b][n][offset[b][n][i] .. offset[b][n][i+1]).
+//
+// A workgroup (16 waves) takes RB = 64 consecutive rows of one slice.  Rows that are
+// close to each other mostly list the same nearby keys (a sliding-window band is the
+// common pattern, e.g. the page's example and local + random layouts), so the workgroup
+// first copies the K and V rows of a key window into LDS with coalesced loads: the WL keys
+// that end at the block's last row (the 128 keys before each row of the block, when they
+// fit the LDS).  Every entry whose column falls in the window then reads its K / V row
+// from LDS; the others are gathered from global memory (L2), so any CSR pattern is served
+// and one without locality costs only the window copy.
+//
+// Each wave takes rows of the block in turn.  Per row:
 //   * score phase: lane e takes entry e of a 64-entry chunk and forms the whole dot
-//     product q . k_col (the query row is broadcast from LDS, the key row is gathered with
-//     16-byte loads);
+//     product q . k_col (the query row is broadcast from LDS, the key row comes from the
+//     window or from global memory through one generic pointer, so a chunk that mixes
+//     both has no divergent branch);
 //   * chunk max and sum by wave butterflies; the running max / sum are rescaled once per
 //     chunk (online softmax in the log2 domain);
 //   * value phase: the chunk's (probability, column) pairs are broadcast lane by lane and
-//     every lane accumulates its own head-dim slice of sum_c p_c v_c (coalesced row reads),
-//     16 value rows per batch with all their loads in flight together.
-// Work per row is proportional to its entry count; four consecutive rows of one slice
-// share a workgroup so their common columns are re-read from L1/L2.
+//     every lane accumulates its own head-dim slice of sum_c p_c v_c (coalesced row reads
+//     from the window or global memory), several value rows per batch with all their
+//     loads in flight together.
 #include "fa_params.h"
 
 namespace miattn {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 1024;                  // threads per workgroup (16 waves)
+constexpr int NW = NT / 64;
+constexpr int RB = kSparseRowBlock;       // rows per workgroup
+constexpr int kBand = 128;                // keys before a row that the window aims to hold
+constexpr int kLdsBytes = 144 * 1024;     // LDS of a workgroup (query rows + K / V window)
 
-template <typename T>
-__device__ inline T wave_max(T x)
+// x combined (max or sum) over the lanes that agree with this one in the lane-index bits
+// below FROM (FROM = 1: the whole wave).  fp32: rotations inside 16-lane rows (DPP), then
+// v_permlane16_swap / v_permlane32_swap across rows, no LDS traffic; fp64: shuffles.
+template <int N>
+__device__ inline float row_ror(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+template <int FROM, bool MAX>
+__device__ inline float lane_reduce(float x)
+{
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (FROM <= 1) x = op(x, row_ror<1>(x));
+    if constexpr (FROM <= 2) x = op(x, row_ror<2>(x));
+    if constexpr (FROM <= 4) x = op(x, row_ror<4>(x));
+    if constexpr (FROM <= 8) x = op(x, row_ror<8>(x));
+    if constexpr (FROM <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (FROM <= 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return x;
+}
+template <int FROM, bool MAX>
+__device__ inline double lane_reduce(double x)
 {
     #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+    for (int o = FROM; o < 64; o <<= 1) {
+        const double y = __shfl_xor(x, o);
+        x = MAX ? fmax(x, y) : x + y;
+    }
     return x;
 }
 template <typename T>
-__device__ inline T wave_sum(T x)
-{
-    #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
+__device__ inline T wave_max(T x) { return lane_reduce<1, true>(x); }
+template <typename T>
+__device__ inline T wave_sum(T x) { return lane_reduce<1, false>(x); }
 __device__ inline float exp2_t(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline double exp2_t(double x) { return exp2(x); }
 __device__ inline float lane_value(float x, int e)
@@ -48,126 +90,323 @@ __device__ inline double lane_value(double x, int e)
     return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// T = float or double (all arithmetic in T); D a multiple of 32.
-template <typename T, int D>
+// The layout of a workgroup's LDS for head dim D: per wave one query row, then the K
+// window (row stride KS, padded by 16 bytes so that lanes reading consecutive window rows
+// at the same offset hit different banks) and the V window (row stride VS, padded by 64
+// bytes: the grouped value phase reads 64-byte pieces of 16 rows at once, and consecutive
+// rows then start 16 banks apart).
+struct SparseLds {
+    int QS, KS, VS, WL;
+};
+
+__host__ __device__ inline SparseLds sparse_lds(int D, int esz, int ve)
+{
+    SparseLds l;
+    l.QS = (D + ve - 1) / ve * ve;
+    l.KS = D + (ve > 1 ? ve : 1);
+    l.VS = D + 64 / esz;
+    const int room = kLdsBytes / esz - NW * l.QS;
+    const int wl = room / (l.KS + l.VS);
+    l.WL = wl < RB + kBand ? wl : RB + kBand;
+    return l;
+}
+
+// T = float or double (all arithmetic in T).  DC = the head dim when it is fixed at compile
+// time (0: the head dim p.D at run time, at most 64 * PL).  VE = elements per vector access
+// of a K / Q row (the head dim and the K pointer are multiples of it).
+template <typename T, int DC, int PL, int VE>
 __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
 {
-    constexpr int VW = 16 / sizeof(T);          // elements per 16-byte load
-    typedef T V __attribute__((ext_vector_type(VW)));
-    constexpr int PL = (D + 63) / 64;           // head-dim values per lane in the value phase
-    __shared__ __attribute__((aligned(16))) T qs[NT / 64][D];
+    typedef T V __attribute__((ext_vector_type(VE)));
+    typedef __attribute__((address_space(3))) const V LVc;    // LDS
+    typedef __attribute__((address_space(1))) const V GVc;    // global
+    // grouped value phase (compile-time head dims whose rows are whole 64-byte slices that
+    // tile a wave): DL lanes per V row, NV elements per lane, EG entry groups, JB entries
+    // of a group in flight per batch
+    constexpr int RBYTES = DC * (int)sizeof(T);
+    constexpr bool GV = DC > 0 && VE > 1 && RBYTES % 64 == 0 && 64 % (RBYTES / 64 ? RBYTES / 64 : 1) == 0;
+    constexpr int DL = GV ? RBYTES / 64 : 1;
+    constexpr int NV = 64 / (int)sizeof(T);
+    constexpr int EG = 64 / DL;
+    constexpr int JB = (RBYTES > 256 || sizeof(T) == 8) ? 2 : DL < 4 ? DL : 4;
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    const int D = DC ? DC : p.D;
+    const SparseLds L = sparse_lds(D, (int)sizeof(T), VE);
+    T* qs_all = (T*)lds;
+    T* ks = qs_all + NW * L.QS;
+    T* vs = ks + L.WL * L.KS;
     const T* q = (const T*)p.q;
     const T* k = (const T*)p.k;
     const T* v = (const T*)p.v;
     T* out = (T*)p.out;
     const T scale_log2 = sizeof(T) == 8 ? (T)p.scale_log2_d : (T)p.scale_log2;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t total = (int64_t)p.B * p.N * p.S;
+
     // workgroups go to the 8 XCDs round-robin (id mod 8); XCD x takes the x-th eighth of
-    // the row blocks in order, so that the rows resident on one XCD are consecutive rows of
-    // one slice and share its K/V rows (the band, and the slice as a whole) in that XCD's L2
-    const int64_t nblk = (total + NT / 64 - 1) / (NT / 64);
+    // the row blocks in order, so that the blocks resident on one XCD are consecutive
+    // blocks of one slice and share its gathered K/V rows in that XCD's L2
+    const int nblk_s = (p.S + RB - 1) / RB;
+    const int64_t nblk = (int64_t)p.B * p.N * nblk_s;
     const int64_t per = (nblk + 7) / 8;
     const int64_t blk = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    const int64_t row = blk * (NT / 64) + wave;
-    const bool valid = row < total;
-    if (valid)
-        for (int d = lane; d < D; d += 64) qs[wave][d] = q[row * D + d];
-    __syncthreads();
-    if (!valid) return;
-
-    const int64_t bn = row / p.S;
-    const int i = (int)(row - bn * p.S);
-    const int32_t* off = p.offset + bn * (p.S + 1);
-    const int32_t* col = p.columns + bn * p.nnz;
+    if (blk >= nblk) return;     // uniform over the workgroup
+    const int64_t bn = blk / nblk_s;
+    const int r0 = (int)(blk - bn * nblk_s) * RB;
+    const int r1 = min(p.S, r0 + RB);
+    const int w1 = r1, w0 = max(0, r1 - L.WL);
+    const int wl = w1 - w0;
     const T* kb = k + bn * p.S * D;
     const T* vb = v + bn * p.S * D;
-    const int e0 = off[i], e1 = off[i + 1];
 
-    T m_run = -INFINITY, l_run = 0;
-    T o[PL];
-    #pragma unroll
-    for (int u = 0; u < PL; ++u) o[u] = 0;
-
-    for (int base = e0; base < e1; base += 64) {
-        const int cnt = min(64, e1 - base);
-        T sc = -INFINITY;
-        int c = 0;
-        if (lane < cnt) {
-            c = col[base + lane];
-            const V* kr = (const V*)(kb + (int64_t)c * D);
-            const V* qr = (const V*)qs[wave];
-            T acc = 0;
-            #pragma unroll
-            for (int dv = 0; dv < D / VW; ++dv) {
-                const V kx = kr[dv], qx = qr[dv];
-                #pragma unroll
-                for (int e = 0; e < VW; ++e) acc = fma(qx[e], kx[e], acc);
-            }
-            sc = acc * scale_log2;
+    // the key window: K rows [w0, w1) into ks (padded rows), V rows into vs
+    {
+        const T* ksrc = kb + (int64_t)w0 * D;
+        const T* vsrc = vb + (int64_t)w0 * D;
+        const int n = wl * D;
+        for (int x = threadIdx.x; x < n; x += NT) {
+            const int r = x / D, d = x - r * D;
+            ks[r * L.KS + d] = ksrc[x];
+            vs[r * L.VS + d] = vsrc[x];
         }
-        const T m_new = fmax(m_run, wave_max(sc));
-        const T alpha = exp2_t(m_run - m_new);
-        const T pv = lane < cnt ? exp2_t(sc - m_new) : (T)0;
-        l_run = l_run * alpha + wave_sum(pv);
+    }
+    __syncthreads();
+
+    const int32_t* off = p.offset + bn * (p.S + 1);
+    typedef __attribute__((address_space(1))) const int32_t GI;
+    GI* colg = (GI*)(p.columns + bn * p.nnz);
+    T* qs = qs_all + wave * L.QS;
+    for (int i = r0 + wave; i < r1; i += NW) {
+        const int64_t row = bn * p.S + i;
+        // the wave's query row (LDS operations of one wave complete in order, so the
+        // previous row's reads are done before these writes land)
+        for (int d = lane; d < D; d += 64) qs[d] = q[row * D + d];
+        const int e0 = off[i], e1 = off[i + 1];
+        T m_run = -INFINITY, l_run = 0;
+        T o[PL];
         #pragma unroll
-        for (int u = 0; u < PL; ++u) o[u] *= alpha;
-        // value rows in batches of VB entries: all loads of a batch are in flight together
-        // (one entry at a time would wait out a full memory latency per entry)
-        constexpr int VB = 16;
-        int e = 0;
-        for (; e + VB <= cnt; e += VB) {
-            T vv[VB][PL];
+        for (int u = 0; u < PL; ++u) o[u] = 0;
+        T ga[GV ? NV : 1];
+        #pragma unroll
+        for (int u = 0; u < (GV ? NV : 1); ++u) ga[u] = 0;
+
+        for (int base = e0; base < e1; base += 64) {
+            const int cnt = min(64, e1 - base);
+            // lanes past cnt take the window's first key (any valid row: their p is 0)
+            const int c = lane < cnt ? colg[base + lane] : w0;
+            const int wr = c - w0;
+            const bool in = (unsigned)wr < (unsigned)wl;
+            // chunk-wide: every entry in the window (LDS reads), none (global reads), or
+            // both (generic reads); band + random rows give mostly one-sided chunks
+            const bool all_in = __all(in), none_in = !__any(in);
+            const V* qr = (const V*)qs;
+            auto dot = [&](auto kr) {
+                T acc = 0;
+                if constexpr (DC != 0 && RBYTES <= 256) {
+                    #pragma unroll
+                    for (int dv = 0; dv < (DC ? DC : VE) / VE; ++dv) {
+                        const V kx = kr[dv], qx = qr[dv];
+                        #pragma unroll
+                        for (int e = 0; e < VE; ++e) acc = fma(qx[e], kx[e], acc);
+                    }
+                } else if constexpr (DC != 0) {
+                    // longer rows: 128 bytes of the row per unrolled step (registers)
+                    #pragma unroll 8
+                    for (int dv = 0; dv < (DC ? DC : VE) / VE; ++dv) {
+                        const V kx = kr[dv], qx = qr[dv];
+                        #pragma unroll
+                        for (int e = 0; e < VE; ++e) acc = fma(qx[e], kx[e], acc);
+                    }
+                } else {
+                    #pragma unroll 4
+                    for (int dv = 0; dv < D / VE; ++dv) {
+                        const V kx = kr[dv], qx = qr[dv];
+                        #pragma unroll
+                        for (int e = 0; e < VE; ++e) acc = fma(qx[e], kx[e], acc);
+                    }
+                }
+                return acc;
+            };
+            T sc = -INFINITY;
+            if (lane < cnt) {
+                T acc;
+                if (all_in)
+                    acc = dot((LVc*)(ks + wr * L.KS));
+                else if (none_in)
+                    acc = dot((GVc*)(kb + (int64_t)c * D));
+                else
+                    acc = dot(in ? (const V*)(ks + wr * L.KS) : (const V*)(kb + (int64_t)c * D));
+                sc = acc * scale_log2;
+            }
+            const T m_new = fmax(m_run, wave_max(sc));
+            const T alpha = exp2_t(m_run - m_new);
+            const T pv = lane < cnt ? exp2_t(sc - m_new) : (T)0;
+            l_run = l_run * alpha + wave_sum(pv);
+            if constexpr (GV) {
+                // grouped value phase: lane = (entry group eg, position dg among the DL
+                // lanes of a row); group eg takes entries eg, eg + EG, ... of the chunk, and
+                // lane dg reads the 16-byte pieces dg, dg + DL, dg + 2 DL, dg + 3 DL of those
+                // V rows (so each load instruction reads 16 DL contiguous bytes per row; a
+                // batch of entries in flight at once) into a partial sum, which the groups
+                // add up at the end of the row.  Entries past cnt have p = 0 and column 0.
+                #pragma unroll
+                for (int u = 0; u < NV; ++u) ga[u] *= alpha;
+                const int eg = lane / DL, dg = lane % DL;
+                typedef T V16 __attribute__((ext_vector_type(16 / sizeof(T))));
+                constexpr int EPV = 16 / (int)sizeof(T);
+                #pragma unroll 1
+                for (int j0 = 0; j0 < DL; j0 += JB) {
+                    V16 vv[JB][4];
+                    T pj[JB];
+                    typedef __attribute__((address_space(3))) const V16 LV16;
+                    typedef __attribute__((address_space(1))) const V16 GV16;
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j) {
+                        const int e = eg + EG * (j0 + j);
+                        const int ce = __shfl(c, e);
+                        pj[j] = __shfl(pv, e);
+                        const int wre = ce - w0;
+                        if (all_in) {
+                            LV16* vr = (LV16*)(vs + wre * L.VS) + dg;
+                            #pragma unroll
+                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
+                        } else if (none_in) {
+                            GV16* vr = (GV16*)(vb + (int64_t)ce * DC) + dg;
+                            #pragma unroll
+                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
+                        } else {
+                            const V16* vr = (const V16*)((unsigned)wre < (unsigned)wl ? vs + wre * L.VS
+                                                                                      : vb + (int64_t)ce * DC) + dg;
+                            #pragma unroll
+                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
+                        }
+                    }
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j)
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            #pragma unroll
+                            for (int y = 0; y < EPV; ++y)
+                                ga[x * EPV + y] = fma(pj[j], vv[j][x][y], ga[x * EPV + y]);
+                }
+                m_run = m_new;
+                continue;
+            }
             #pragma unroll
-            for (int x = 0; x < VB; ++x) {
-                const T* vr = vb + (int64_t)__builtin_amdgcn_readlane(c, e + x) * D;
+            for (int u = 0; u < PL; ++u) o[u] *= alpha;
+            // value rows in batches of VB entries: all loads of a batch are in flight
+            // together (one entry at a time would wait out a full latency per entry)
+            constexpr int VREGS = PL * (int)sizeof(T) / 4;     // registers per value row
+            constexpr int VB = VREGS >= 32 ? 1 : 32 / VREGS > 16 ? 16 : 32 / VREGS;
+            int e = 0;
+            for (; e + VB <= cnt; e += VB) {
+                T vv[VB][PL];
+                #pragma unroll
+                for (int x = 0; x < VB; ++x) {
+                    const int ce = __builtin_amdgcn_readlane(c, e + x);
+                    const int wr = ce - w0;
+                    const T* vr = (unsigned)wr < (unsigned)wl ? vs + wr * L.VS : vb + (int64_t)ce * D;
+                    #pragma unroll
+                    for (int u = 0; u < PL; ++u)
+                        vv[x][u] = (DC % 64 == 0 && DC) || lane + 64 * u < D ? vr[lane + 64 * u] : (T)0;
+                }
+                #pragma unroll
+                for (int x = 0; x < VB; ++x) {
+                    const T pe = lane_value(pv, e + x);
+                    #pragma unroll
+                    for (int u = 0; u < PL; ++u) o[u] = fma(pe, vv[x][u], o[u]);
+                }
+            }
+            for (; e < cnt; ++e) {
+                const T pe = lane_value(pv, e);
+                const int ce = __builtin_amdgcn_readlane(c, e);
+                const int wr = ce - w0;
+                const T* vr = (unsigned)wr < (unsigned)wl ? vs + wr * L.VS : vb + (int64_t)ce * D;
                 #pragma unroll
                 for (int u = 0; u < PL; ++u)
-                    vv[x][u] = (D % 64 == 0 || lane + 64 * u < D) ? vr[lane + 64 * u] : (T)0;
+                    if ((DC % 64 == 0 && DC) || lane + 64 * u < D) o[u] = fma(pe, vr[lane + 64 * u], o[u]);
             }
+            m_run = m_new;
+        }
+        const T inv = l_run > 0 ? (T)1 / l_run : (T)0;
+        if constexpr (GV) {
+            // add up the entry groups' partial sums (lanes with the same slice dg)
             #pragma unroll
-            for (int x = 0; x < VB; ++x) {
-                const T pe = lane_value(pv, e + x);
+            for (int u = 0; u < NV; ++u) ga[u] = lane_reduce<DL, false>(ga[u]);
+            if (lane < DL) {
+                typedef T V16 __attribute__((ext_vector_type(16 / sizeof(T))));
+                constexpr int EPV = 16 / (int)sizeof(T);
+                V16* dst = (V16*)(out + row * DC) + lane;
                 #pragma unroll
-                for (int u = 0; u < PL; ++u) o[u] = fma(pe, vv[x][u], o[u]);
+                for (int x = 0; x < 4; ++x) {
+                    V16 r;
+                    #pragma unroll
+                    for (int y = 0; y < EPV; ++y) r[y] = ga[x * EPV + y] * inv;
+                    dst[x * DL] = r;
+                }
             }
+            continue;
         }
-        for (; e < cnt; ++e) {
-            const T pe = lane_value(pv, e);
-            const int ce = __builtin_amdgcn_readlane(c, e);
-            const T* vr = vb + (int64_t)ce * D;
-            #pragma unroll
-            for (int u = 0; u < PL; ++u)
-                if (D % 64 == 0 || lane + 64 * u < D) o[u] = fma(pe, vr[lane + 64 * u], o[u]);
-        }
-        m_run = m_new;
+        #pragma unroll
+        for (int u = 0; u < PL; ++u)
+            if ((DC % 64 == 0 && DC) || lane + 64 * u < D) out[row * D + lane + 64 * u] = o[u] * inv;
     }
-    const T inv = l_run > 0 ? (T)1 / l_run : (T)0;
-    #pragma unroll
-    for (int u = 0; u < PL; ++u)
-        if (D % 64 == 0 || lane + 64 * u < D) out[row * D + lane + 64 * u] = o[u] * inv;
+}
+
+template <typename T, int DC, int PL, int VE>
+hipError_t launch_one(const SparseParams& p, hipStream_t stream)
+{
+    const int64_t nblk = (int64_t)p.B * p.N * ((p.S + RB - 1) / RB);
+    dim3 grid((unsigned)((nblk + 7) / 8 * 8)), block(NT);
+    hipLaunchKernelGGL((sparse_csr_kernel<T, DC, PL, VE>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// the head dim at run time: PL = values per lane of the output row (D <= 64 PL)
+template <typename T, int VE>
+hipError_t launch_general(const SparseParams& p, hipStream_t stream)
+{
+    const int D = p.D;
+    if (D <= 64) return launch_one<T, 0, 1, VE>(p, stream);
+    if (D <= 128) return launch_one<T, 0, 2, VE>(p, stream);
+    if (D <= 256) return launch_one<T, 0, 4, VE>(p, stream);
+    if (D <= 512) return launch_one<T, 0, 8, VE>(p, stream);
+    return launch_one<T, 0, 12, VE>(p, stream);
 }
 
 template <typename T>
-hipError_t launch_t(const SparseParams& p, int D, hipStream_t stream)
+hipError_t launch_t(const SparseParams& p, bool aligned16, hipStream_t stream)
 {
-    const int64_t rows = (int64_t)p.B * p.N * p.S;
-    dim3 grid((unsigned)(((rows + NT / 64 - 1) / (NT / 64) + 7) / 8 * 8)), block(NT);
-    switch (D) {
-    case 32: hipLaunchKernelGGL((sparse_csr_kernel<T, 32>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((sparse_csr_kernel<T, 64>), grid, block, 0, stream, p); break;
-    case 96: hipLaunchKernelGGL((sparse_csr_kernel<T, 96>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((sparse_csr_kernel<T, 128>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+    constexpr int VE = 16 / sizeof(T);
+    const bool vec = aligned16 && p.D % VE == 0;
+    if (vec) {
+        switch (p.D) {
+        case 32: return launch_one<T, 32, 1, VE>(p, stream);
+        case 64: return launch_one<T, 64, 1, VE>(p, stream);
+        case 96: return launch_one<T, 96, 2, VE>(p, stream);
+        case 128: return launch_one<T, 128, 2, VE>(p, stream);
+        default: return launch_general<T, VE>(p, stream);
+        }
     }
-    return hipGetLastError();
+    return launch_general<T, 1>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_sparse_csr(const SparseParams& p, int D, bool f64, hipStream_t stream)
+int sparse_window_keys(int D, bool f64, bool aligned16)
 {
-    return f64 ? launch_t<double>(p, D, stream) : launch_t<float>(p, D, stream);
+    const int ve = f64 ? 2 : 4;
+    return sparse_lds(D, f64 ? 8 : 4, aligned16 && D % ve == 0 ? ve : 1).WL;
+}
+
+bool sparse_head_dim_fits(int D, bool f64)
+{
+    // the window must hold at least one key row beside the query rows
+    return D >= 1 && D <= 768 && sparse_lds(D, f64 ? 8 : 4, f64 ? 2 : 4).WL >= 1;
+}
+
+hipError_t launch_sparse_csr(const SparseParams& p, bool f64, bool aligned16, hipStream_t stream)
+{
+    return f64 ? launch_t<double>(p, aligned16, stream) : launch_t<float>(p, aligned16, stream);
 }
 
 }  // namespace miattn

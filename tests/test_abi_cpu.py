@@ -24,7 +24,7 @@ def test_header_declares_every_entry_point():
     d = _declared()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_update", "attn_fwd_varlen_update",
                  "attn_fwd_ext", "attn_fwd_varlen_ext", "attn_fwd_route", "attn_lse_merge",
-                 "sparse_csr_attn", "mha_workspace_bytes", "mha_self_attn_fwd",
+                 "sparse_csr_attn", "sparse_csr_window", "mha_workspace_bytes", "mha_self_attn_fwd",
                  "mha_self_attn_fwd_noalloc", "miattn_status_str"):
         assert name in d, d
 
@@ -329,7 +329,23 @@ def test_sparse_csr_attn_validation(mi):
     assert call(nnz=-1) == "MIATTN_ERR_SHAPE"
     assert call(S=0) == "MIATTN_ERR_SHAPE"
     assert call(scale=0.0) == "MIATTN_ERR_SCALE"
-    assert call(D=48) == "MIATTN_ERR_UNSUPPORTED"
+    assert call(D=769) == "MIATTN_ERR_SHAPE"
+    assert call(D=0) == "MIATTN_ERR_SHAPE"
+    assert call(D=768, dtype="f64", q=None) == "MIATTN_ERR_NULL"   # 768 fp64 is accepted
+
+
+def test_sparse_csr_window(mi):
+    """The LDS window: the 128 keys before a 64-row block's rows (192) where they fit."""
+    assert mi.sparse_csr_window(64, "f32") == 192
+    assert mi.sparse_csr_window(2, "f32") == 192
+    assert 1 <= mi.sparse_csr_window(768, "f64") < mi.sparse_csr_window(768, "f32") < 64
+    w = [mi.sparse_csr_window(d, dt) for d in range(1, 769) for dt in ("f32", "f64")]
+    assert min(w) >= 1 and max(w) == 192
+    for bad, status in (((0, "f32"), "MIATTN_ERR_SHAPE"), ((769, "f32"), "MIATTN_ERR_SHAPE"),
+                        ((64, "bf16"), "MIATTN_ERR_UNSUPPORTED"), ((64, 9), "MIATTN_ERR_DTYPE")):
+        with pytest.raises(mi.MiattnError) as e:
+            mi.sparse_csr_window(*bad)
+        assert mi.STATUS[e.value.status] == status
 
 
 def test_mha_self_attn_fwd_validation(mi):

@@ -5,7 +5,9 @@ end to end: two GPU partial forwards over the halves of K/V merged on the GPU ag
 the oracle's full causal attention.  The sparse kernel is checked on small patterns and
 on the full-size band + random pattern (B 2, N 8, S 4096, D 64).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -16,6 +18,8 @@ import synthetic
 from gpu_utils import (TOL_OUT, check_out, check_stats, dev, empty_like_storage, host_values,
                        nan_stats)
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "paddle_sparse_attention_example.json")
 pytestmark = pytest.mark.gpu
 
 
@@ -155,34 +159,83 @@ def _sparse_gpu(mi, w, scale, dtype="f32"):
     return host_values(out)
 
 
+# head dims: the compile-time sizes (32, 64, 96, 128) and every run-time class (values per
+# lane 1, 2, 4, 8, 12), odd dims (scalar K reads) and even ones, up to the 768 limit
+SPARSE_DIMS = [1, 2, 3, 8, 17, 32, 64, 77, 96, 100, 128, 130, 200, 256, 257, 384, 511, 512,
+               513, 640, 766, 768]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64"])
-@pytest.mark.parametrize("D", [32, 64, 96, 128])
+@pytest.mark.parametrize("D", SPARSE_DIMS)
 def test_sparse_small(mi, D, dtype):
-    w = synthetic.sparse_inputs(51, 2, 3, 300, D, band=16, n_random=80, dtype=dtype)
+    """Band 16 + 80 random columns per row, S 300 (a ragged last block of rows)."""
+    w = synthetic.sparse_inputs(51 + D, 2, 3, 300, D, band=16, n_random=80, dtype=dtype)
     # the entry point takes a float scale: the oracle gets the same float value
     sc = float(np.float32(1 / math.sqrt(D)))
     go = _sparse_gpu(mi, w, sc, dtype)
     wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], sc)
-    check_out(go, wo, dtype)
+    check_out(go, wo, dtype, f"D {D}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("D", [64, 768])
+def test_sparse_band_wider_than_the_window(mi, D, dtype):
+    """A band of 300 keys: at D 64 the LDS window holds the 128 keys before each row of a
+    block, at D 768 only a few (fp32 15, fp64 3), so most entries are gathered from global
+    memory next to window reads, in the same chunks."""
+    w = synthetic.sparse_inputs(60 + D, 1, 2, 700, D, band=300, n_random=20, dtype=dtype)
+    sc = float(np.float32(1 / math.sqrt(D)))
+    go = _sparse_gpu(mi, w, sc, dtype)
+    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], sc)
+    check_out(go, wo, dtype, f"D {D}")
+
+
+def test_sparse_no_locality(mi):
+    """Every row lists 150 uniformly random columns of the whole slice (unsorted, repeats
+    allowed): entries in and out of the window in the same chunk."""
+    rng = np.random.default_rng(61)
+    S, D, N = 500, 64, 2
+    q, k, v = (rng.standard_normal((1, N, S, D), dtype=np.float32) for _ in range(3))
+    cnt = 150
+    offset = np.broadcast_to(np.arange(S + 1, dtype=np.int32) * cnt, (1, N, S + 1)).copy()
+    columns = rng.integers(0, S, size=(1, N, S * cnt)).astype(np.int32)
+    w = dict(q=q, k=k, v=v, offset=offset, columns=columns, nnz=S * cnt, B=1, N=N, S=S, D=D)
+    go = _sparse_gpu(mi, w, 0.125)
+    wo, _, _ = oracle.sparse(q, k, v, offset, columns, 0.125)
+    check_out(go, wo, "f32")
+
+
+def test_sparse_unaligned_key_pointer(mi):
+    """A K pointer 4 bytes past a 16-byte boundary takes the scalar-read kernel."""
+    w = synthetic.sparse_inputs(62, 1, 2, 200, 64, band=32, n_random=30, dtype="f32")
+    q, v = dev(w["q"], "f32"), dev(w["v"], "f32")
+    kbuf = torch.zeros(w["k"].size + 1, dtype=torch.float32, device="cuda:0")
+    kbuf[1:] = torch.from_numpy(np.ascontiguousarray(w["k"]).reshape(-1)).to("cuda:0")
+    k = kbuf[1:]
+    assert k.data_ptr() % 16 == 4
+    off = torch.from_numpy(np.ascontiguousarray(w["offset"])).to("cuda:0")
+    col = torch.from_numpy(np.ascontiguousarray(w["columns"])).to("cuda:0")
+    out = empty_like_storage(q.shape, "f32")
+    mi.sparse_csr_attn(q, k, v, out, off, col, w["nnz"], 1, 2, 200, 64, "f32", 0.125)
+    torch.cuda.synchronize()
+    wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], 0.125)
+    check_out(host_values(out), wo, "f32")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64"])
 def test_sparse_paddle_example(mi, dtype):
-    """The Paddle sparse_attention worked example on the GPU (D = 2 is not built, so the
-    example is embedded in D = 64 with zero padding, which leaves every dot product and
-    every output column of the example unchanged)."""
-    base = np.array([[0, 1], [2, 3], [0, 1], [2, 3]], dtype=np.float32)
-    x = np.zeros((1, 1, 4, 64), dtype=np.float32)
-    x[0, 0, :, :2] = base
-    w = dict(q=x, k=x, v=x, offset=np.array([[[0, 2, 4, 6, 8]]], np.int32),
-             columns=np.array([[[0, 1, 0, 1, 2, 3, 2, 3]]], np.int32), nnz=8, B=1, N=1, S=4, D=64)
-    if dtype == "f64":
-        w = dict(w, q=x.astype(np.float64), k=x.astype(np.float64), v=x.astype(np.float64))
+    """The Paddle sparse_attention worked example on the GPU at its own shape [1, 1, 4, 2],
+    against the output the page prints (fp32 to 8 decimals) and the oracle."""
+    fx = json.load(open(GOLDEN))
+    npdt = np.float32 if dtype == "f32" else np.float64
+    x = np.array(fx["query"], dtype=npdt).reshape(fx["shape"])
+    assert np.array_equal(x, np.array(fx["key"], npdt).reshape(fx["shape"]))
+    w = dict(q=x, k=x, v=x, offset=np.array(fx["offset"], np.int32).reshape(1, 1, 5),
+             columns=np.array(fx["columns"], np.int32).reshape(1, 1, 8), nnz=8, B=1, N=1, S=4, D=2)
     sc = float(np.float32(1 / math.sqrt(2)))
     go = _sparse_gpu(mi, w, sc, dtype)
-    printed = np.array([[1.60885942, 2.60885954], [1.99830270, 2.99830270]] * 2)
-    assert np.max(np.abs(go[0, 0, :, :2] - printed)) < 1e-6
-    assert np.all(go[0, 0, :, 2:] == 0)
+    printed = np.array(fx["printed_output"])
+    assert np.max(np.abs(go[0, 0] - printed)) < 1e-6
     wo, _, _ = oracle.sparse(w["q"], w["k"], w["v"], w["offset"], w["columns"], sc)
     check_out(go, wo, dtype)
 
