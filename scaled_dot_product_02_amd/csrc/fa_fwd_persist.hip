@@ -505,14 +505,18 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
             m_ref = m_new;
         }
         const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-        float rq[4] = {0.f, 0.f, 0.f, 0.f};
+        // four partial row sums, each starting from its first term (no add of 0)
+        float rq[4];
         #pragma unroll
         for (int b = 0; b < PNKB; ++b)
             #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][i], cl2, -mu));
                 s[b][i] = e;
-                rq[i & 3] += e;
+                if (b == 0 && i < 4)
+                    rq[i] = e;
+                else
+                    rq[i & 3] += e;
             }
         l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
         #pragma unroll
