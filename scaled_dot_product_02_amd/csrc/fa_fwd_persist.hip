@@ -161,108 +161,102 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         } else {
             ntd = (p.Sq + R - 1) / R;
         }
-        // wave 0 walks the global order: item i goes to workgroup i mod G in even rounds
-        // and G - 1 - (i mod G) in odd ones; items that see no key get the empty result.
-        // Batches of up to 64 sequences keep the sorted tables in wave 0's lanes (lane k:
-        // sorted entry k, and the bounds of sequence k), read back with readlane.
+        // Item i of the global order goes to workgroup i mod G in even rounds and
+        // G - 1 - (i mod G) in odd ones.  Wave 0 first lists the groups of query-tile levels
+        // that hold the same sequences (level t holds kp x n_groups items, kp the sequences
+        // with more than t tiles, from the largest t down), then every lane takes one of the
+        // workgroup's items and finds its level, sequence and head group from that table;
+        // items that see no key get the empty result.  Batches of up to 64 sequences keep
+        // the sorted tile counts in wave 0's lanes for the table walk.
         if (wave == 0) {
             const int nwg = gridDim.x, wg = blockIdx.x;
-            const bool regs = VARLEN && nseq <= 64;
-            int r_nts = 0, r_perm = 0, r_q0 = 0, r_kv0 = 0, r_lq = 0, r_lkv = 0;
+            int* s_gbase = s_perm + kPersistMaxSeq;    // group x: index of its first item,
+            int* s_gtop = s_gbase + kPersistMaxSeq;    //   its top level,
+            int* s_gper = s_gtop + kPersistMaxSeq;     //   and items per level
+            int n_grp = 1, total = 0;
             if constexpr (VARLEN) {
-                if (regs && lane < nseq) {
-                    r_nts = s_nts[lane];
-                    r_perm = s_perm[lane];
-                    r_q0 = s_q0[lane];
-                    r_kv0 = s_kv0[lane];
-                    r_lq = s_lq[lane];
-                    r_lkv = s_lkv[lane];
-                }
-            }
-            auto tab = [&](int reg, const int* lds, int k) -> int {
-                return regs ? __builtin_amdgcn_readlane(reg, k) : __builtin_amdgcn_readfirstlane(lds[k]);
-            };
-            auto tiles_sorted = [&](int k) -> int {
-                if constexpr (VARLEN) return tab(r_nts, s_nts, k);
-                else return ntd;
-            };
-            // cursor: level t (query tiles from the largest down), the global index of its
-            // first item, and kp = sequences (sorted) with more than t tiles; the levels from
-            // t down to the next sorted tile count all hold kp x n_groups items, so the walk
-            // jumps over them at once
-            int t = nseq > 0 ? tiles_sorted(0) - 1 : -1;
-            int kp = 0, base = 0;
-            if constexpr (VARLEN) {
+                const bool regs = nseq <= 64;
+                const int r_nts = regs && lane < nseq ? s_nts[lane] : 0;
+                auto tiles_sorted = [&](int k) -> int {
+                    return regs ? __builtin_amdgcn_readlane(r_nts, k) : __builtin_amdgcn_readfirstlane(s_nts[k]);
+                };
+                int t = nseq > 0 ? tiles_sorted(0) - 1 : -1;
+                int kp = 0, base = 0;
                 while (kp < nseq && tiles_sorted(kp) > t) ++kp;
-            } else {
-                kp = nseq;
-            }
-            int n = 0, steps = 0;
-            for (int k = 0; t >= 0 && n < MAXI; ++k) {
-                const int i = k * nwg + ((k & 1) ? nwg - 1 - wg : wg);
+                n_grp = 0;
                 while (t >= 0) {
                     const int per = kp * n_groups;
                     const int stop = kp < nseq ? tiles_sorted(kp) : 0;
-                    const int span = (t - stop + 1) * per;
-                    if (i < base + span) {
-                        const int d = (i - base) / per;
-                        t -= d;
-                        base += d * per;
-                        break;
+                    if (lane == 0) {
+                        s_gbase[n_grp] = base;
+                        s_gtop[n_grp] = t;
+                        s_gper[n_grp] = per;
                     }
-                    base += span;
+                    ++n_grp;
+                    base += (t - stop + 1) * per;
                     t = stop - 1;
+                    while (kp < nseq && tiles_sorted(kp) > t) ++kp;
+                }
+                total = base;
+            } else {
+                total = ntd * nseq * n_groups;
+            }
+            int n = 0, steps = 0;
+            for (int k0 = 0;; k0 += 64) {
+                const int k = k0 + lane;
+                const int i = k * nwg + ((k & 1) ? nwg - 1 - wg : wg);
+                const bool valid = k0 * nwg < total && i < total;
+                if (!__any(valid)) break;
+                PItem it{};
+                it.T1 = 0;
+                if (valid) {
+                    int base = 0, top = ntd - 1, per = nseq * n_groups;
                     if constexpr (VARLEN) {
-                        while (kp < nseq && tiles_sorted(kp) > t) ++kp;
-                    }
-                }
-                if (t < 0) break;
-                PItem it;
-                const int j = i - base;
-                const int kk = j / n_groups;
-                it.g = j - kk * n_groups;
-                it.t = t;
-                if constexpr (VARLEN) {
-                    it.b = tab(r_perm, s_perm, kk);
-                    it.q0 = tab(r_q0, s_q0, it.b);
-                    it.kv0 = tab(r_kv0, s_kv0, it.b);
-                    it.len_q = tab(r_lq, s_lq, it.b);
-                    it.len_kv = tab(r_lkv, s_lkv, it.b);
-                } else {
-                    it.b = kk;
-                    it.q0 = it.kv0 = 0;
-                    it.len_q = p.Sq;
-                    it.len_kv = p.Skv;
-                }
-                it.r0 = it.t * R;
-                it.r1 = min(it.len_q, it.r0 + R);
-                it.off = p.align_br ? it.len_kv - it.len_q : 0;
-                // causal: rows [r0, r1) see keys 0 .. r1 - 1 + off
-                const int hi = max(0, min(it.r1 + it.off, it.len_kv));
-                it.T0 = 0;
-                it.T1 = (hi + PBN - 1) / PBN;
-                const int h0 = it.g * HPI;
-                if (it.T1 == 0) {
-                    // no visible key: every row of the item's heads gets the empty result
-                    for (int hh = 0; hh < HPI; ++hh)
-                        for (int qi = it.r0 + lq; qi < it.r1; qi += 32) {
-                            T* orow = (T*)p.out + (int64_t)it.b * p.o_sb + (it.q0 + qi) * p.o_ss +
-                                      (int64_t)(h0 + hh) * p.o_sh + 4 * hf;
-                            #pragma unroll
-                            for (int r = 0; r < C::RT; ++r)
-                                #pragma unroll
-                                for (int g4 = 0; g4 < 4; ++g4) *(X4*)(orow + 32 * r + 8 * g4) = X4{};
-                            if (hf == 0) {
-                                const int64_t si = (int64_t)it.b * p.st_sb + (int64_t)(h0 + hh) * p.st_sh + it.q0 + qi;
-                                if (p.smax) p.smax[si] = -INFINITY;
-                                if (p.ssum) p.ssum[si] = 0.f;
-                            }
+                        // the last group that starts at or before item i
+                        int lo = 0, hi = n_grp - 1;
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if (s_gbase[mid] <= i) lo = mid;
+                            else hi = mid - 1;
                         }
-                    continue;
+                        base = s_gbase[lo];
+                        top = s_gtop[lo];
+                        per = s_gper[lo];
+                    }
+                    const int d = (i - base) / per;
+                    const int j = i - base - d * per;
+                    const int kk = j / n_groups;
+                    it.g = j - kk * n_groups;
+                    it.t = top - d;
+                    if constexpr (VARLEN) {
+                        it.b = s_perm[kk];
+                        it.q0 = s_q0[it.b];
+                        it.kv0 = s_kv0[it.b];
+                        it.len_q = s_lq[it.b];
+                        it.len_kv = s_lkv[it.b];
+                    } else {
+                        it.b = kk;
+                        it.q0 = it.kv0 = 0;
+                        it.len_q = p.Sq;
+                        it.len_kv = p.Skv;
+                    }
+                    it.r0 = it.t * R;
+                    it.r1 = min(it.len_q, it.r0 + R);
+                    it.off = p.align_br ? it.len_kv - it.len_q : 0;
+                    // causal: rows [r0, r1) see keys 0 .. r1 - 1 + off
+                    const int vis = max(0, min(it.r1 + it.off, it.len_kv));
+                    it.T0 = 0;
+                    it.T1 = (vis + PBN - 1) / PBN;
                 }
-                if (lane == 0) {
+                const bool live = valid && it.T1 > 0;
+                // records of the live items in item order (lanes below this one first)
+                const uint64_t live_mask = __ballot(live);
+                const int pos = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(live_mask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)live_mask, 0u));
+                if (live && pos < MAXI) {
+                    const int h0 = it.g * HPI;
                     const int kvh = h0 / p.group;
-                    PRec& rc = s_rec[n];
+                    PRec& rc = s_rec[pos];
                     rc.kaddr = (int64_t)p.k + ((int64_t)it.b * p.k_sb + it.kv0 * p.k_ss + (int64_t)kvh * p.k_sh) * 2;
                     rc.vaddr = (int64_t)p.v + ((int64_t)it.b * p.v_sb + it.kv0 * p.v_ss + (int64_t)kvh * p.v_sh) * 2;
                     rc.qaddr = (int64_t)p.q + ((int64_t)it.b * p.q_sb + (it.q0 + it.r0) * p.q_ss + (int64_t)h0 * p.q_sh) * 2;
@@ -274,8 +268,37 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                     rc.T0 = it.T0;
                     rc.T1 = it.T1;
                 }
-                ++n;
-                steps += it.T1 - it.T0;
+                int st = live && pos < MAXI ? it.T1 - it.T0 : 0;
+                #pragma unroll
+                for (int o = 32; o > 0; o >>= 1) st += __shfl_xor(st, o);
+                steps += st;
+                n = min(MAXI, n + (int)__builtin_popcountll(live_mask));
+                // items that see no key (rare): the wave writes their empty result one by one
+                uint64_t empty_mask = __ballot(valid && it.T1 == 0);
+                while (empty_mask) {
+                    const int e = __builtin_ctzll(empty_mask);
+                    empty_mask &= empty_mask - 1;
+                    const int eb = __builtin_amdgcn_readlane(it.b, e);
+                    const int eg = __builtin_amdgcn_readlane(it.g, e);
+                    const int er0 = __builtin_amdgcn_readlane(it.r0, e);
+                    const int er1 = __builtin_amdgcn_readlane(it.r1, e);
+                    const int64_t eq0 = __builtin_amdgcn_readlane((int)it.q0, e);
+                    const int h0 = eg * HPI;
+                    for (int hh = 0; hh < HPI; ++hh)
+                        for (int qi = er0 + lq; qi < er1; qi += 32) {
+                            T* orow = (T*)p.out + (int64_t)eb * p.o_sb + (eq0 + qi) * p.o_ss +
+                                      (int64_t)(h0 + hh) * p.o_sh + 4 * hf;
+                            #pragma unroll
+                            for (int r = 0; r < C::RT; ++r)
+                                #pragma unroll
+                                for (int g4 = 0; g4 < 4; ++g4) *(X4*)(orow + 32 * r + 8 * g4) = X4{};
+                            if (hf == 0) {
+                                const int64_t si = (int64_t)eb * p.st_sb + (int64_t)(h0 + hh) * p.st_sh + eq0 + qi;
+                                if (p.smax) p.smax[si] = -INFINITY;
+                                if (p.ssum) p.ssum[si] = 0.f;
+                            }
+                        }
+                }
             }
             if (lane == 0) {
                 s_nitems = n;
@@ -349,11 +372,15 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         #pragma unroll
         for (int r = 0; r < 2; ++r) voff[2 * u + r] = (uint32_t)((2 * kp[u] + r) * vrb + 16 * vc[u]);
 
-    // load the loader's next tile (zeros past the list) and advance the loader
+    // load the loader's next tile (zeros past the list) and advance the loader; the row
+    // count is clamped with scalar instructions (the compiler would form a vector
+    // v_med3_i32 and multiply on the vector ALU, which the softmax of the partner wave needs)
     auto load_next = [&](u32x4 (&stage)[C::SREG]) {
         if (l_tile == l_T1 && l_k + 1 < n_items) loader_item(++l_k);
         const int j0 = l_tile * PBN;
-        const int rows = l_tile < l_T1 ? max(0, min(PBN, l_len - j0)) : 0;
+        int rows = l_len - j0;
+        asm("s_max_i32 %0, %0, 0\n\ts_min_i32 %0, %0, %1" : "+s"(rows) : "n"(PBN));
+        if (l_tile >= l_T1) rows = 0;
         const __amdgpu_buffer_rsrc_t rk = rsrc(l_kb + (int64_t)j0 * krb, rows * krb);
         const __amdgpu_buffer_rsrc_t rv = rsrc(l_vb + (int64_t)j0 * vrb, rows * vrb);
         #pragma unroll
