@@ -334,7 +334,7 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
  * blocks of 64 ([64 j, 64 j + 64) of each slice, the last one ragged), and an entry of a row
  * in a block that ends at row r1 (exclusive) is read from the LDS copy when its column lies
  * in [max(0, r1 - W), r1), W the value returned; every other entry is gathered from global
- * memory.  For 16-byte aligned K, V and out (the value may be larger for unaligned ones).
+ * memory.  For 16-byte aligned Q, K, V and out (the value may differ for unaligned ones).
  * A property of this implementation (for measurement), not of the Paddle page.
  *   Returns W >= 1, or minus the status sparse_csr_attn would return for this D and dtype.
  */

@@ -91,7 +91,7 @@ hipError_t launch_fa_fwd_persist(const FaParams& p, int D, bool f16, hipStream_t
 int fa_persist_heads_per_item(int group);
 int fa_wide_tile_m(int dtype);
 hipError_t launch_lse_merge(const MergeParams& p, int dtype, hipStream_t stream);
-// the CSR kernel; aligned16: K, V and out are 16-byte aligned (vector row accesses)
+// the CSR kernel; aligned16: Q, K, V and out are 16-byte aligned (vector row accesses)
 hipError_t launch_sparse_csr(const SparseParams& p, bool f64, bool aligned16, hipStream_t stream);
 // whether the CSR kernel takes head dim D (1..768; fp64 at 768 still fits its LDS)
 bool sparse_head_dim_fits(int D, bool f64);

@@ -517,8 +517,8 @@ miattn_status_t sparse_csr_attn(const void* q, const void* k, const void* v, voi
     p.B = (int32_t)B; p.N = (int32_t)N; p.S = (int32_t)S; p.D = (int32_t)D;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.scale_log2_d = (double)scale * 1.4426950408889634074;
-    // vector reads of K / V rows and vector stores of output rows
-    const bool aligned16 = (((uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) == 0;
+    // vector reads of Q / K / V rows and vector stores of output rows
+    const bool aligned16 = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) == 0;
     return launch_sparse_csr(p, dtype == MIATTN_F64, aligned16, (hipStream_t)stream) == hipSuccess
                ? MIATTN_OK : MIATTN_ERR_LAUNCH;
 }

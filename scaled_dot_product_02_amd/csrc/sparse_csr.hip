@@ -5,7 +5,7 @@
 // Row i of slice (b, n) attends to the key rows listed in
 // columns[b][n][offset[b][n][i] .. offset[b][n][i+1]).
 //
-// A workgroup (16 waves) takes RB = 64 consecutive rows of one slice.  Rows that are
+// A workgroup (8 waves) takes RB = 64 consecutive rows of one slice.  Rows that are
 // close to each other mostly list the same nearby keys (a sliding-window band is the
 // common pattern, e.g. the page's example and local + random layouts), so the workgroup
 // first copies the K and V rows of a key window into LDS with coalesced loads: the WL keys
@@ -14,23 +14,26 @@
 // from LDS; the others are gathered from global memory (L2), so any CSR pattern is served
 // and one without locality costs only the window copy.
 //
-// Each wave takes rows of the block in turn.  Per row:
+// Each wave takes rows of the block in turn.  fp32 rows of 32, 64 or 128 and fp64 rows of
+// 32 or 64 take the grouped layout described at grouped_row below; every other row:
 //   * score phase: lane e takes entry e of a 64-entry chunk and forms the whole dot
 //     product q . k_col (the query row is broadcast from LDS, the key row comes from the
 //     window or from global memory through one generic pointer, so a chunk that mixes
 //     both has no divergent branch);
-//   * chunk max and sum by wave butterflies; the running max / sum are rescaled once per
+//   * chunk max and sum by wave reductions; the running max / sum are rescaled once per
 //     chunk (online softmax in the log2 domain);
 //   * value phase: the chunk's (probability, column) pairs are broadcast lane by lane and
 //     every lane accumulates its own head-dim slice of sum_c p_c v_c (coalesced row reads
 //     from the window or global memory), several value rows per batch with all their
 //     loads in flight together.
+#include <type_traits>
+
 #include "fa_params.h"
 
 namespace miattn {
 namespace {
 
-constexpr int NT = 1024;                  // threads per workgroup (16 waves)
+constexpr int NT = 512;                   // threads per workgroup (8 waves)
 constexpr int NW = NT / 64;
 constexpr int RB = kSparseRowBlock;       // rows per workgroup
 constexpr int kBand = 128;                // keys before a row that the window aims to hold
@@ -72,6 +75,28 @@ __device__ inline double lane_reduce(double x)
     }
     return x;
 }
+// x summed over the DL lanes that share lane / DL (DL = 2, 4, 8 or 16): DPP quad swaps, then
+// half-row and row mirrors; fp64: shuffles
+template <int DL>
+__device__ inline float group_sum(float x)
+{
+    if constexpr (DL >= 2)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    if constexpr (DL >= 4)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    if constexpr (DL >= 8)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+    if constexpr (DL >= 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+    return x;
+}
+template <int DL>
+__device__ inline double group_sum(double x)
+{
+    #pragma unroll
+    for (int o = 1; o < DL; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
 template <typename T>
 __device__ inline T wave_max(T x) { return lane_reduce<1, true>(x); }
 template <typename T>
@@ -93,17 +118,17 @@ __device__ inline double lane_value(double x, int e)
 // The layout of a workgroup's LDS for head dim D: per wave one query row, then the K
 // window (row stride KS, padded by 16 bytes so that lanes reading consecutive window rows
 // at the same offset hit different banks) and the V window (row stride VS, padded by 64
-// bytes: the grouped value phase reads 64-byte pieces of 16 rows at once, and consecutive
-// rows then start 16 banks apart).
+// bytes: the grouped layout below reads 64-byte pieces of 16 rows at once, and consecutive
+// rows then start 16 banks apart; grouped rows read K that way too).
 struct SparseLds {
     int QS, KS, VS, WL;
 };
 
-__host__ __device__ inline SparseLds sparse_lds(int D, int esz, int ve)
+__host__ __device__ inline SparseLds sparse_lds(int D, int esz, int ve, bool grouped)
 {
     SparseLds l;
-    l.QS = (D + ve - 1) / ve * ve;
-    l.KS = D + (ve > 1 ? ve : 1);
+    l.QS = grouped ? 0 : (D + ve - 1) / ve * ve;     // grouped rows keep the query in registers
+    l.KS = grouped ? D + 64 / esz : D + (ve > 1 ? ve : 1);
     l.VS = D + 64 / esz;
     const int room = kLdsBytes / esz - NW * l.QS;
     const int wl = room / (l.KS + l.VS);
@@ -120,18 +145,20 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
     typedef T V __attribute__((ext_vector_type(VE)));
     typedef __attribute__((address_space(3))) const V LVc;    // LDS
     typedef __attribute__((address_space(1))) const V GVc;    // global
-    // grouped value phase (compile-time head dims whose rows are whole 64-byte slices that
-    // tile a wave): DL lanes per V row, NV elements per lane, EG entry groups, JB entries
-    // of a group in flight per batch
+    // grouped rows (compile-time head dims whose rows are whole 64-byte slices that tile a
+    // wave): DL lanes per row, NV elements per lane, EG entry groups, JB entries of a group
+    // loaded per batch
     constexpr int RBYTES = DC * (int)sizeof(T);
-    constexpr bool GV = DC > 0 && VE > 1 && RBYTES % 64 == 0 && 64 % (RBYTES / 64 ? RBYTES / 64 : 1) == 0;
+    // (fp64 rows of 1 KB would need 16 lanes of scores and spill: they take the other path)
+    constexpr bool GV = DC > 0 && VE > 1 && RBYTES % 64 == 0 && RBYTES <= 512 &&
+                        64 % (RBYTES / 64 ? RBYTES / 64 : 1) == 0;
     constexpr int DL = GV ? RBYTES / 64 : 1;
     constexpr int NV = 64 / (int)sizeof(T);
     constexpr int EG = 64 / DL;
-    constexpr int JB = (RBYTES > 256 || sizeof(T) == 8) ? 2 : DL < 4 ? DL : 4;
+    constexpr int JB = sizeof(T) == 8 ? 1 : DL < 2 ? DL : 2;
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     const int D = DC ? DC : p.D;
-    const SparseLds L = sparse_lds(D, (int)sizeof(T), VE);
+    const SparseLds L = sparse_lds(D, (int)sizeof(T), VE, GV);
     T* qs_all = (T*)lds;
     T* ks = qs_all + NW * L.QS;
     T* vs = ks + L.WL * L.KS;
@@ -175,8 +202,145 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
     typedef __attribute__((address_space(1))) const int32_t GI;
     GI* colg = (GI*)(p.columns + bn * p.nnz);
     T* qs = qs_all + wave * L.QS;
+
+    // Grouped rows (compile-time head dims whose rows tile a wave in 64-byte pieces): lane =
+    // (entry group eg, position dg among the DL lanes of a row).  Group eg takes entries eg,
+    // eg + EG, ... of a 64-entry chunk; lane dg holds the 16-byte pieces dg, dg + DL,
+    // dg + 2 DL, dg + 3 DL of the query row and reads the same pieces of those entries' K
+    // and V rows (each load instruction reads 16 DL contiguous bytes of a row).  A score is
+    // the group's sum of its lanes' partial dot products; every lane of a group then holds
+    // the group's scores and probabilities, so no value moves between lanes until the end
+    // of the row, where the groups' partial outputs are added up.  Entries past the chunk
+    // take the window's first key with probability 0.
+    auto grouped_row = [&](int i, int64_t row) {
+        typedef T V16 __attribute__((ext_vector_type(16 / sizeof(T))));
+        typedef __attribute__((address_space(3))) const V16 LV16;
+        typedef __attribute__((address_space(1))) const V16 GV16;
+        constexpr int EPV = 16 / (int)sizeof(T);
+        const int eg = lane / DL, dg = lane % DL;
+        V16 qv[4];
+        GV16* qrow = (GV16*)(q + row * DC) + dg;
+        #pragma unroll
+        for (int x = 0; x < 4; ++x) qv[x] = qrow[x * DL];
+        const int e0 = off[i], e1 = off[i + 1];
+        T m_run = -INFINITY, l_run = 0;
+        T ga[NV];
+        #pragma unroll
+        for (int u = 0; u < NV; ++u) ga[u] = 0;
+        for (int base = e0; base < e1; base += 64) {
+            const int cnt = min(64, e1 - base);
+            int cj[DL];
+            bool any_in = false, all_in_l = true;
+            #pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                const int e = eg + EG * j;
+                cj[j] = e < cnt ? colg[base + e] : w0;
+                const bool in = (unsigned)(cj[j] - w0) < (unsigned)wl;
+                any_in |= in;
+                all_in_l &= in;
+            }
+            // chunk-wide: every row in the window (LDS reads), none (global reads), or both
+            // (generic reads); one straight-line body per case
+            const bool all_in = __all(all_in_l), none_in = !__any(any_in);
+            auto body = [&](auto mode) {
+                constexpr int M = decltype(mode)::value;   // 0 LDS, 1 global, 2 either
+                auto load4 = [&](V16 (&dst)[4], const T* win, int stride, const T* glob, int c) {
+                    if constexpr (M == 0) {
+                        LV16* r = (LV16*)(win + (c - w0) * stride) + dg;
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x) dst[x] = r[x * DL];
+                    } else if constexpr (M == 1) {
+                        GV16* r = (GV16*)(glob + (int64_t)c * DC) + dg;
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x) dst[x] = r[x * DL];
+                    } else {
+                        const int wr = c - w0;
+                        const V16* r = (const V16*)((unsigned)wr < (unsigned)wl ? win + wr * stride
+                                                                                : glob + (int64_t)c * DC) + dg;
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x) dst[x] = r[x * DL];
+                    }
+                };
+                T sj[DL];
+                #pragma unroll
+                for (int j0 = 0; j0 < DL; j0 += JB) {
+                    V16 kk[JB][4];
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j) load4(kk[j], ks, L.KS, kb, cj[j0 + j]);
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j) {
+                        T acc = 0;
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            #pragma unroll
+                            for (int y = 0; y < EPV; ++y) acc = fma(qv[x][y], kk[j][x][y], acc);
+                        sj[j0 + j] = acc;
+                    }
+                    // keep the next batch's loads behind this one (registers)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                T mloc = -INFINITY;
+                #pragma unroll
+                for (int j = 0; j < DL; ++j) {
+                    sj[j] = eg + EG * j < cnt ? group_sum<DL>(sj[j]) * scale_log2 : (T)-INFINITY;
+                    mloc = fmax(mloc, sj[j]);
+                }
+                const T m_new = fmax(m_run, lane_reduce<DL, true>(mloc));
+                const T alpha = exp2_t(m_run - m_new);
+                T psum = 0;
+                #pragma unroll
+                for (int j = 0; j < DL; ++j) {
+                    sj[j] = exp2_t(sj[j] - m_new);
+                    psum += sj[j];
+                }
+                l_run = l_run * alpha + lane_reduce<DL, false>(psum);
+                #pragma unroll
+                for (int u = 0; u < NV; ++u) ga[u] *= alpha;
+                #pragma unroll
+                for (int j0 = 0; j0 < DL; j0 += JB) {
+                    V16 vv[JB][4];
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j) load4(vv[j], vs, L.VS, vb, cj[j0 + j]);
+                    #pragma unroll
+                    for (int j = 0; j < JB; ++j)
+                        #pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            #pragma unroll
+                            for (int y = 0; y < EPV; ++y)
+                                ga[x * EPV + y] = fma(sj[j0 + j], vv[j][x][y], ga[x * EPV + y]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                m_run = m_new;
+            };
+            if (all_in)
+                body(std::integral_constant<int, 0>{});
+            else if (none_in)
+                body(std::integral_constant<int, 1>{});
+            else
+                body(std::integral_constant<int, 2>{});
+        }
+        // add up the entry groups' partial sums (lanes with the same dg) and store
+        const T inv = l_run > 0 ? (T)1 / l_run : (T)0;
+        #pragma unroll
+        for (int u = 0; u < NV; ++u) ga[u] = lane_reduce<DL, false>(ga[u]);
+        if (lane < DL) {
+            V16* dst = (V16*)(out + row * DC) + lane;
+            #pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                V16 r;
+                #pragma unroll
+                for (int y = 0; y < EPV; ++y) r[y] = ga[x * EPV + y] * inv;
+                dst[x * DL] = r;
+            }
+        }
+    };
+
     for (int i = r0 + wave; i < r1; i += NW) {
         const int64_t row = bn * p.S + i;
+        if constexpr (GV) {
+            grouped_row(i, row);
+            continue;
+        }
         // the wave's query row (LDS operations of one wave complete in order, so the
         // previous row's reads are done before these writes land)
         for (int d = lane; d < D; d += 64) qs[d] = q[row * D + d];
@@ -185,9 +349,6 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
         T o[PL];
         #pragma unroll
         for (int u = 0; u < PL; ++u) o[u] = 0;
-        T ga[GV ? NV : 1];
-        #pragma unroll
-        for (int u = 0; u < (GV ? NV : 1); ++u) ga[u] = 0;
 
         for (int base = e0; base < e1; base += 64) {
             const int cnt = min(64, e1 - base);
@@ -241,56 +402,6 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
             const T alpha = exp2_t(m_run - m_new);
             const T pv = lane < cnt ? exp2_t(sc - m_new) : (T)0;
             l_run = l_run * alpha + wave_sum(pv);
-            if constexpr (GV) {
-                // grouped value phase: lane = (entry group eg, position dg among the DL
-                // lanes of a row); group eg takes entries eg, eg + EG, ... of the chunk, and
-                // lane dg reads the 16-byte pieces dg, dg + DL, dg + 2 DL, dg + 3 DL of those
-                // V rows (so each load instruction reads 16 DL contiguous bytes per row; a
-                // batch of entries in flight at once) into a partial sum, which the groups
-                // add up at the end of the row.  Entries past cnt have p = 0 and column 0.
-                #pragma unroll
-                for (int u = 0; u < NV; ++u) ga[u] *= alpha;
-                const int eg = lane / DL, dg = lane % DL;
-                typedef T V16 __attribute__((ext_vector_type(16 / sizeof(T))));
-                constexpr int EPV = 16 / (int)sizeof(T);
-                #pragma unroll 1
-                for (int j0 = 0; j0 < DL; j0 += JB) {
-                    V16 vv[JB][4];
-                    T pj[JB];
-                    typedef __attribute__((address_space(3))) const V16 LV16;
-                    typedef __attribute__((address_space(1))) const V16 GV16;
-                    #pragma unroll
-                    for (int j = 0; j < JB; ++j) {
-                        const int e = eg + EG * (j0 + j);
-                        const int ce = __shfl(c, e);
-                        pj[j] = __shfl(pv, e);
-                        const int wre = ce - w0;
-                        if (all_in) {
-                            LV16* vr = (LV16*)(vs + wre * L.VS) + dg;
-                            #pragma unroll
-                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
-                        } else if (none_in) {
-                            GV16* vr = (GV16*)(vb + (int64_t)ce * DC) + dg;
-                            #pragma unroll
-                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
-                        } else {
-                            const V16* vr = (const V16*)((unsigned)wre < (unsigned)wl ? vs + wre * L.VS
-                                                                                      : vb + (int64_t)ce * DC) + dg;
-                            #pragma unroll
-                            for (int x = 0; x < 4; ++x) vv[j][x] = vr[x * DL];
-                        }
-                    }
-                    #pragma unroll
-                    for (int j = 0; j < JB; ++j)
-                        #pragma unroll
-                        for (int x = 0; x < 4; ++x)
-                            #pragma unroll
-                            for (int y = 0; y < EPV; ++y)
-                                ga[x * EPV + y] = fma(pj[j], vv[j][x][y], ga[x * EPV + y]);
-                }
-                m_run = m_new;
-                continue;
-            }
             #pragma unroll
             for (int u = 0; u < PL; ++u) o[u] *= alpha;
             // value rows in batches of VB entries: all loads of a batch are in flight
@@ -328,24 +439,6 @@ __global__ __launch_bounds__(NT) void sparse_csr_kernel(SparseParams p)
             m_run = m_new;
         }
         const T inv = l_run > 0 ? (T)1 / l_run : (T)0;
-        if constexpr (GV) {
-            // add up the entry groups' partial sums (lanes with the same slice dg)
-            #pragma unroll
-            for (int u = 0; u < NV; ++u) ga[u] = lane_reduce<DL, false>(ga[u]);
-            if (lane < DL) {
-                typedef T V16 __attribute__((ext_vector_type(16 / sizeof(T))));
-                constexpr int EPV = 16 / (int)sizeof(T);
-                V16* dst = (V16*)(out + row * DC) + lane;
-                #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    V16 r;
-                    #pragma unroll
-                    for (int y = 0; y < EPV; ++y) r[y] = ga[x * EPV + y] * inv;
-                    dst[x * DL] = r;
-                }
-            }
-            continue;
-        }
         #pragma unroll
         for (int u = 0; u < PL; ++u)
             if ((DC % 64 == 0 && DC) || lane + 64 * u < D) out[row * D + lane + 64 * u] = o[u] * inv;
@@ -395,13 +488,18 @@ hipError_t launch_t(const SparseParams& p, bool aligned16, hipStream_t stream)
 int sparse_window_keys(int D, bool f64, bool aligned16)
 {
     const int ve = f64 ? 2 : 4;
-    return sparse_lds(D, f64 ? 8 : 4, aligned16 && D % ve == 0 ? ve : 1).WL;
+    // compile-time head dims whose rows tile a wave in 64-byte pieces take the grouped layout
+    const int rb = D * (f64 ? 8 : 4);
+    const bool grouped = aligned16 && (D == 32 || D == 64 || D == 128) && rb % 64 == 0 && rb <= 512 &&
+                         64 % (rb / 64) == 0;
+    return sparse_lds(D, f64 ? 8 : 4, aligned16 && D % ve == 0 ? ve : 1, grouped).WL;
 }
 
 bool sparse_head_dim_fits(int D, bool f64)
 {
     // the window must hold at least one key row beside the query rows
-    return D >= 1 && D <= 768 && sparse_lds(D, f64 ? 8 : 4, f64 ? 2 : 4).WL >= 1;
+    return D >= 1 && D <= 768 && sparse_lds(D, f64 ? 8 : 4, f64 ? 2 : 4, false).WL >= 1 &&
+           sparse_lds(D, f64 ? 8 : 4, 1, false).WL >= 1;
 }
 
 hipError_t launch_sparse_csr(const SparseParams& p, bool f64, bool aligned16, hipStream_t stream)
