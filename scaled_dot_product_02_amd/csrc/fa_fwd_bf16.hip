@@ -447,7 +447,9 @@ void fa_fwd_bf16_kernel(FaParams p)
     // Step t is two phases, each closed by a barrier:
     //   M: prefetch tile t+PF into registers; S(t) = K(t) Q^T and O += P(t-1) V(t-1) on the
     //      matrix cores (the P V MFMAs cover the latency of S(t));
-    //   S: softmax(t) on the vector ALUs; land tile t+2 in LDS.
+    //   S: land tile t+2 in LDS (its buffer's last reader finished before this phase
+    //      began), then softmax(t) on the vector ALUs (the mask tensor instance, whose
+    //      prefetch is one tile shallower, lands the tile after the softmax).
     // Waves 4-7 run the same code one phase behind waves 0-3, so on every SIMD one wave is
     // in its M phase while the other is in its S phase and the matrix cores and the vector
     // ALUs work at the same time.  The M phase runs at raised wave priority: the SIMD
@@ -471,8 +473,12 @@ void fa_fwd_bf16_kernel(FaParams p)
         if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
+        // the staged tile goes to LDS first, so that the writes complete under the softmax
+        // (with the shallower prefetch of the mask tensor instance its loads were issued
+        // only one phase earlier: there it goes last)
+        if constexpr (PF == 3) store_tile(t + 2, sto);
         if (wave_active(t)) softmax(t, sa, pp);
-        store_tile(t + 2, sto);
+        if constexpr (PF != 3) store_tile(t + 2, sto);
         __syncthreads();
     };
 

@@ -604,8 +604,8 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     // Step s (stream position s, LDS slot s % 4) is two phases, each closed by a barrier:
     //   M: load stream position s + 3; S(s) = K(s) Q^T; O += P(s-1) V(s-1) (at an item's
     //      first tile, that is the previous item's last P V);
-    //   S: at an item's first tile, the previous item's epilogue; softmax(s); land position
-    //      s + 2 in LDS.
+    //   S: land position s + 2 in LDS (its slot's last reader finished before this
+    //      phase began); at an item's first tile, the previous item's epilogue; softmax(s).
     // The next item's Q is loaded at the start of the item's last softmax phase, once the
     // current item's last S = K Q^T has been issued.
     // Waves 4-7 run one phase behind waves 0-3, so each SIMD always has one wave in each
@@ -624,6 +624,8 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         if (p_act) pv((s - 1) & (PNBUF - 1), pp);
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
+        // the staged tile goes to LDS first, so that the writes complete under the softmax
+        store_tile((s + 2) & (PNBUF - 1), sto);
         const bool last = c_tile + 1 == c_T1;
         if (last && c_k + 1 < n_items) load_q(c_k + 1);
         if (first) {
@@ -638,7 +640,6 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
             c_tile = c_T0;
             first = true;
         }
-        store_tile((s + 2) & (PNBUF - 1), sto);
         ++s;
         __syncthreads();
     };
