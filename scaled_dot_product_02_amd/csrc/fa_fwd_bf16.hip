@@ -94,7 +94,7 @@ struct Cfg {
 
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
-// masks are read one tile ahead, and tiles are prefetched one step less deep to make room.
+// each tile's mask words are loaded at the end of the previous tile's softmax phase.
 // DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
 template <int D, int DV, bool MASKED, bool DROP>
 using KCfg = Cfg<D, DV, fa_four_waves(D, MASKED || DROP)>;
@@ -106,8 +106,8 @@ void fa_fwd_bf16_kernel(FaParams p)
     using C = KCfg<D, DV, MASKED, DROP>;
     constexpr int NT = C::NT, BM = C::BM, BN = C::BN, NKB = C::NKB;
     static_assert(!(C::BIG && (MASKED || DROP)), "the mask tensor and dropout assume 64-key tiles");
-    constexpr int PF = MASKED ? 2 : ::miattn::PF;
-    constexpr int LDSD = MASKED ? 3 : ::miattn::LDSD;
+    constexpr int PF = ::miattn::PF;
+    constexpr int LDSD = ::miattn::LDSD;
     using X8 = typename Elem<T>::v8;   // one MFMA operand: 8 elements
     using X4 = typename Elem<T>::v4;
     __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF * C::KBUF];
@@ -234,10 +234,9 @@ void fa_fwd_bf16_kernel(FaParams p)
         const int n = __builtin_amdgcn_readfirstlane((int)bytes);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
     };
-    // explicit mask: this lane's row; the 8 words of the next tile in flight and those of
-    // the current tile (byte e of word 4b + g: key 32b + 8g + 4hf + e of the tile)
+    // explicit mask: this lane's row; the 8 words of the tile in softmax, loaded a step
+    // ahead (byte e of word 4b + g: key 32b + 8g + 4hf + e of the tile)
     unsigned mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    unsigned mcur[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t rmask;
     uint32_t moff = 0;
     if constexpr (MASKED) {
@@ -346,7 +345,7 @@ void fa_fwd_bf16_kernel(FaParams p)
             for (int b = 0; b < NKB; ++b)
                 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if ((mcur[4 * b + (i >> 2)] >> (8 * (i & 3)) & 0xffu) != 0u) s[b][i] = -INFINITY;
+                    if ((mw[4 * b + (i >> 2)] >> (8 * (i & 3)) & 0xffu) != 0u) s[b][i] = -INFINITY;
         }
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
@@ -462,11 +461,6 @@ void fa_fwd_bf16_kernel(FaParams p)
     f32x16 sa[NKB];
     const bool late = C::NW == 8 && wave >= 4;   // one wave per SIMD: no partner to skew against
     auto step = [&](int t, u32x4 (&ld)[C::SREG], u32x4 (&sto)[C::SREG]) {
-        if constexpr (MASKED) {
-            #pragma unroll
-            for (int k = 0; k < 8; ++k) mcur[k] = mw[k];   // mask of tile t, read one step earlier
-            if (t + 1 < T1) load_mask(t + 1);
-        }
         __builtin_amdgcn_s_setprio(3);
         load_tile(t + PF, ld);
         if (wave_active(t)) qk(t, sa);
@@ -474,11 +468,14 @@ void fa_fwd_bf16_kernel(FaParams p)
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         // the staged tile goes to LDS first, so that the writes complete under the softmax
-        // (with the shallower prefetch of the mask tensor instance its loads were issued
-        // only one phase earlier: there it goes last)
+        // (with a shallower prefetch its loads were issued only one phase earlier: there it
+        // goes last)
         if constexpr (PF == 3) store_tile(t + 2, sto);
         if (wave_active(t)) softmax(t, sa, pp);
         if constexpr (PF != 3) store_tile(t + 2, sto);
+        // the mask words of the next tile, used by the next softmax (a step from now)
+        if constexpr (MASKED)
+            if (t + 1 < T1) load_mask(t + 1);
         __syncthreads();
     };
 
