@@ -1,5 +1,6 @@
-// Attention forward, bf16 / fp16 inputs, causal masks: the persistent form of the tiled
-// MFMA kernel, for the packed (TND) and dense causal forward with GQA.
+// Attention forward, bf16 / fp16 inputs, masks whose visible keys start at key 0 (causal
+// either way round, no mask, or a band with no lower bound): the persistent form of the
+// tiled MFMA kernel, for packed (TND) and dense forwards with GQA.
 //
 // What it computes is what the tiled kernel computes (out = softmax(scale * Q K^T) V per
 // sequence and query head with the per-row softmax max and sum; Paddle "sparse_attention"
@@ -242,8 +243,14 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                     }
                     it.r0 = it.t * R;
                     it.r1 = min(it.len_q, it.r0 + R);
-                    it.off = p.align_br ? it.len_kv - it.len_q : 0;
-                    // causal: rows [r0, r1) see keys 0 .. r1 - 1 + off
+                    // row i sees keys 0 .. i + off: the diagonal (top-left or bottom-right)
+                    // moved by the band's upper bound (causal: 0; no mask: every key),
+                    // clamped to the sequence so that it stays a 32-bit value
+                    {
+                        const int64_t off64 = (p.align_br ? (int64_t)it.len_kv - it.len_q : 0) + p.next;
+                        it.off = (int)(off64 > it.len_kv ? it.len_kv : (off64 < -(int64_t)it.len_q - 1 ? -it.len_q - 1 : off64));
+                    }
+                    // rows [r0, r1) see keys 0 .. r1 - 1 + off
                     const int vis = max(0, min(it.r1 + it.off, it.len_kv));
                     it.T0 = 0;
                     it.T1 = (vis + PBN - 1) / PBN;

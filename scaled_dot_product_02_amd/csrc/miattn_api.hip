@@ -163,7 +163,9 @@ bool use_persistent(const FaParams& p, int64_t D, int64_t Tq, int n_wg)
 {
     if (D != 64 && D != 128) return false;
     if (p.Dv != D || p.prev_out || p.amask || p.drop_thr || p.prefix) return false;
-    if (p.pre != kTokensClamp || p.next != 0) return false;
+    // every row's visible keys start at key 0 (no mask, causal, or a band with no lower
+    // bound): the kernel moves the causal diagonal by the band's upper bound
+    if (p.pre != kTokensClamp) return false;
     if (p.cu_q && p.B > kPersistMaxSeq) return false;
     // items: sum over sequences of their query tiles, times the head groups; packed
     // batches have at most Tq / rows + B tiles.  Each workgroup lists its items in LDS.

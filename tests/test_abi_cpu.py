@@ -127,15 +127,19 @@ def test_attn_fwd_validation(mi):
 
 
 def test_attn_fwd_route_persistent(mi, monkeypatch):
-    """Causal bf16 / fp16 forwards at head dim 64 or 128 without a prefix, mask tensor,
-    dropout or prior run on the persistent kernel while every workgroup's items fit its
-    LDS list; MIATTN_PERSIST=0 sends them to the tiled kernel."""
+    """bf16 / fp16 forwards at head dim 64 or 128 whose visible keys start at key 0 (causal,
+    no mask, a band without a lower bound), without a prefix, mask tensor, dropout or prior,
+    run on the persistent kernel while every workgroup's items fit its LDS list;
+    MIATTN_PERSIST=0 sends them to the tiled kernel."""
     r = mi.attn_fwd_route
     for mask in ("causal", "causal_br"):
         for dt in ("bf16", "f16"):
             for D in (64, 128):
                 assert r(2, 32, 8, 4096, 4096, D, D, dt, "BNSD", mask) == "persistent"
-    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "none") == "tiled"
+    # no mask: every row's keys start at key 0 as under causal
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "none") == "persistent"
+    assert r(2, 32, 8, 4096, 4096, 64, 64, "f16", "BSND", "none") == "persistent"
+    # a band with a lower bound (pre = next = 0 here) keeps the tiled kernel
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "band") == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 64, "bf16", "BNSD", "causal") == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", dropout_p=0.1) == "tiled"

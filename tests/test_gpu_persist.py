@@ -171,3 +171,74 @@ def test_deterministic(mi):
     run = _varlen_run(mi, w)
     a, b = run(), run()
     _assert_identical(a, b, "repeat")
+
+
+def _varlen_band_run(mi, w, mask, pre, nxt):
+    dt = w["dtype"]
+    q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
+    cq = torch.from_numpy(w["cu_q"]).to("cuda:0")
+    ck = torch.from_numpy(w["cu_kv"]).to("cuda:0")
+    mq = max(1, int(w["lengths_q"].max()))
+    mk = max(1, int(w["lengths_kv"].max()))
+    scale = 1 / math.sqrt(w["D"])
+
+    def run():
+        out = empty_like_storage(q.shape, dt)
+        m, l = nan_stats((w["Nq"], w["Tq"])), nan_stats((w["Nq"], w["Tq"]))
+        mi.attn_fwd_varlen(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"], mq, mk,
+                           w["Nq"], w["Nkv"], w["D"], dt, scale, mask, pre, nxt)
+        torch.cuda.synchronize()
+        return host_values(out), host_values(m), host_values(l)
+    return run
+
+
+# masks whose visible keys start at key 0: no mask, and bands without a lower bound whose
+# upper bound moves the causal diagonal up (33), down (-70: rows near the top see nothing)
+# or, bottom-right aligned, by -5
+OPEN_MASKS = [("none", 0, 0), ("band", 1 << 40, 33), ("band", 1 << 40, -70), ("band_br", 1 << 40, -5)]
+
+
+@pytest.mark.parametrize("mask,pre,nxt", OPEN_MASKS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Nq,Nkv", [(8, 2), (6, 6)])
+def test_open_masks_against_oracle_and_tiled(mi, mask, pre, nxt, D, Nq, Nkv):
+    """Packed batches with query and key lengths that differ per sequence (zeros included):
+    the persistent kernel equals the tiled one bit for bit and the oracle within tolerance."""
+    lq = [300, 0, 1, 129, 64, 517, 2, 65, 190]
+    lk = [300, 40, 0, 200, 64, 400, 2, 65, 3]
+    w = synthetic.varlen_inputs(500 + D + Nq + len(mask) + (nxt & 0xff), Nq=Nq, Nkv=Nkv, D=D,
+                                dtype="bf16", lengths_q=lq, lengths_kv=lk)
+    a, b = _both(_varlen_band_run(mi, w, mask, pre, nxt))
+    _assert_identical(a, b, f"{mask} {pre} {nxt} D {D}")
+    q, k, v = (synthetic.storage_values(w[x], "bf16") for x in ("q", "k", "v"))
+    align = "bottom_right" if mask.endswith("_br") else "top_left"
+    nxt_o = (1 << 62) if mask == "none" else nxt
+    wo, wm, wl = oracle.attn_varlen_keep(
+        q, k, v, w["cu_q"], w["cu_kv"],
+        lambda bb, sq, sk: oracle.keep_band(sq, sk, 1 << 62, nxt_o, align), 1 / math.sqrt(D))
+    check_out(a[0], wo, "bf16", f"{mask} {nxt} D {D}")
+    check_stats(a[1], a[2], wm, wl)
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "SBH"])
+def test_dense_no_mask(mi, layout):
+    """Dense batches without a mask (the multi-head module's attention), 3 x 700 queries
+    over 900 keys, GQA 8 / 2, D 64 in fp16 and D 128 in bf16."""
+    for D, dt in ((64, "f16"), (128, "bf16")):
+        assert mi.attn_fwd_route(3, 8, 2, 700, 900, D, D, dt, layout, "none") == "persistent"
+        w = synthetic.dense_inputs(530 + D, 3, 8, 2, 700, 900, D, dt, layout)
+        q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
+
+        def run():
+            out = empty_like_storage(q.shape, dt)
+            m, l = nan_stats((3, 8, 700)), nan_stats((3, 8, 700))
+            mi.attn_fwd(q, k, v, out, m, l, 3, 8, 2, 700, 900, D, dt, layout, 1 / math.sqrt(D), "none")
+            torch.cuda.synchronize()
+            return host_values(out), host_values(m), host_values(l)
+        a, b = _both(run)
+        _assert_identical(a, b, f"dense none {layout} D {D}")
+        qo, ko, vo = (synthetic.to_bnsd(synthetic.storage_values(w[x], dt), layout, n)
+                      for x, n in (("q", 8), ("k", 2), ("v", 2)))
+        wo, wm, wl = oracle.attn(qo, ko, vo, 1 / math.sqrt(D), "none")
+        check_out(synthetic.to_bnsd(a[0], layout, 8), wo, dt, f"dense none {layout} D {D}")
+        check_stats(a[1], a[2], wm, wl)
