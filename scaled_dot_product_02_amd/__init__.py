@@ -15,6 +15,10 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch ships its own HIP runtime and must be loaded before the library: with the library
+# loaded first (and torch imported after it), every kernel launch of the library fails
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_HERE, "libmiattn.so")
 
@@ -100,7 +104,6 @@ def _enum(x, table):
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
-    import torch
     return torch.cuda.current_stream().cuda_stream
 
 

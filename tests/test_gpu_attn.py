@@ -228,3 +228,22 @@ def test_stats_pointers_may_be_null(mi):
     torch.cuda.synchronize()
     wo, _, _ = _oracle_dense(w, 0.125, "causal")
     check_out(host_values(out), wo, "bf16")
+
+
+def test_package_imported_before_torch():
+    """A fresh process that imports the package before torch launches kernels correctly
+    (the package loads torch's HIP runtime before the library)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import scaled_dot_product_02_amd as mi\n"
+        "import torch\n"
+        "q = torch.ones(1, 2, 128, 64, device='cuda', dtype=torch.bfloat16)\n"
+        "o = torch.zeros_like(q)\n"
+        "mi.attn_fwd(q, q, q, o, None, None, 1, 2, 2, 128, 128, 64, 'bf16', 'BNSD', 0.125, 'causal')\n"
+        "torch.cuda.synchronize()\n"
+        "assert bool((o.float() == 1).all()), 'attention of constant V must return V'\n"
+        "print('ok')\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
