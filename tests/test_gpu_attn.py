@@ -6,6 +6,7 @@ several 128-row / 64-key tiles with ragged tails; the full-size packed workload 
 checked on whole sequences x sampled heads.
 """
 import math
+import os
 
 import numpy as np
 import pytest
