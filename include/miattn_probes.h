@@ -6,7 +6,8 @@
  * v_mfma_f32_32x32x16_bf16 on independent accumulators, with random operands: the chip
  * clocks lower on random data than on constant operands), the bandwidth of a plain
  * streaming pass that reads two arrays and writes one, and the rate of random 256-byte row
- * gathers from a table that each XCD's L2 holds (the access of the CSR-sparse kernel).  The caller times the launches
+ * gathers from a table that each XCD's L2 holds (the access of the CSR-sparse kernel), and
+ * the issue rates of one or two waves per SIMD on matrix and vector instructions.  The caller times the launches
  * (e.g. with events on `stream`); the functions only enqueue work.  All pointers are device
  * pointers owned by the caller.  Each returns 0 on success or the HIP error code.
  */
@@ -39,6 +40,18 @@ int miattn_probe_l2_gather(const void* table, int32_t rows_log2, int32_t blocks,
 
 /* bytes gathered by one miattn_probe_l2_gather launch: blocks * 256 * iters * 16. */
 int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters);
+
+/* Issue-rate probe: `blocks` workgroups of 256 * waves_per_simd threads (one per CU; 4 SIMDs),
+ * each wave timing `iters` rounds of one pattern with the shader clock.  kind: 0 = 16 MFMA
+ * (v_mfma_f32_32x32x16_bf16, two accumulators); 1 = 64 v_fma_f32; 2 = 32 v_exp_f32; 3 = the
+ * 16 MFMAs each followed by 2 v_fma_f32 + 2 v_exp_f32 in the same wave; 4 (waves_per_simd 2
+ * only) = waves 0-3 the 16 MFMAs, waves 4-7 the 32 v_fma_f32 + 32 v_exp_f32; 5 = the 16 MFMAs
+ * each followed by 4 v_fma_f32 + 2 v_exp_f32.  waves_per_simd: 1 or 2.  out: float
+ * [blocks * 256 * waves_per_simd]; cycles: uint64 [blocks * 16], the start and end clock of
+ * wave w of workgroup g at [16 g + 2 w] and [16 g + 2 w + 1].  Returns 0 or the HIP error code
+ * (invalid arguments: hipErrorInvalidValue, nothing launched). */
+int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t blocks, int32_t waves_per_simd,
+                       int32_t iters, void* stream);
 
 #ifdef __cplusplus
 }

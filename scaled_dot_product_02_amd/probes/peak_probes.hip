@@ -1,7 +1,9 @@
 // Peak probes of the running GPU, declared in include/miattn_probes.h: the dense bf16 MFMA
-// rate of the chip, the bandwidth of a plain 2-read / 1-write stream, and the rate of
-// random 256-byte row gathers from an L2-resident table.  They give the benchmark measured
-// ceilings beside the datasheet ones.
+// rate of the chip, the bandwidth of a plain 2-read / 1-write stream, the rate of random
+// 256-byte row gathers from an L2-resident table, and the issue rates of single waves and
+// wave pairs (how matrix and vector instructions overlap on a SIMD).  They give the
+// benchmark measured ceilings beside the datasheet ones, and the attention kernels' phase
+// design its measured basis.
 #include <hip/hip_runtime.h>
 
 #include "miattn_probes.h"
@@ -92,6 +94,77 @@ __global__ __launch_bounds__(kThreads) void l2_gather(const u32x4* table, int ro
     out[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// Issue-rate and overlap probe: one workgroup of 4 or 8 waves per CU (the static LDS array
+// keeps a second workgroup off the CU), every wave timing `iters` rounds of one instruction
+// pattern with the shader clock.  Each round issues, in the named encodings:
+//   0: 16 v_mfma_f32_32x32x16_bf16 on two accumulators;
+//   1: 64 independent v_fma_f32;
+//   2: 32 independent v_exp_f32;
+//   3: the 16 MFMAs of 0, each followed by 2 v_fma_f32 and 2 v_exp_f32 (one instruction stream);
+//   4: waves 0-3 the 16 MFMAs, waves 4-7 the 32 v_fma_f32 and 32 v_exp_f32 (two streams on each
+//      SIMD: one wave of matrix work, one of vector work);
+//   5: the 16 MFMAs, each followed by 4 v_fma_f32 and 2 v_exp_f32.
+// The vector instructions are written as inline assembly so that the count and encoding are
+// exactly these; none of them reads memory.
+#define PROBE_MFMA(acc) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+#define PROBE_FMA(i) asm volatile("v_fma_f32 %0, %0, %1, -1.0" : "+v"(x[i]) : "s"(c))
+#define PROBE_EXP(i) asm volatile("v_exp_f32_e32 %0, %0" : "+v"(x[i]))
+template <int K>
+__global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long long* cyc, int iters, float seed)
+{
+    __shared__ float pad[24576];
+    if (iters < 0) pad[threadIdx.x] = seed;   // never taken: the array only reserves LDS
+    float x[64];
+    #pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = seed * (float)(threadIdx.x + i);
+    const float c = seed * 0.5f;
+    bf16x8 a, b;
+    #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(seed * (float)(threadIdx.x + i));
+        b[i] = (__bf16)(seed * (float)i);
+    }
+    f32x16 acc0 = {}, acc1 = {};
+    const bool mfma_wave = K != 4 || threadIdx.x < 256;
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        #pragma unroll
+        for (int f = 0; f < 16; ++f) {
+            if constexpr (K == 0 || K == 3 || K == 5) {
+                if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
+            }
+            if constexpr (K == 1) { PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3); }
+            if constexpr (K == 2) { PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1); }
+            if constexpr (K == 3) { PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f); }
+            if constexpr (K == 4) {
+                if (mfma_wave) {
+                    if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
+                } else {
+                    PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f);
+                }
+            }
+            if constexpr (K == 5) {
+                PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3);
+                PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1);
+            }
+        }
+    }
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    float r = 0.f;
+    #pragma unroll
+    for (int i = 0; i < 64; ++i) r += x[i];
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc0[i] + acc1[i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if ((threadIdx.x & 63) == 0) {
+        cyc[16 * blockIdx.x + 2 * (threadIdx.x >> 6)] = t0;
+        cyc[16 * blockIdx.x + 2 * (threadIdx.x >> 6) + 1] = t1;
+    }
+}
+#undef PROBE_MFMA
+#undef PROBE_FMA
+#undef PROBE_EXP
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +205,26 @@ int miattn_probe_l2_gather(const void* table, int32_t rows_log2, int32_t blocks,
 int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters)
 {
     return (int64_t)blocks * kThreads * iters * 16;
+}
+
+int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t blocks, int32_t waves_per_simd,
+                       int32_t iters, void* stream)
+{
+    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 5) return (int)hipErrorInvalidValue;
+    if (waves_per_simd != 1 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
+    if (kind == 4 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
+    const dim3 g(blocks), b(256 * waves_per_simd);
+    const hipStream_t st = (hipStream_t)stream;
+    unsigned long long* cy = (unsigned long long*)cycles;
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(issue_probe<0>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 1: hipLaunchKernelGGL(issue_probe<1>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 2: hipLaunchKernelGGL(issue_probe<2>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 3: hipLaunchKernelGGL(issue_probe<3>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 4: hipLaunchKernelGGL(issue_probe<4>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    default: hipLaunchKernelGGL(issue_probe<5>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    }
+    return (int)hipGetLastError();
 }
 
 }  // extern "C"

@@ -59,7 +59,7 @@ def test_probe_library_exports_its_declared_symbols():
     declared = set(re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", src, re.M))
     assert declared == {"miattn_probe_mfma_bf16", "miattn_probe_mfma_bf16_flops",
                         "miattn_probe_stream_r2w1", "miattn_probe_l2_gather",
-                        "miattn_probe_l2_gather_bytes"}
+                        "miattn_probe_l2_gather_bytes", "miattn_probe_issue"}
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -78,6 +78,12 @@ def test_probe_library_exports_its_declared_symbols():
     probes.miattn_probe_l2_gather.argtypes = ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p])
     assert probes.miattn_probe_l2_gather(256, 13, 8, 12, 256, None) != 0   # iters % 8
+    probes.miattn_probe_issue.argtypes = ([ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] +
+                                          [ctypes.c_int32] * 3 + [ctypes.c_void_p])
+    assert probes.miattn_probe_issue(6, 256, 256, 1, 1, 1, None) != 0    # unknown kind
+    assert probes.miattn_probe_issue(4, 256, 256, 1, 1, 1, None) != 0    # kind 4 needs two waves per SIMD
+    assert probes.miattn_probe_issue(0, 256, 256, 1, 3, 1, None) != 0    # waves per SIMD 1 or 2
+    assert probes.miattn_probe_issue(0, None, 256, 1, 1, 1, None) != 0
     assert probes.miattn_probe_l2_gather(256, 21, 8, 16, 256, None) != 0   # rows_log2 > 20
 
 
