@@ -49,17 +49,17 @@ constexpr int kPRsrcFlags = 0x00020000;   // buffer descriptor word 3: 32-bit da
 template <int D>
 struct PCfg {
     static constexpr int KS = D + 8;                   // K row stride in LDS (elements)
-    static constexpr int VS = PBN + 8;                 // V^T row stride in LDS
+    static constexpr int VP = D + 32;                  // V row stride in LDS (elements): the
+                                                       // rows of a transposed read fall in
+                                                       // disjoint bank ranges
     static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
     static constexpr int KCH = PBN * CPR;              // K chunks per tile
     static constexpr int KPT = KCH / PT;               // K chunks per thread
-    static constexpr int VUNITS = (PBN / 2) * (D / 8); // V units (2 keys x 8 dims) per tile
-    static constexpr int VPT = (VUNITS + PT - 1) / PT; // V units per thread (some repeat)
-    static constexpr int SREG = KPT + 2 * VPT;         // staging registers (16 B each)
+    static constexpr int SREG = 2 * KPT;               // staging registers (16 B each): K, then V
     static constexpr int KK = D / 16;                  // MFMA k-steps over the head dim
     static constexpr int RT = D / 32;                  // 32-row output tiles
     static constexpr int KBUF = PBN * KS;
-    static constexpr int VBUF = D * VS;
+    static constexpr int VBUF = PBN * VP;
     static_assert(KCH % PT == 0, "K chunks split evenly over the threads");
 };
 
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     __shared__ PRec s_rec[MAXI];
     __shared__ int s_nitems, s_nsteps;
     __bf16* Ks = ring;
-    __bf16* Vt = ring + PNBUF * C::KBUF;
+    __bf16* Vs = ring + PNBUF * C::KBUF;
     // sequence tables of a packed batch: bounds, and the sequences sorted by query tiles
     // (descending, ties by index) so that every workgroup derives the same item order
     int* s_q0 = (int*)ring;
@@ -361,23 +361,13 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     // ---- staging of one tile: every thread takes KPT K chunks (16 B of a key row) and one
     //      V unit (2 keys x 8 dims); rows past the sequence end read as zero
     u32x4 stA[C::SREG], stB[C::SREG];
-    int kp[C::VPT], vc[C::VPT];
-    #pragma unroll
-    for (int u = 0; u < C::VPT; ++u) {
-        const int vu = (tid + PT * u) % C::VUNITS;
-        kp[u] = vu % (PBN / 2);
-        vc[u] = vu / (PBN / 2);
-    }
-    uint32_t koff[C::KPT], voff[2 * C::VPT];
+    uint32_t koff[C::KPT], voff[C::KPT];
     #pragma unroll
     for (int u = 0; u < C::KPT; ++u) {
         const int c = tid + PT * u;
         koff[u] = (uint32_t)((c / C::CPR) * krb + 16 * (c % C::CPR));
+        voff[u] = (uint32_t)((c / C::CPR) * vrb + 16 * (c % C::CPR));
     }
-    #pragma unroll
-    for (int u = 0; u < C::VPT; ++u)
-        #pragma unroll
-        for (int r = 0; r < 2; ++r) voff[2 * u + r] = (uint32_t)((2 * kp[u] + r) * vrb + 16 * vc[u]);
 
     // load the loader's next tile (zeros past the list) and advance the loader; the row
     // count is clamped with scalar instructions (the compiler would form a vector
@@ -393,26 +383,17 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) stage[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0);
         #pragma unroll
-        for (int r = 0; r < 2 * C::VPT; ++r) stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
+        for (int u = 0; u < C::KPT; ++u) stage[C::KPT + u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, 0);
         ++l_tile;
     };
     auto store_tile = [&](int slot, const u32x4 (&stage)[C::SREG]) {
         __bf16* kb = Ks + slot * C::KBUF;
+        __bf16* vb = Vs + slot * C::VBUF;
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
             const int c = tid + PT * u;
             *(u32x4*)(kb + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
-        }
-        #pragma unroll
-        for (int u = 0; u < C::VPT; ++u) {
-            __bf16* vb = Vt + slot * C::VBUF + 8 * vc[u] * C::VS + vt_pos(2 * kp[u]);
-            const u32x4 x0 = stage[C::KPT + 2 * u], x1 = stage[C::KPT + 2 * u + 1];
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // low (even e) or high (odd e) halves of the two keys' words
-                const unsigned w = __builtin_amdgcn_perm(x1[e >> 1], x0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-                *(unsigned*)(vb + e * C::VS) = w;
-            }
+            *(u32x4*)(vb + (c / C::CPR) * C::VP + 8 * (c % C::CPR)) = stage[C::KPT + u];
         }
     };
 
@@ -478,25 +459,37 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
     };
 
-    // ---- O^T += V^T P^T for the tile in LDS slot `slot`
+    // ---- O^T += V^T P^T for the tile in LDS slot `slot`.  V sits in LDS as [key][dim]; the
+    //      A operand of fragment f (32-dim block r = f / (2 PNKB), 16-key block j) comes from
+    //      two ds_read_b64_tr_b16: lane l, slot e of a transposed read receives element l % 4
+    //      of the 8-byte block read by lane 16 (l / 16) + 4 e + (l % 16) / 4, so lane l reading
+    //      dims 32 r + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 of key 16 j + 4 hf + (l % 16) / 4
+    //      (then 8 keys further) leaves lane (lq, hf) with V[16 j + 8 (e / 4) + 4 hf + e % 4]
+    //      [32 r + lq], e = 0..7: the key order of the P operand taken from the S accumulators
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const int v_lane = (4 * hf + ((lane & 15) >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto vfrag = [&](int slot, int f) -> X8 {
+        const __bf16* v = Vs + slot * C::VBUF + v_lane + 16 * (f % (2 * PNKB)) * C::VP + 32 * (f / (2 * PNKB));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)v);
+        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v + 8 * C::VP));
+        return __builtin_bit_cast(X8, i16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
     auto pv = [&](int slot, const X8 (&pp)[2 * PNKB]) {
-        const __bf16* vb = Vt + slot * C::VBUF + lq * C::VS + 8 * hf;
         constexpr int NF = C::RT * 2 * PNKB;
         X8 a[NF];
         #pragma unroll
-        for (int f = 0; f < PLDSD && f < NF; ++f)
-            a[f] = *(const X8*)(vb + 32 * (f / (2 * PNKB)) * C::VS + 16 * (f % (2 * PNKB)));
+        for (int f = 0; f < PLDSD && f < NF; ++f) a[f] = vfrag(slot, f);
         #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            if (f + PLDSD < NF)
-                a[f + PLDSD] = *(const X8*)(vb + 32 * ((f + PLDSD) / (2 * PNKB)) * C::VS + 16 * ((f + PLDSD) % (2 * PNKB)));
+            if (f + PLDSD < NF) a[f + PLDSD] = vfrag(slot, f + PLDSD);
             o[f / (2 * PNKB)] = Elem<T>::mfma(a[f], pp[f % (2 * PNKB)], o[f / (2 * PNKB)]);
         }
         constexpr int AH = PLDSD < NF ? PLDSD : NF;
-        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
         #pragma unroll
         for (int f = 0; f < NF - AH; ++f) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
