@@ -479,7 +479,131 @@ void fa_fwd_bf16_kernel(FaParams p)
         __syncthreads();
     };
 
-    if (T0 < T1) {
+    if constexpr (C::BIG) {
+        // ---- one wave per SIMD (head dims above 128): no partner wave overlaps the softmax
+        //      with the matrix core, so each wave overlaps its own: step t issues
+        //      S(t+1) = K(t+1) Q^T with the softmax of tile t between the MFMAs, then O and
+        //      the row sum move to the new reference max where it changed (rare), then
+        //      O += P(t) V(t).  One barrier per step: tile t+2 lands in LDS during step t
+        //      (its slot's last reader, P V of tile t-2, finished before the previous
+        //      barrier) and tile t+3 is loaded.  A tile that a wave does not see is
+        //      computed as fully masked (its probabilities are zero), which keeps the
+        //      interleaved block free of branches.
+        if (T0 < T1) {
+            load_tile(T0, stA);
+            load_tile(T0 + 1, stB);
+            __builtin_amdgcn_s_waitcnt(0);
+            store_tile(T0, stA);
+            store_tile(T0 + 1, stB);
+            if (PF == 3) load_tile(T0 + 2, stB);
+            __syncthreads();
+            f32x16 sa[NKB], sb[NKB];
+            X8 pp[2 * NKB];
+            qk(T0, sa);
+            float mq[2], mu = 0.f, rq[4] = {0.f, 0.f, 0.f, 0.f}, ex[4];
+            float m_ref_n = -INFINITY, m_true_n = -INFINITY;
+            // the softmax of tile t (16 scores per lane in s[0]) in slots: max over
+            // elements 0-7 and 8-15, the reduction and reference update, then the eight
+            // pairs with each pair's exponentials one slot before its sums and rounding.
+            // The empty asm statements pin the work to its slot.
+            auto sm_slot = [&](int f, f32x16 (&sx)[NKB]) __attribute__((always_inline)) {
+                if (f < 2) {
+                    float m = sx[0][8 * f];
+                    #pragma unroll
+                    for (int k = 1; k < 8; k += 2)
+                        m = k + 1 < 8 ? fmaxf(fmaxf(m, sx[0][8 * f + k]), sx[0][8 * f + k + 1]) : fmaxf(m, sx[0][8 * f + k]);
+                    mq[f] = m;
+                    asm volatile("" : "+v"(mq[f]));
+                } else if (f == 2) {
+                    const float mx = pair_max(fmaxf(mq[0], mq[1]));
+                    const float mt = mx * cl2;
+                    m_true_n = fmaxf(m_true, mt);
+                    m_ref_n = mt > m_ref + kLazyThresh ? mt : m_ref;
+                    mu = m_ref_n == -INFINITY ? 0.f : m_ref_n;
+                    asm volatile("" : "+v"(mu), "+v"(m_ref_n), "+v"(m_true_n));
+                } else {
+                    const int k = f - 3;
+                    if (k >= 1 && k <= 8) {
+                        const int q = k - 1, i = 2 * q;
+                        const float x0 = ex[2 * (q & 1)], x1 = ex[2 * (q & 1) + 1];
+                        if (q < 2) {
+                            rq[i & 3] = x0;
+                            rq[(i + 1) & 3] = x1;
+                        } else {
+                            rq[i & 3] += x0;
+                            rq[(i + 1) & 3] += x1;
+                        }
+                        pp[i >> 3][i & 7] = (T)x0;
+                        pp[i >> 3][(i & 7) + 1] = (T)x1;
+                        asm volatile("" : "+v"(rq[i & 3]), "+v"(rq[(i + 1) & 3]));
+                    }
+                    if (k < 8) {
+                        float y0 = sx[0][2 * k], y1 = sx[0][2 * k + 1];
+                        asm volatile("" : "+v"(y0), "+v"(y1));
+                        float& x0 = ex[2 * (k & 1)];
+                        float& x1 = ex[2 * (k & 1) + 1];
+                        x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(y0, cl2, -mu));
+                        x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(y1, cl2, -mu));
+                        asm volatile("" : "+v"(x0), "+v"(x1));
+                    }
+                }
+            };
+            constexpr int NSL = 12;   // softmax slots
+            // tile t's scores in cur; S(t+1) into nxt
+            auto big_step = [&](int t, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], u32x4 (&ld)[C::SREG],
+                                u32x4 (&sto)[C::SREG]) __attribute__((always_inline)) {
+                load_tile(t + PF, ld);
+                // keys past each lane's last visible one, and tiles the wave does not see
+                if (!wave_active(t) || t < full_lo || t >= full_hi) {
+                    const bool act = wave_active(t);
+                    const int lo = act ? jlo : 1 << 30, hi = act ? jhi : -1;
+                    const int jb = t * BN + 4 * hf;
+                    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = jb + 8 * (i >> 2) + (i & 3);
+                        if (j < lo || j > hi) cur[0][i] = -INFINITY;
+                    }
+                }
+                {
+                    const __bf16* kb = Ks + ((t + 1) & (NBUF - 1)) * C::KBUF + lq * C::KS + 8 * hf;
+                    X8 a[C::KK];
+                    nxt[0] = f32x16{};
+                    #pragma unroll
+                    for (int f = 0; f < LDSD && f < C::KK; ++f) a[f] = *(const X8*)(kb + 16 * f);
+                    #pragma unroll
+                    for (int f = 0; f < C::KK; ++f) {
+                        if (f + LDSD < C::KK) a[f + LDSD] = *(const X8*)(kb + 16 * (f + LDSD));
+                        nxt[0] = Elem<T>::mfma(a[f], qf[f], nxt[0]);
+                        if (f < NSL) sm_slot(f, cur);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    #pragma unroll
+                    for (int f = C::KK; f < NSL; ++f) sm_slot(f, cur);
+                }
+                if (__any(m_ref_n != m_ref)) {
+                    const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_ref_n);
+                    l_run *= alpha;
+                    #pragma unroll
+                    for (int r = 0; r < C::RT; ++r)
+                        #pragma unroll
+                        for (int i = 0; i < 16; ++i) o[r][i] *= alpha;
+                }
+                m_ref = m_ref_n;
+                m_true = m_true_n;
+                l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
+                pv(t, pp);
+                store_tile(t + 2, sto);
+                __syncthreads();
+            };
+            int t = T0;
+            u32x4 (&sB)[C::SREG] = PF == 3 ? stB : stA;
+            for (; t + 1 < T1; t += 2) {
+                big_step(t, sa, sb, stA, sB);
+                big_step(t + 1, sb, sa, sB, stA);
+            }
+            if (t < T1) big_step(t, sa, sb, stA, sB);
+        }
+    } else if (T0 < T1) {
         // Q and the first two tiles in one memory round trip; the wait also drains Q, so
         // no wait on it is left for the key loop (where it would also wait for prefetches)
         if constexpr (MASKED) load_mask(T0);
