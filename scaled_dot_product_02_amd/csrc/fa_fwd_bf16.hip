@@ -70,6 +70,16 @@ constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit da
 // run 4 waves, one per SIMD, so that a wave may hold up to 512 registers (the O
 // accumulators of D 256 alone take 128), on 32-key tiles so that the 4-deep K and V^T
 // rings fit in LDS (about 146 KB at D 256).
+// Row pitch (elements) of V staged as [key][dim] for transposed reads: the four key rows and
+// two 16-dim halves that a ds_read_b64_tr_b16 gathers for 32 lanes fall in disjoint bank
+// ranges when the pitch is 32 or 96 modulo 128 elements.
+constexpr int vrow_pitch(int dv)
+{
+    int p = dv + 8;
+    while (p % 128 != 32 && p % 128 != 96) p += 8;
+    return p;
+}
+
 template <int D, int DV, bool FOUR = (D > 128)>
 struct Cfg {
     static constexpr bool BIG = FOUR;
@@ -85,11 +95,18 @@ struct Cfg {
     static constexpr int KPT = (KCH + NT - 1) / NT;   // K chunks per thread (some repeat)
     static constexpr int VUNITS = (BN / 2) * (DV / 8); // V units (2 keys x 8 dims) per tile
     static constexpr int VPT = (VUNITS + NT - 1) / NT; // V units per thread (some repeat)
-    static constexpr int SREG = KPT + 2 * VPT;        // staging registers (16 B each)
+    // one wave per SIMD: V staged as [key][dim] (16-byte chunks like K) and read back
+    // transposed as the P V operand, instead of transposed into V^T by the staging threads
+    static constexpr bool VROW = BIG;
+    static constexpr int VP = vrow_pitch(DV);         // V row pitch in LDS (VROW)
+    static constexpr int CPRV = DV / 8;               // 16-byte chunks per V row
+    static constexpr int VCH = BN * CPRV;             // V chunks per tile (VROW)
+    static constexpr int VRT = (VCH + NT - 1) / NT;   // V chunks per thread (VROW; some repeat)
+    static constexpr int SREG = KPT + (VROW ? VRT : 2 * VPT);  // staging registers (16 B each)
     static constexpr int KK = D / 16;                 // MFMA k-steps over the Q/K head dim
     static constexpr int RT = DV / 32;                // 32-row output tiles over the V head dim
     static constexpr int KBUF = BN * KS;
-    static constexpr int VBUF = DV * VS;
+    static constexpr int VBUF = VROW ? BN * VP : DV * VS;
 };
 
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
@@ -214,16 +231,24 @@ void fa_fwd_bf16_kernel(FaParams p)
         vc[u] = vu / (BN / 2);
     }
     const int64_t krb = 2 * p.k_ss, vrb = 2 * p.v_ss;   // row strides in bytes
-    uint32_t koff[C::KPT], voff[2 * C::VPT];
+    uint32_t koff[C::KPT], voff[C::VROW ? C::VRT : 2 * C::VPT];
     #pragma unroll
     for (int u = 0; u < C::KPT; ++u) {
         const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
         koff[u] = (uint32_t)((c / C::CPR) * krb + 16 * (c % C::CPR));
     }
-    #pragma unroll
-    for (int u = 0; u < C::VPT; ++u)
+    if constexpr (C::VROW) {
         #pragma unroll
-        for (int r = 0; r < 2; ++r) voff[2 * u + r] = (uint32_t)((2 * kp[u] + r) * vrb + 16 * vc[u]);
+        for (int u = 0; u < C::VRT; ++u) {
+            const int c = C::VCH % NT ? (tid + NT * u) % C::VCH : tid + NT * u;
+            voff[u] = (uint32_t)((c / C::CPRV) * vrb + 16 * (c % C::CPRV));
+        }
+    } else {
+        #pragma unroll
+        for (int u = 0; u < C::VPT; ++u)
+            #pragma unroll
+            for (int r = 0; r < 2; ++r) voff[2 * u + r] = (uint32_t)((2 * kp[u] + r) * vrb + 16 * vc[u]);
+    }
 
     // descriptor inputs are workgroup-uniform; readfirstlane keeps them in scalar registers
     // (a descriptor the compiler thinks divergent would be looped over lane by lane)
@@ -256,11 +281,28 @@ void fa_fwd_bf16_kernel(FaParams p)
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) stage[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0);
         #pragma unroll
-        for (int r = 0; r < 2 * C::VPT; ++r) stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
+        for (int r = 0; r < (C::VROW ? C::VRT : 2 * C::VPT); ++r)
+            stage[C::KPT + r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
+    };
+    // staged chunk u (K chunks, then V chunks) of tile t into LDS (the V-as-rows layout)
+    auto store_chunk = [&](int t, const u32x4 (&stage)[C::SREG], int u) __attribute__((always_inline)) {
+        const int bf = t & (NBUF - 1);
+        if (u < C::KPT) {
+            const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
+            *(u32x4*)(Ks + bf * C::KBUF + (c / C::CPR) * C::KS + 8 * (c % C::CPR)) = stage[u];
+        } else {
+            const int c = C::VCH % NT ? (tid + NT * (u - C::KPT)) % C::VCH : tid + NT * (u - C::KPT);
+            *(u32x4*)(Vt + bf * C::VBUF + (c / C::CPRV) * C::VP + 8 * (c % C::CPRV)) = stage[u];
+        }
     };
     auto store_tile = [&](int t, const u32x4 (&stage)[C::SREG]) {
         const int bf = t & (NBUF - 1);
         __bf16* kb = Ks + bf * C::KBUF;
+        if constexpr (C::VROW) {
+            #pragma unroll
+            for (int u = 0; u < C::SREG; ++u) store_chunk(t, stage, u);
+            return;
+        }
         #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
             const int c = C::KCH % NT ? (tid + NT * u) % C::KCH : tid + NT * u;
@@ -310,8 +352,43 @@ void fa_fwd_bf16_kernel(FaParams p)
 #endif
     };
 
+    // ---- V^T fragment f of tile t from V staged as [key][dim] (VROW): two
+    //      ds_read_b64_tr_b16.  Lane l, slot e of a transposed read receives element l % 4 of
+    //      the 8-byte block read by lane 16 (l / 16) + 4 e + (l % 16) / 4, so lane l reading
+    //      dims 32 r + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 of key 16 j + 4 hf + (l % 16) / 4
+    //      (then 8 keys further) leaves lane (lq, hf) with V[16 j + 8 (e / 4) + 4 hf + e % 4]
+    //      [32 r + lq], e = 0..7: the key order of the P operand (r = f / (2 NKB),
+    //      j = f % (2 NKB))
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const int v_lane = (4 * hf + ((lane & 15) >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto vfrag_rows = [&](int t, int f) __attribute__((always_inline)) -> X8 {
+        const __bf16* v = Vt + (t & (NBUF - 1)) * C::VBUF + v_lane + 16 * (f % (2 * NKB)) * C::VP + 32 * (f / (2 * NKB));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)v);
+        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v + 8 * C::VP));
+        return __builtin_bit_cast(X8, i16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    // O^T += V^T P^T for tile t (VROW) with work(f) issued after MFMA f
+    auto pv_rows = [&](int t, const X8 (&pp)[2 * NKB], auto&& work) __attribute__((always_inline)) {
+        constexpr int NF = C::RT * 2 * NKB;
+        X8 a[NF];
+        #pragma unroll
+        for (int f = 0; f < LDSD && f < NF; ++f) a[f] = vfrag_rows(t, f);
+        #pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f + LDSD < NF) a[f + LDSD] = vfrag_rows(t, f + LDSD);
+            o[f / (2 * NKB)] = Elem<T>::mfma(a[f], pp[f % (2 * NKB)], o[f / (2 * NKB)]);
+            work(f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // ---- O^T += V^T P^T for tile t
     auto pv = [&](int t, const X8 (&pp)[2 * NKB]) {
+        if constexpr (C::VROW) {
+            pv_rows(t, pp, [](int) {});
+            return;
+        }
         const __bf16* vb = Vt + (t & (NBUF - 1)) * C::VBUF + lq * C::VS + 8 * hf;
         constexpr int NF = C::RT * 2 * NKB;   // fragment f: r = f / (2 NKB), j = f % (2 NKB)
         X8 a[NF];
@@ -591,8 +668,12 @@ void fa_fwd_bf16_kernel(FaParams p)
                 m_ref = m_ref_n;
                 m_true = m_true_n;
                 l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
-                pv(t, pp);
-                store_tile(t + 2, sto);
+                // the staged tile t+2 lands in LDS one chunk per P V MFMA
+                pv_rows(t, pp, [&](int f) __attribute__((always_inline)) {
+                    if (f < C::SREG) store_chunk(t + 2, sto, f);
+                });
+                #pragma unroll
+                for (int u = C::RT * 2 * NKB; u < C::SREG; ++u) store_chunk(t + 2, sto, u);
                 __syncthreads();
             };
             int t = T0;
