@@ -12,11 +12,11 @@
 //     VGPRs, so two waves share each SIMD.  Waves w and w + 4 share a SIMD, which evens
 //     out the causal triangle across the four SIMDs, and they run one phase apart (below)
 //     so that one wave's softmax (vector ALU) overlaps the other's matrix-core work.
-//   * Keys advance in tiles of 64.  K (row-major) and V (transposed, V^T[d][key]) tiles
-//     are staged from 128-bit buffer loads through registers into a 4-deep ring of LDS
-//     buffers; a tile's loads are issued two steps before its LDS stores (two register
-//     sets), which covers the memory latency under load.  Every thread stages the same
-//     share of each tile, with no branch.
+//   * Keys advance in tiles of 64.  K (row-major) and V (transposed, V^T[d][key]; row-
+//     major for head dims above 128, below) tiles are staged from 128-bit buffer loads
+//     through registers into a 4-deep ring of LDS buffers; a tile's loads are issued two
+//     steps before its LDS stores (two register sets), which covers the memory latency
+//     under load.  Every thread stages the same share of each tile, with no branch.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns ONE query column and 16 of the
 //     32 keys, so the row max / row sum are in-lane reductions plus one exchange with the
 //     lane 32 apart.
@@ -65,11 +65,6 @@ constexpr int NBUF = 4;         // LDS ring depth (tiles)
 constexpr float kLazyThresh = 8.0f;  // log2 units
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw
 
-// D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
-// Head dims up to 128 run 8 waves (two per SIMD) on 64-key tiles.  Larger ones (160..256)
-// run 4 waves, one per SIMD, so that a wave may hold up to 512 registers (the O
-// accumulators of D 256 alone take 128), on 32-key tiles so that the 4-deep K and V^T
-// rings fit in LDS (about 146 KB at D 256).
 // Row pitch (elements) of V staged as [key][dim] for transposed reads: the four key rows and
 // two 16-dim halves that a ds_read_b64_tr_b16 gathers for 32 lanes fall in disjoint bank
 // ranges when the pitch is 32 or 96 modulo 128 elements.
@@ -79,6 +74,13 @@ constexpr int vrow_pitch(int dv)
     while (p % 128 != 32 && p % 128 != 96) p += 8;
     return p;
 }
+
+// D: head dim of Q and K; DV: head dim of V and the output (DV <= D).
+// Head dims up to 128 run 8 waves (two per SIMD) on 64-key tiles.  Larger ones (160..256)
+// run 4 waves, one per SIMD, so that a wave may hold up to 512 registers (the O
+// accumulators of D 256 alone take 128), on 32-key tiles so that the 4-deep K and V
+// rings fit in LDS (138 KB at D 256); there V is staged row-major like K and read back
+// transposed as the matrix operand.
 
 template <int D, int DV, bool FOUR = (D > 128)>
 struct Cfg {

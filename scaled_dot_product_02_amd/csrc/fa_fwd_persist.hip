@@ -29,9 +29,9 @@
 // Within a step everything is as in the tiled kernel: S^T = K Q^T on
 // v_mfma_f32_32x32x16 with the scores of a query row in one lane pair, the online softmax
 // in the log2 domain with a lazily moved reference max, P used as the B operand of
-// O^T += V^T P^T straight from the accumulators, K / V^T staged through a 4-deep LDS ring
-// three tiles ahead, and the two waves of each SIMD one phase apart (matrix-core phase M,
-// softmax phase S).
+// O^T += V^T P^T straight from the accumulators, K and V staged row-major through a 4-deep
+// LDS ring three tiles ahead (V read back transposed as the matrix operand), and the two
+// waves of each SIMD one phase apart (matrix-core phase M, softmax phase S).
 #include "fa_common.h"
 #include "fa_mfma.h"
 
@@ -86,7 +86,7 @@ struct PRec {
 };
 static_assert(sizeof(PRec) == 64, "one LDS record per item");
 
-// LDS of a workgroup beside the K / V^T ring: the item records (the packed batch's
+// LDS of a workgroup beside the K / V ring: the item records (the packed batch's
 // sequence tables, needed only while the records are built, share the ring's space).
 template <int D>
 constexpr int persist_max_items()

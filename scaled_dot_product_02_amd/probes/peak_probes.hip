@@ -103,8 +103,14 @@ __global__ __launch_bounds__(kThreads) void l2_gather(const u32x4* table, int ro
 //   3: the 16 MFMAs of 0, each followed by 2 v_fma_f32 and 2 v_exp_f32 (one instruction stream);
 //   4: waves 0-3 the 16 MFMAs, waves 4-7 the 32 v_fma_f32 and 32 v_exp_f32 (two streams on each
 //      SIMD: one wave of matrix work, one of vector work);
-//   5: the 16 MFMAs, each followed by 4 v_fma_f32 and 2 v_exp_f32.
-// The vector instructions are written as inline assembly so that the count and encoding are
+//   5: the 16 MFMAs, each followed by 4 v_fma_f32 and 2 v_exp_f32;
+//   6: as 4, with the MFMA waves at s_setprio 3;
+//   7: waves 0-3 the 16 MFMAs, waves 4-7 48 v_fma_f32 and 16 v_exp_f32 (a softmax's mix of
+//      vector work per 16 MFMAs);
+//   8: as 7, with the MFMA waves at s_setprio 3.
+// In the two-stream patterns the role is taken from a wave-uniform (scalar) wave index
+// outside the timed loop, so that each wave's loop holds its own instructions only.  The
+// vector instructions are written as inline assembly so that the count and encoding are
 // exactly these; none of them reads memory.
 #define PROBE_MFMA(acc) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
 #define PROBE_FMA(i) asm volatile("v_fma_f32 %0, %0, %1, -1.0" : "+v"(x[i]) : "s"(c))
@@ -125,27 +131,43 @@ __global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long lon
         b[i] = (__bf16)(seed * (float)i);
     }
     f32x16 acc0 = {}, acc1 = {};
-    const bool mfma_wave = K != 4 || threadIdx.x < 256;
+    constexpr bool SPLIT = K == 4 || K >= 6;
+    const bool mfma_wave = !SPLIT || __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4;
     const unsigned long long t0 = __builtin_readcyclecounter();
-    for (int it = 0; it < iters; ++it) {
-        #pragma unroll
-        for (int f = 0; f < 16; ++f) {
-            if constexpr (K == 0 || K == 3 || K == 5) {
+    if (SPLIT && mfma_wave) {
+        if constexpr (K == 6 || K == 8) __builtin_amdgcn_s_setprio(3);
+        for (int it = 0; it < iters; ++it) {
+            #pragma unroll
+            for (int f = 0; f < 16; ++f) {
                 if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
             }
-            if constexpr (K == 1) { PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3); }
-            if constexpr (K == 2) { PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1); }
-            if constexpr (K == 3) { PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f); }
-            if constexpr (K == 4) {
-                if (mfma_wave) {
-                    if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
-                } else {
+        }
+        if constexpr (K == 6 || K == 8) __builtin_amdgcn_s_setprio(0);
+    } else if (SPLIT) {
+        for (int it = 0; it < iters; ++it) {
+            #pragma unroll
+            for (int f = 0; f < 16; ++f) {
+                if constexpr (K == 4 || K == 6) {
                     PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f);
+                } else {
+                    PROBE_FMA(3 * f); PROBE_FMA(3 * f + 1); PROBE_FMA(3 * f + 2); PROBE_EXP(48 + f);
                 }
             }
-            if constexpr (K == 5) {
-                PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3);
-                PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            #pragma unroll
+            for (int f = 0; f < 16; ++f) {
+                if constexpr (K == 0 || K == 3 || K == 5) {
+                    if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
+                }
+                if constexpr (K == 1) { PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3); }
+                if constexpr (K == 2) { PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1); }
+                if constexpr (K == 3) { PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f); }
+                if constexpr (K == 5) {
+                    PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3);
+                    PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1);
+                }
             }
         }
     }
@@ -157,8 +179,10 @@ __global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long lon
     for (int i = 0; i < 16; ++i) r += acc0[i] + acc1[i];
     out[blockIdx.x * blockDim.x + threadIdx.x] = r;
     if ((threadIdx.x & 63) == 0) {
-        cyc[16 * blockIdx.x + 2 * (threadIdx.x >> 6)] = t0;
-        cyc[16 * blockIdx.x + 2 * (threadIdx.x >> 6) + 1] = t1;
+        cyc[32 * blockIdx.x + 2 * (threadIdx.x >> 6)] = t0;
+        cyc[32 * blockIdx.x + 2 * (threadIdx.x >> 6) + 1] = t1;
+        // SIMD of this wave: HW_ID bits 5:4 (s_getreg_b32 hwreg(HW_REG_HW_ID, 4, 2))
+        cyc[32 * blockIdx.x + 16 + (threadIdx.x >> 6)] = (unsigned long long)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
     }
 }
 #undef PROBE_MFMA
@@ -210,9 +234,9 @@ int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters)
 int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t blocks, int32_t waves_per_simd,
                        int32_t iters, void* stream)
 {
-    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 5) return (int)hipErrorInvalidValue;
+    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 8) return (int)hipErrorInvalidValue;
     if (waves_per_simd != 1 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
-    if (kind == 4 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
+    if ((kind == 4 || kind >= 6) && waves_per_simd != 2) return (int)hipErrorInvalidValue;
     const dim3 g(blocks), b(256 * waves_per_simd);
     const hipStream_t st = (hipStream_t)stream;
     unsigned long long* cy = (unsigned long long*)cycles;
@@ -222,7 +246,10 @@ int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t block
     case 2: hipLaunchKernelGGL(issue_probe<2>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 3: hipLaunchKernelGGL(issue_probe<3>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 4: hipLaunchKernelGGL(issue_probe<4>, g, b, 0, st, out, cy, iters, 0.001f); break;
-    default: hipLaunchKernelGGL(issue_probe<5>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 5: hipLaunchKernelGGL(issue_probe<5>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 6: hipLaunchKernelGGL(issue_probe<6>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 7: hipLaunchKernelGGL(issue_probe<7>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    default: hipLaunchKernelGGL(issue_probe<8>, g, b, 0, st, out, cy, iters, 0.001f); break;
     }
     return (int)hipGetLastError();
 }

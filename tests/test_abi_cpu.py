@@ -80,8 +80,9 @@ def test_probe_library_exports_its_declared_symbols():
     assert probes.miattn_probe_l2_gather(256, 13, 8, 12, 256, None) != 0   # iters % 8
     probes.miattn_probe_issue.argtypes = ([ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] +
                                           [ctypes.c_int32] * 3 + [ctypes.c_void_p])
-    assert probes.miattn_probe_issue(6, 256, 256, 1, 1, 1, None) != 0    # unknown kind
-    assert probes.miattn_probe_issue(4, 256, 256, 1, 1, 1, None) != 0    # kind 4 needs two waves per SIMD
+    assert probes.miattn_probe_issue(9, 256, 256, 1, 2, 1, None) != 0    # unknown kind
+    assert probes.miattn_probe_issue(4, 256, 256, 1, 1, 1, None) != 0    # two-stream kinds need two waves per SIMD
+    assert probes.miattn_probe_issue(8, 256, 256, 1, 1, 1, None) != 0
     assert probes.miattn_probe_issue(0, 256, 256, 1, 3, 1, None) != 0    # waves per SIMD 1 or 2
     assert probes.miattn_probe_issue(0, None, 256, 1, 1, 1, None) != 0
     assert probes.miattn_probe_l2_gather(256, 21, 8, 16, 256, None) != 0   # rows_log2 > 20
@@ -151,10 +152,10 @@ def test_attn_fwd_route_persistent(mi, monkeypatch):
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", dropout_p=0.1) == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", update=True) == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 128, "f32", "BNSD", "causal") == "general"
-    # at most 319 items per workgroup at head dim 128 (256 workgroups): 256 heads of one
-    # kv head each (256-row items) x 319 query tiles fit, 320 do not
-    assert r(1, 256, 256, 319 * 256, 319 * 256, 128, 128, "bf16", "BNSD", "causal") == "persistent"
-    assert r(1, 256, 256, 320 * 256, 320 * 256, 128, 128, "bf16", "BNSD", "causal") == "tiled"
+    # at most 191 items per workgroup at head dim 128 (256 workgroups): 256 heads of one
+    # kv head each (256-row items) x 191 query tiles fit, 192 do not
+    assert r(1, 256, 256, 191 * 256, 191 * 256, 128, 128, "bf16", "BNSD", "causal") == "persistent"
+    assert r(1, 256, 256, 192 * 256, 192 * 256, 128, 128, "bf16", "BNSD", "causal") == "tiled"
     monkeypatch.setenv("MIATTN_PERSIST", "0")
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal") == "tiled"
 
@@ -175,7 +176,10 @@ def test_attn_fwd_route_large_sbh_stride(mi):
         assert r(16384, 8, 8, 64, 64, 128, 128, "bf16", lay, "causal") != "general"
     # GQA: the K / V stride counts the kv heads only
     assert r(16384, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "general"
-    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "persistent"
+    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") != "general"
+    # (8192 x 8 items of 64 rows are 256 per workgroup, over the persistent list's 191)
+    assert r(8192, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "tiled"
+    assert r(4096, 32, 8, 64, 64, 128, 128, "bf16", "SBH", "causal") == "persistent"
     # other routes: fp32 and head dims outside the tiled set, mask tensors by alignment
     assert r(1, 4, 4, 100, 100, 128, 128, "f32", "BNSD", "none") == "general"
     assert r(1, 4, 4, 100, 100, 80, 80, "bf16", "BNSD", "none") == "general"
