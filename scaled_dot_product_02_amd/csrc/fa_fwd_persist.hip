@@ -459,8 +459,10 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
     };
 
-    // ---- O^T += V^T P^T for the tile in LDS slot `slot`.  V sits in LDS as [key][dim]; the
-    //      A operand of fragment f (32-dim block r = f / (2 PNKB), 16-key block j) comes from
+    // ---- O^T += V^T P^T for the tile in LDS slot `slot`.  Fragment f is 32-dim block
+    //      r = f % RT and 16-key block j = f / RT, so consecutive MFMAs feed different
+    //      accumulators while each accumulator still takes its key blocks in order.  V sits
+    //      in LDS as [key][dim]; the A operand of fragment (r, j) comes from
     //      two ds_read_b64_tr_b16: lane l, slot e of a transposed read receives element l % 4
     //      of the 8-byte block read by lane 16 (l / 16) + 4 e + (l % 16) / 4, so lane l reading
     //      dims 32 r + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 of key 16 j + 4 hf + (l % 16) / 4
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const int v_lane = (4 * hf + ((lane & 15) >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto vfrag = [&](int slot, int f) -> X8 {
-        const __bf16* v = Vs + slot * C::VBUF + v_lane + 16 * (f % (2 * PNKB)) * C::VP + 32 * (f / (2 * PNKB));
+        const __bf16* v = Vs + slot * C::VBUF + v_lane + 16 * (f / C::RT) * C::VP + 32 * (f % C::RT);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)v);
         const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(v + 8 * C::VP));
         return __builtin_bit_cast(X8, i16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         #pragma unroll
         for (int f = 0; f < NF; ++f) {
             if (f + PLDSD < NF) a[f + PLDSD] = vfrag(slot, f + PLDSD);
-            o[f / (2 * PNKB)] = Elem<T>::mfma(a[f], pp[f % (2 * PNKB)], o[f / (2 * PNKB)]);
+            o[f % C::RT] = Elem<T>::mfma(a[f], pp[f / C::RT], o[f % C::RT]);
         }
         constexpr int AH = PLDSD < NF ? PLDSD : NF;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);

@@ -22,6 +22,7 @@ LIB = os.path.join(os.path.dirname(HERE), "libmiattn_probes.so")
 
 PATTERNS = [
     (0, "16 v_mfma_f32_32x32x16_bf16"),
+    (9, "16 v_mfma_f32_32x32x16_bf16 on one accumulator (dependent chain)"),
     (1, "64 v_fma_f32"),
     (2, "32 v_exp_f32"),
     (3, "16 MFMA, each followed by 2 v_fma_f32 + 2 v_exp_f32 (one stream)"),

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void l2_gather(const u32x4* table, int ro
 //   6: as 4, with the MFMA waves at s_setprio 3;
 //   7: waves 0-3 the 16 MFMAs, waves 4-7 48 v_fma_f32 and 16 v_exp_f32 (a softmax's mix of
 //      vector work per 16 MFMAs);
-//   8: as 7, with the MFMA waves at s_setprio 3.
+//   8: as 7, with the MFMA waves at s_setprio 3;
+//   9: 16 MFMAs on one accumulator (each depends on the one before).
 // In the two-stream patterns the role is taken from a wave-uniform (scalar) wave index
 // outside the timed loop, so that each wave's loop holds its own instructions only.  The
 // vector instructions are written as inline assembly so that the count and encoding are
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long lon
         b[i] = (__bf16)(seed * (float)i);
     }
     f32x16 acc0 = {}, acc1 = {};
-    constexpr bool SPLIT = K == 4 || K >= 6;
+    constexpr bool SPLIT = K == 4 || (K >= 6 && K <= 8);
     const bool mfma_wave = !SPLIT || __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4;
     const unsigned long long t0 = __builtin_readcyclecounter();
     if (SPLIT && mfma_wave) {
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long lon
                 if constexpr (K == 0 || K == 3 || K == 5) {
                     if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
                 }
+                if constexpr (K == 9) PROBE_MFMA(acc0);
                 if constexpr (K == 1) { PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3); }
                 if constexpr (K == 2) { PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1); }
                 if constexpr (K == 3) { PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f); }
@@ -234,9 +236,9 @@ int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters)
 int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t blocks, int32_t waves_per_simd,
                        int32_t iters, void* stream)
 {
-    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 8) return (int)hipErrorInvalidValue;
+    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 9) return (int)hipErrorInvalidValue;
     if (waves_per_simd != 1 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
-    if ((kind == 4 || kind >= 6) && waves_per_simd != 2) return (int)hipErrorInvalidValue;
+    if ((kind == 4 || (kind >= 6 && kind <= 8)) && waves_per_simd != 2) return (int)hipErrorInvalidValue;
     const dim3 g(blocks), b(256 * waves_per_simd);
     const hipStream_t st = (hipStream_t)stream;
     unsigned long long* cy = (unsigned long long*)cycles;
@@ -249,7 +251,8 @@ int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t block
     case 5: hipLaunchKernelGGL(issue_probe<5>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 6: hipLaunchKernelGGL(issue_probe<6>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 7: hipLaunchKernelGGL(issue_probe<7>, g, b, 0, st, out, cy, iters, 0.001f); break;
-    default: hipLaunchKernelGGL(issue_probe<8>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 8: hipLaunchKernelGGL(issue_probe<8>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    default: hipLaunchKernelGGL(issue_probe<9>, g, b, 0, st, out, cy, iters, 0.001f); break;
     }
     return (int)hipGetLastError();
 }
