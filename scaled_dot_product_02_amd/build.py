@@ -73,9 +73,12 @@ def _hipcc(out: str, srcs, verbose: bool, libs=(), extra=(), link_extra=()) -> N
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip into libmiattn.so, and the peak probes (a measurement aid
     of the benchmark) into libmiattn_probes.so.  Always recompiles."""
-    # rocBLAS runs the two projections of the multi-head module (mha.hip)
-    _hipcc(LIB, sources(), verbose, libs=("-L/opt/rocm/lib", "-lrocblas"))
-    _hipcc(PROBES_LIB, [PROBES_SRC], verbose)
+    # rocBLAS runs the two projections of the multi-head module (mha.hip); an unresolved
+    # symbol (a kernel whose host launch stub the compiler did not emit) fails the link
+    # instead of the first launch
+    strict = ("-Wl,--no-undefined",)
+    _hipcc(LIB, sources(), verbose, libs=("-L/opt/rocm/lib", "-lrocblas"), link_extra=strict)
+    _hipcc(PROBES_LIB, [PROBES_SRC], verbose, link_extra=strict)
     return LIB
 
 
