@@ -115,11 +115,20 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def time_launches(fn, steps: int, warmup: int, stream):
+def time_launches(fn, steps: int, warmup: int, stream, warm_ms: float = 30.0):
+    """Mean milliseconds per launch of fn over `steps` launches, after `warmup` launches and
+    then more until at least warm_ms of warm-up work has run (the chip takes some
+    milliseconds of load to reach its steady clock; the first launches of a large kernel
+    run up to 20% slower)."""
+    import time as _time
     import torch
+    t0 = _time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while warm_ms > 0 and (_time.perf_counter() - t0) * 1e3 < warm_ms:
+        fn()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -244,7 +253,7 @@ def main():
         mi.attn_fwd_varlen(q, k, v, out, smax, ssum, cu, cu, B, T, T, maxlen, maxlen, Nq, Nkv, D,
                            "bf16", scale, "causal", 0, 0, stream.cuda_stream)
 
-    ms = time_launches(step, args.steps, args.warmup, stream)
+    ms = time_launches(step, args.steps, args.warmup, stream, warm_ms=0.0)   # exactly W warm-up steps
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic()
 
