@@ -104,7 +104,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     // compiler must assume that generic (flat) loads complete out of order with the buffer
     // loads of the tile prefetch, and would make each use of Q wait for all of them
     typedef __attribute__((address_space(1))) const X8 GX8;
-    typedef __attribute__((address_space(1))) X4 GX4;
+    typedef __attribute__((address_space(1))) X8 GX8w;
     typedef __attribute__((address_space(1))) const T GT_c;
     typedef __attribute__((address_space(1))) T GT;
     typedef __attribute__((address_space(1))) float GF;
@@ -561,26 +561,49 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         const int rows = rec32(s_rec[k].rows);
         const float lt = pair_sum(l_run);
         const int qi = wrow + lq;
-        if (qi < rows) {
-            const bool any = lt > 0.f;
+        const bool any = lt > 0.f;
+        const float wc = any ? 1.f / lt : 0.f;
+        // Lane (lq, hf) holds dims 8 g + 4 hf .. + 3 of its row in group g of each 32-dim
+        // block.  One exchange with the lane 32 apart (lanes 32-63 of the first operand
+        // trade with lanes 0-31 of the second) per pair of groups leaves lane (lq, 0) with
+        // dims 16 p .. + 7 and lane (lq, 1) with dims 16 p + 8 .. + 15 of the pair p, so
+        // each row takes 32 contiguous bytes per 16-byte-per-lane store, in half the
+        // store instructions of 8-byte pieces.  Every lane takes part in the exchange;
+        // only the stores are guarded by the row bound (both lanes of a row share it).
+        GT* orow = (GT*)(rec64(s_rec[k].oaddr) + o_wave + lq * o_row) + 8 * hf;
+        #pragma unroll
+        for (int r = 0; r < C::RT; ++r) {
+            uint32_t d[4][2];
+            #pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                X4 w;
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * wc);
+                const auto wd = __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), w);
+                d[g4][0] = wd[0];
+                d[g4][1] = wd[1];
+            }
+            #pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+                #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto x = __builtin_amdgcn_permlane32_swap(d[2 * pr][h], d[2 * pr + 1][h], false, false);
+                    d[2 * pr][h] = x[0];
+                    d[2 * pr + 1][h] = x[1];
+                }
+            if (qi < rows) {
+                #pragma unroll
+                for (int pr = 0; pr < 2; ++pr)
+                    *(GX8w*)(orow + 32 * r + 16 * pr) =
+                        __builtin_bit_cast(X8, u32x4{d[2 * pr][0], d[2 * pr][1], d[2 * pr + 1][0], d[2 * pr + 1][1]});
+            }
+        }
+        if (qi < rows && hf == 0) {
             const float m_out = any ? m_true * 0.69314718055994530942f : -INFINITY;
             const float l_out = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
-            const float wc = any ? 1.f / lt : 0.f;
-            GT* orow = (GT*)(rec64(s_rec[k].oaddr) + o_wave + lq * o_row) + 4 * hf;
-            #pragma unroll
-            for (int r = 0; r < C::RT; ++r)
-                #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    X4 w;
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * wc);
-                    *(GX4*)(orow + 32 * r + 8 * g4) = w;
-                }
-            if (hf == 0) {
-                const int64_t si = rec64(s_rec[k].st) + st_wave + lq;
-                if (want_max) ((GF*)smax)[si] = m_out;
-                if (want_sum) ((GF*)ssum)[si] = l_out;
-            }
+            const int64_t si = rec64(s_rec[k].st) + st_wave + lq;
+            if (want_max) ((GF*)smax)[si] = m_out;
+            if (want_sum) ((GF*)ssum)[si] = l_out;
         }
         m_ref = m_true = -INFINITY;
         l_run = 0.f;
