@@ -717,51 +717,76 @@ void fa_fwd_bf16_kernel(FaParams p)
     //      out = o_p a / (a + c) + (O / lt) c / (a + c), before the single rounding.
     const float lt = pair_sum(l_run);
     const int qi = rb + lq;
-    if (qi < re) {
-        const bool any = lt > 0.f;
-        const float mc = any ? m_true * 0.69314718055994530942f : -INFINITY;
-        float m_out = mc;
-        float l_out = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
-        float wc = any ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;   // weight of the accumulator O
-        float wp = 0.f;                    // weight of the prior output
-        if constexpr (UPDATE) {
-            const float mp = p.prev_max[st_base + qi], lp = p.prev_sum[st_base + qi];
-            const float m = fmaxf(mp, mc);
-            wc = 0.f;
-            l_out = 0.f;
-            if (m != -INFINITY) {
-                const float a = lp * __builtin_amdgcn_exp2f((mp - m) * 1.4426950408889634f);
-                const float f = any ? __builtin_amdgcn_exp2f(m_ref - m * 1.4426950408889634f) : 0.f;
-                l_out = a + lt * f;
-                wp = a / l_out;
-                wc = f / l_out;
-            }
-            m_out = m;
+    const bool valid = qi < re;          // both lanes of a row share it
+    const bool any = lt > 0.f;
+    const float mc = any ? m_true * 0.69314718055994530942f : -INFINITY;
+    float m_out = mc;
+    float l_out = any ? lt * __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
+    float wc = any ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;   // weight of the accumulator O
+    float wp = 0.f;                    // weight of the prior output
+    if constexpr (UPDATE) {
+        const float mp = valid ? p.prev_max[st_base + qi] : -INFINITY;
+        const float lp = valid ? p.prev_sum[st_base + qi] : 0.f;
+        const float m = fmaxf(mp, mc);
+        wc = 0.f;
+        l_out = 0.f;
+        if (m != -INFINITY) {
+            const float a = lp * __builtin_amdgcn_exp2f((mp - m) * 1.4426950408889634f);
+            const float f = any ? __builtin_amdgcn_exp2f(m_ref - m * 1.4426950408889634f) : 0.f;
+            l_out = a + lt * f;
+            wp = a / l_out;
+            wc = f / l_out;
         }
-        T* orow = og + (int64_t)qi * p.o_ss + 4 * hf;
+        m_out = m;
+    }
+    // Lane (lq, hf) holds dims 8 g + 4 hf .. + 3 of its row in group g of each 32-dim block;
+    // one exchange with the lane 32 apart per pair of groups (lanes 32-63 of the first
+    // operand trade with lanes 0-31 of the second) leaves lane (lq, 0) with dims 16 p .. + 7
+    // and lane (lq, 1) with dims 16 p + 8 .. + 15 of pair p: each row then takes 32
+    // contiguous bytes per 16-byte-per-lane store.  Every lane takes part in the exchange;
+    // the reads of the prior and the stores are guarded by the row bound.
+    T* orow = og + (int64_t)qi * p.o_ss + 4 * hf;    // this lane's 8-byte pieces
+    T* orow16 = og + (int64_t)qi * p.o_ss + 8 * hf;  // this lane's 16-byte pieces
+    #pragma unroll
+    for (int r = 0; r < C::RT; ++r) {
+        uint32_t d[4][2];
         #pragma unroll
-        for (int r = 0; r < C::RT; ++r)
-            #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                X4 w;
-                if constexpr (UPDATE) {
-                    // an empty prior (weight 0) is not read: its buffer may hold anything
-                    const T* prow = (const T*)p.prev_out + (orow - (T*)p.out);
-                    X4 po{};
-                    if (wp != 0.f) po = *(const X4*)(prow + 32 * r + 8 * g4);
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = (T)__builtin_fmaf((float)po[e], wp, o[r][4 * g4 + e] * wc);
-                } else {
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * wc);
-                }
-                *(X4*)(orow + 32 * r + 8 * g4) = w;
+        for (int g4 = 0; g4 < 4; ++g4) {
+            X4 w;
+            if constexpr (UPDATE) {
+                // an empty prior (weight 0) is not read: its buffer may hold anything
+                const T* prow = (const T*)p.prev_out + (orow - (T*)p.out);
+                X4 po{};
+                if (valid && wp != 0.f) po = *(const X4*)(prow + 32 * r + 8 * g4);
+                #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (T)__builtin_fmaf((float)po[e], wp, o[r][4 * g4 + e] * wc);
+            } else {
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (T)(o[r][4 * g4 + e] * wc);
             }
-        if (hf == 0) {
-            if (p.smax) p.smax[st_base + qi] = m_out;
-            if (p.ssum) p.ssum[st_base + qi] = l_out;
+            const auto wd = __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), w);
+            d[g4][0] = wd[0];
+            d[g4][1] = wd[1];
         }
+        #pragma unroll
+        for (int pr = 0; pr < 2; ++pr)
+            #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const auto x = __builtin_amdgcn_permlane32_swap(d[2 * pr][h], d[2 * pr + 1][h], false, false);
+                d[2 * pr][h] = x[0];
+                d[2 * pr + 1][h] = x[1];
+            }
+        if (valid) {
+            #pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+                *(X8*)(orow16 + 32 * r + 16 * pr) =
+                    __builtin_bit_cast(X8, u32x4{d[2 * pr][0], d[2 * pr][1], d[2 * pr + 1][0], d[2 * pr + 1][1]});
+        }
+    }
+    if (valid && hf == 0) {
+        if (p.smax) p.smax[st_base + qi] = m_out;
+        if (p.ssum) p.ssum[st_base + qi] = l_out;
     }
 }
 
