@@ -48,8 +48,9 @@ int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters);
  * each followed by 4 v_fma_f32 + 2 v_exp_f32.  Two streams per SIMD (waves_per_simd 2 only;
  * waves 0-3 issue the 16 MFMAs, waves 4-7 vector work): 4 = 32 v_fma_f32 + 32 v_exp_f32;
  * 6 = as 4 with the MFMA waves at s_setprio 3; 7 = 48 v_fma_f32 + 16 v_exp_f32; 8 = as 7 with
- * the MFMA waves at s_setprio 3; 9 = 16 MFMAs on one accumulator (a dependent chain).
- * waves_per_simd: 1 or 2.  out: float
+ * the MFMA waves at s_setprio 3; 9 = 16 MFMAs on one accumulator (a dependent chain);
+ * 10 = 64 v_fma_f32 in one dependent chain; 11 = 32 v_exp_f32, each followed by a
+ * v_add_f32 of its result.  waves_per_simd: 1 or 2.  out: float
  * [blocks * 256 * waves_per_simd]; cycles: uint64 [blocks * 32], the start and end clock of
  * wave w of workgroup g at [32 g + 2 w] and [32 g + 2 w + 1] and the SIMD the wave ran on at
  * [32 g + 16 + w].  Returns 0 or the HIP error code (invalid arguments:

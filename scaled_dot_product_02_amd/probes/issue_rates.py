@@ -24,7 +24,9 @@ PATTERNS = [
     (0, "16 v_mfma_f32_32x32x16_bf16"),
     (9, "16 v_mfma_f32_32x32x16_bf16 on one accumulator (dependent chain)"),
     (1, "64 v_fma_f32"),
+    (10, "64 v_fma_f32 in one dependent chain"),
     (2, "32 v_exp_f32"),
+    (11, "32 v_exp_f32, each followed by a v_add_f32 of its result"),
     (3, "16 MFMA, each followed by 2 v_fma_f32 + 2 v_exp_f32 (one stream)"),
     (5, "16 MFMA, each followed by 4 v_fma_f32 + 2 v_exp_f32 (one stream)"),
     (4, "per SIMD: one wave 16 MFMA, the other 32 v_fma_f32 + 32 v_exp_f32"),

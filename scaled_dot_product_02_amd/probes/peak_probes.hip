@@ -108,7 +108,9 @@ __global__ __launch_bounds__(kThreads) void l2_gather(const u32x4* table, int ro
 //   7: waves 0-3 the 16 MFMAs, waves 4-7 48 v_fma_f32 and 16 v_exp_f32 (a softmax's mix of
 //      vector work per 16 MFMAs);
 //   8: as 7, with the MFMA waves at s_setprio 3;
-//   9: 16 MFMAs on one accumulator (each depends on the one before).
+//   9: 16 MFMAs on one accumulator (each depends on the one before);
+//  10: 64 v_fma_f32 in one dependent chain;
+//  11: 32 v_exp_f32, each followed by a v_add_f32 that reads its result (into 4 sums).
 // In the two-stream patterns the role is taken from a wave-uniform (scalar) wave index
 // outside the timed loop, so that each wave's loop holds its own instructions only.  The
 // vector instructions are written as inline assembly so that the count and encoding are
@@ -163,6 +165,11 @@ __global__ __launch_bounds__(512) void issue_probe(float* out, unsigned long lon
                     if (f & 1) PROBE_MFMA(acc1); else PROBE_MFMA(acc0);
                 }
                 if constexpr (K == 9) PROBE_MFMA(acc0);
+                if constexpr (K == 10) { PROBE_FMA(0); PROBE_FMA(0); PROBE_FMA(0); PROBE_FMA(0); }
+                if constexpr (K == 11) {
+                    PROBE_EXP(8 + 2 * f); asm volatile("v_add_f32_e32 %0, %0, %1" : "+v"(x[f & 3]) : "v"(x[8 + 2 * f]));
+                    PROBE_EXP(9 + 2 * f); asm volatile("v_add_f32_e32 %0, %0, %1" : "+v"(x[(f + 2) & 3]) : "v"(x[9 + 2 * f]));
+                }
                 if constexpr (K == 1) { PROBE_FMA(4 * f); PROBE_FMA(4 * f + 1); PROBE_FMA(4 * f + 2); PROBE_FMA(4 * f + 3); }
                 if constexpr (K == 2) { PROBE_EXP(2 * f); PROBE_EXP(2 * f + 1); }
                 if constexpr (K == 3) { PROBE_FMA(2 * f); PROBE_FMA(2 * f + 1); PROBE_EXP(32 + 2 * f); PROBE_EXP(33 + 2 * f); }
@@ -236,7 +243,7 @@ int64_t miattn_probe_l2_gather_bytes(int32_t blocks, int32_t iters)
 int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t blocks, int32_t waves_per_simd,
                        int32_t iters, void* stream)
 {
-    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 9) return (int)hipErrorInvalidValue;
+    if (!out || !cycles || blocks < 1 || iters < 1 || kind < 0 || kind > 11) return (int)hipErrorInvalidValue;
     if (waves_per_simd != 1 && waves_per_simd != 2) return (int)hipErrorInvalidValue;
     if ((kind == 4 || (kind >= 6 && kind <= 8)) && waves_per_simd != 2) return (int)hipErrorInvalidValue;
     const dim3 g(blocks), b(256 * waves_per_simd);
@@ -252,7 +259,9 @@ int miattn_probe_issue(int32_t kind, float* out, uint64_t* cycles, int32_t block
     case 6: hipLaunchKernelGGL(issue_probe<6>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 7: hipLaunchKernelGGL(issue_probe<7>, g, b, 0, st, out, cy, iters, 0.001f); break;
     case 8: hipLaunchKernelGGL(issue_probe<8>, g, b, 0, st, out, cy, iters, 0.001f); break;
-    default: hipLaunchKernelGGL(issue_probe<9>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 9: hipLaunchKernelGGL(issue_probe<9>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    case 10: hipLaunchKernelGGL(issue_probe<10>, g, b, 0, st, out, cy, iters, 0.001f); break;
+    default: hipLaunchKernelGGL(issue_probe<11>, g, b, 0, st, out, cy, iters, 0.001f); break;
     }
     return (int)hipGetLastError();
 }

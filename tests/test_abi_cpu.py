@@ -80,7 +80,7 @@ def test_probe_library_exports_its_declared_symbols():
     assert probes.miattn_probe_l2_gather(256, 13, 8, 12, 256, None) != 0   # iters % 8
     probes.miattn_probe_issue.argtypes = ([ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] +
                                           [ctypes.c_int32] * 3 + [ctypes.c_void_p])
-    assert probes.miattn_probe_issue(10, 256, 256, 1, 2, 1, None) != 0   # unknown kind
+    assert probes.miattn_probe_issue(12, 256, 256, 1, 2, 1, None) != 0   # unknown kind
     assert probes.miattn_probe_issue(4, 256, 256, 1, 1, 1, None) != 0    # two-stream kinds need two waves per SIMD
     assert probes.miattn_probe_issue(8, 256, 256, 1, 1, 1, None) != 0
     assert probes.miattn_probe_issue(0, 256, 256, 1, 3, 1, None) != 0    # waves per SIMD 1 or 2
