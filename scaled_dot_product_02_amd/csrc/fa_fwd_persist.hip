@@ -1,6 +1,7 @@
 // Attention forward, bf16 / fp16 inputs, masks whose visible keys start at key 0 (causal
-// either way round, no mask, or a band with no lower bound): the persistent form of the
-// tiled MFMA kernel, for packed (TND) and dense forwards with GQA.
+// either way round, with or without a per-sequence prefix, no mask, or a band with no lower
+// bound): the persistent form of the tiled MFMA kernel, for packed (TND) and dense forwards
+// with GQA.
 //
 // What it computes is what the tiled kernel computes (out = softmax(scale * Q K^T) V per
 // sequence and query head with the per-row softmax max and sum; Paddle "sparse_attention"
@@ -71,6 +72,7 @@ struct PItem {
     int r0, r1;
     int T0, T1;             // key tiles [T0, T1) seen by some row of the item
     int off;                // causal diagonal: row i sees keys 0 .. i + off
+    int pfx;                // and keys 0 .. pfx - 1 (the prefix; 0 without one)
 };
 
 // What the key loop needs of an item, computed once when the workgroup lists its items
@@ -82,7 +84,7 @@ struct PRec {
     int32_t rows;           // r1 - r0
     int32_t diag;           // r0 + off: item row i sees keys 0 .. diag + i
     int32_t T0, T1;         // key tiles
-    int32_t pad;
+    int32_t pfx;            // keys 0 .. pfx - 1 are visible from every row (the prefix)
 };
 static_assert(sizeof(PRec) == 64, "one LDS record per item");
 
@@ -250,8 +252,14 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                         const int64_t off64 = (p.align_br ? (int64_t)it.len_kv - it.len_q : 0) + p.next;
                         it.off = (int)(off64 > it.len_kv ? it.len_kv : (off64 < -(int64_t)it.len_q - 1 ? -it.len_q - 1 : off64));
                     }
-                    // rows [r0, r1) see keys 0 .. r1 - 1 + off
-                    const int vis = max(0, min(it.r1 + it.off, it.len_kv));
+                    // a per-sequence prefix: keys below it are visible from every row
+                    it.pfx = 0;
+                    if (p.prefix) {
+                        const int64_t x = p.prefix[it.b];
+                        it.pfx = x < 0 ? 0 : (x > it.len_kv ? it.len_kv : (int)x);
+                    }
+                    // rows [r0, r1) see keys 0 .. max(r1 - 1 + off, pfx - 1)
+                    const int vis = max(0, min(max(it.r1 + it.off, it.pfx), it.len_kv));
                     it.T0 = 0;
                     it.T1 = (vis + PBN - 1) / PBN;
                 }
@@ -274,6 +282,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                     rc.diag = it.r0 + it.off;
                     rc.T0 = it.T0;
                     rc.T1 = it.T1;
+                    rc.pfx = it.pfx;
                 }
                 int st = live && pos < MAXI ? it.T1 - it.T0 : 0;
                 #pragma unroll
@@ -407,20 +416,21 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     int full_hi = 0;     // tiles [0, full_hi) are visible in full from every row of the wave
     int jhi = -1;        // keys [0, jhi] are visible from this lane's row
 
-    // bounds of item k for this wave (causal: item row i sees keys 0 .. diag + i)
+    // bounds of item k for this wave (causal: item row i sees keys 0 .. max(diag + i, pfx - 1))
     auto item_bounds = [&](int k) {
         const int rows = rec32(s_rec[k].rows);
         const int diag = rec32(s_rec[k].diag);
         const int len_kv = rec32(s_rec[k].len_kv);
+        const int pfx = rec32(s_rec[k].pfx);
         c_T0 = rec32(s_rec[k].T0);
         c_T1 = rec32(s_rec[k].T1);
         const int re = min(wrow + 32, rows);   // this wave's item rows [wrow, re)
         w_hi = full_hi = 0;
         jhi = -1;
         if (wrow < re) {
-            w_hi = (max(0, min(diag + re, len_kv)) + PBN - 1) / PBN;
-            full_hi = max(0, min(diag + wrow + 1, len_kv)) / PBN;
-            jhi = min(diag + wrow + lq, len_kv - 1);
+            w_hi = (max(0, min(max(diag + re, pfx), len_kv)) + PBN - 1) / PBN;
+            full_hi = max(0, min(max(diag + wrow + 1, pfx), len_kv)) / PBN;
+            jhi = min(max(diag + wrow + lq, pfx - 1), len_kv - 1);
         }
     };
     // Q rows of item k for this wave: B operand of S^T = K Q^T, lane (lq, hf) holds

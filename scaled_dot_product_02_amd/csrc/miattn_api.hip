@@ -157,14 +157,16 @@ bool persist_enabled()
 }
 
 // Whether a forward that the tiled kernel would serve runs on the persistent one: causal
-// (either alignment) without a prefix, mask tensor, dropout or prior, head dim 64 or 128
-// with V of the same head dim, packed batches of at most kPersistMaxSeq sequences.
+// (either alignment, with or without a prefix) without a mask tensor, dropout or prior,
+// head dim 64 or 128 with V of the same head dim, packed batches of at most
+// kPersistMaxSeq sequences.
 bool use_persistent(const FaParams& p, int64_t D, int64_t Tq, int n_wg)
 {
     if (D != 64 && D != 128) return false;
-    if (p.Dv != D || p.prev_out || p.amask || p.drop_thr || p.prefix) return false;
-    // every row's visible keys start at key 0 (no mask, causal, or a band with no lower
-    // bound): the kernel moves the causal diagonal by the band's upper bound
+    if (p.Dv != D || p.prev_out || p.amask || p.drop_thr) return false;
+    // every row's visible keys start at key 0 (no mask, causal with or without a prefix,
+    // or a band with no lower bound): the kernel moves the causal diagonal by the band's
+    // upper bound and extends each row's keys to the prefix
     if (p.pre != kTokensClamp) return false;
     if (p.cu_q && p.B > kPersistMaxSeq) return false;
     // items: sum over sequences of their query tiles, times the head groups; packed

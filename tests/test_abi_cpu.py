@@ -135,7 +135,8 @@ def test_attn_fwd_validation(mi):
 
 def test_attn_fwd_route_persistent(mi, monkeypatch):
     """bf16 / fp16 forwards at head dim 64 or 128 whose visible keys start at key 0 (causal,
-    no mask, a band without a lower bound), without a prefix, mask tensor, dropout or prior,
+    no mask, a band without a lower bound; with or without a prefix), without a mask tensor,
+    dropout or prior,
     run on the persistent kernel while every workgroup's items fit its LDS list;
     MIATTN_PERSIST=0 sends them to the tiled kernel."""
     r = mi.attn_fwd_route

@@ -242,3 +242,108 @@ def test_dense_no_mask(mi, layout):
         wo, wm, wl = oracle.attn(qo, ko, vo, 1 / math.sqrt(D), "none")
         check_out(synthetic.to_bnsd(a[0], layout, 8), wo, dt, f"dense none {layout} D {D}")
         check_stats(a[1], a[2], wm, wl)
+
+
+def _varlen_prefix_run(mi, w, mask, prefix):
+    dt = w["dtype"]
+    q, k, v = dev(w["q"], dt), dev(w["k"], dt), dev(w["v"], dt)
+    cq = torch.from_numpy(w["cu_q"]).to("cuda:0")
+    ck = torch.from_numpy(w["cu_kv"]).to("cuda:0")
+    pf = torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
+    mq = max(1, int(w["lengths_q"].max()))
+    mk = max(1, int(w["lengths_kv"].max()))
+    D = w["D"]
+
+    def run():
+        out = empty_like_storage(q.shape, dt)
+        m, l = nan_stats((w["Nq"], w["Tq"])), nan_stats((w["Nq"], w["Tq"]))
+        mi.attn_fwd_varlen_ext(q, k, v, out, m, l, cq, ck, w["B"], w["Tq"], w["Tkv"], mq, mk,
+                               w["Nq"], w["Nkv"], D, D, dt, 1 / math.sqrt(D), mask, 0, 0, pf, None)
+        torch.cuda.synchronize()
+        return host_values(out), host_values(m), host_values(l)
+    return run
+
+
+def _keep_prefix(mask, prefix):
+    """Visibility of sequence b under causal (top-left) or bottom-right causal plus the prefix
+    clamped to [0, Skv] (the oracle's own definitions)."""
+    def keep(b, sq, sk):
+        pfx = min(max(int(prefix[b]), 0), sk)
+        if mask == "causal_br":
+            return oracle.keep_prefix_causal(sq, sk, pfx)
+        return oracle.keep_band(sq, sk, 1 << 62, 0) | (np.arange(sk)[None, :] < pfx)
+    return keep
+
+
+@pytest.mark.parametrize("mask", ["causal", "causal_br"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Nq,Nkv", [(8, 2), (6, 6)])
+def test_prefix_against_oracle_and_tiled(mi, mask, D, Nq, Nkv):
+    """A per-sequence prefix (keys below it visible from every row) on packed batches whose
+    query and key lengths differ per sequence: prefixes of 0, inside the first key tile,
+    across tiles, past the keys (clamped) and negative (clamped to 0), so that some items
+    see more key tiles than their causal diagonal and some rows see only prefix keys.  The
+    persistent kernel equals the tiled one bit for bit and the oracle within tolerance."""
+    lq = [300, 0, 1, 129, 64, 517, 2, 65, 190]
+    lk = [300, 40, 0, 200, 64, 400, 2, 65, 3]
+    prefix = [200, 7, 5, 150, 0, 333, -4, 64, 900]
+    w = synthetic.varlen_inputs(540 + D + Nq + len(mask), Nq=Nq, Nkv=Nkv, D=D, dtype="bf16",
+                                lengths_q=lq, lengths_kv=lk)
+    a, b = _both(_varlen_prefix_run(mi, w, mask, prefix))
+    _assert_identical(a, b, f"prefix {mask} D {D}")
+    q, k, v = (synthetic.storage_values(w[x], "bf16") for x in ("q", "k", "v"))
+    wo, wm, wl = oracle.attn_varlen_keep(q, k, v, w["cu_q"], w["cu_kv"], _keep_prefix(mask, prefix),
+                                         1 / math.sqrt(D))
+    check_out(a[0], wo, "bf16", f"prefix {mask} D {D}")
+    check_stats(a[1], a[2], wm, wl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_full_workload_prefix_matches_tiled_bit_for_bit(mi, dtype):
+    """The 16-sequence packed causal GQA workload with a prefix of a third of each sequence
+    (bottom-right causal): persistent and tiled kernels agree bit for bit; sampled
+    (sequence, head) slices against the oracle."""
+    w = synthetic.varlen_inputs(0, Nq=32, Nkv=8, D=128, dtype=dtype, B=16)
+    prefix = [int(L) // 3 for L in w["lengths_kv"]]
+    a, b = _both(_varlen_prefix_run(mi, w, "causal_br", prefix))
+    _assert_identical(a, b, f"full workload prefix {dtype}")
+    q, k, v = (synthetic.storage_values(w[x], dtype) for x in ("q", "k", "v"))
+    cu = w["cu_q"]
+    keep = _keep_prefix("causal_br", prefix)
+    for s, h in ((0, 0), (5, 17), (11, 31), (15, 8)):
+        lo, hi = (int(cu[s - 1]) if s else 0), int(cu[s])
+        if hi == lo:
+            continue
+        hk = h // 4
+        wo, wm, wl = oracle.attn_keep(q[lo:hi, h][None, None], k[lo:hi, hk][None, None],
+                                      v[lo:hi, hk][None, None], keep(s, hi - lo, hi - lo),
+                                      1 / math.sqrt(128))
+        check_out(a[0][lo:hi, h], wo[0, 0], dtype, f"prefix seq {s} head {h}")
+        check_stats(a[1][h, lo:hi], a[2][h, lo:hi], wm[0, 0], wl[0, 0])
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "SBH"])
+def test_dense_prefix_against_oracle_and_tiled(mi, layout):
+    """Dense batches with a prefix per batch entry (0, inside the diagonal, past Skv),
+    causal top-left with Sq < Skv, GQA 8 / 2, D 128 bf16."""
+    B, Nq, Nkv, Sq, Skv, D = 3, 8, 2, 500, 700, 128
+    prefix = [0, 300, 1000]
+    w = synthetic.dense_inputs(560, B, Nq, Nkv, Sq, Skv, D, "bf16", layout)
+    q, k, v = dev(w["q"], "bf16"), dev(w["k"], "bf16"), dev(w["v"], "bf16")
+    pf = torch.from_numpy(np.asarray(prefix, np.int64)).to("cuda:0")
+
+    def run():
+        out = empty_like_storage(q.shape, "bf16")
+        m, l = nan_stats((B, Nq, Sq)), nan_stats((B, Nq, Sq))
+        mi.attn_fwd_ext(q, k, v, out, m, l, B, Nq, Nkv, Sq, Skv, D, D, "bf16", layout,
+                        1 / math.sqrt(D), "causal", 0, 0, pf, None)
+        torch.cuda.synchronize()
+        return host_values(out), host_values(m), host_values(l)
+    a, b = _both(run)
+    _assert_identical(a, b, f"dense prefix {layout}")
+    qo, ko, vo = (synthetic.to_bnsd(synthetic.storage_values(w[x], "bf16"), layout, n)
+                  for x, n in (("q", Nq), ("k", Nkv), ("v", Nkv)))
+    keep = np.stack([_keep_prefix("causal", prefix)(bb, Sq, Skv) for bb in range(B)])
+    wo, wm, wl = oracle.attn_keep(qo, ko, vo, keep, 1 / math.sqrt(D))
+    check_out(synthetic.to_bnsd(a[0], layout, Nq), wo, "bf16", f"dense prefix {layout}")
+    check_stats(a[1], a[2], wm, wl)
