@@ -113,7 +113,7 @@ struct Cfg {
 
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
-// each tile's mask words are loaded at the end of the previous tile's softmax phase.
+// each tile's mask bytes are loaded at the end of the previous tile's softmax phase.
 // DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
 template <int D, int DV, bool MASKED, bool DROP>
 using KCfg = Cfg<D, DV, fa_four_waves(D, MASKED || DROP)>;
@@ -261,19 +261,35 @@ void fa_fwd_bf16_kernel(FaParams p)
         const int n = __builtin_amdgcn_readfirstlane((int)bytes);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
     };
-    // explicit mask: this lane's row; the 8 words of the tile in softmax, loaded a step
-    // ahead (byte e of word 4b + g: key 32b + 8g + 4hf + e of the tile)
-    unsigned mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // explicit mask: this lane's row, loaded a step ahead as two 16-byte pieces: lane
+    // (lq, hf) reads the 32 bytes of 32-key block hf of the tile (word j: keys 4j .. 4j + 3
+    // of the block).  The softmax needs, in word 4b + g, the bytes of keys
+    // 32b + 8g + 4hf .. + 3 (byte e: key + e), so lane hf keeps words 2g + hf of both
+    // blocks: one lane-pair exchange per g trades block 0's odd words (held by the hf = 0
+    // lanes) for block 1's even words (held by the hf = 1 lanes).  Two wide loads touch a
+    // quarter of the cache lines that eight 4-byte loads do.
+    u32x4 mraw[2] = {u32x4{}, u32x4{}};
     __amdgpu_buffer_rsrc_t rmask;
     uint32_t moff = 0;
     if constexpr (MASKED) {
         rmask = rsrc(p.amask, (int64_t)p.Sq * p.amask_ld);
-        moff = (uint32_t)((int64_t)min(rb + lq, p.Sq - 1) * p.amask_ld) + 4 * hf;
+        moff = (uint32_t)((int64_t)min(rb + lq, p.Sq - 1) * p.amask_ld) + 32 * hf;
     }
     auto load_mask = [&](int t) {
         #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            mw[k] = __builtin_amdgcn_raw_buffer_load_b32(rmask, moff + t * BN + 32 * (k >> 2) + 8 * (k & 3), 0, 0);
+        for (int k = 0; k < 2; ++k)
+            mraw[k] = __builtin_amdgcn_raw_buffer_load_b128(rmask, moff + t * BN + 16 * k, 0, 0);
+    };
+    // the words of the softmax order (byte e of word 4b + g: key 32b + 8g + 4hf + e)
+    auto mask_words = [&](unsigned (&mw)[8]) {
+        #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const unsigned even = mraw[g >> 1][2 * (g & 1)], odd = mraw[g >> 1][2 * (g & 1) + 1];
+            // lanes 32-63 of the first operand trade with lanes 0-31 of the second
+            const auto x = __builtin_amdgcn_permlane32_swap(even, odd, false, false);
+            mw[g] = x[0];
+            mw[4 + g] = x[1];
+        }
     };
     auto load_tile = [&](int t, u32x4 (&stage)[C::SREG]) {
         const int j0 = t * BN;
@@ -420,6 +436,8 @@ void fa_fwd_bf16_kernel(FaParams p)
         const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
         if constexpr (MASKED) {
             // element i of block b: byte i % 4 of word 4b + i / 4 (one byte-select compare each)
+            unsigned mw[8];
+            mask_words(mw);
             #pragma unroll
             for (int b = 0; b < NKB; ++b)
                 #pragma unroll
