@@ -113,7 +113,8 @@ struct Cfg {
 
 // UPDATE = true: the epilogue merges the partial result into p.prev_* (ring update).
 // MASKED = true: the explicit mask p.amask (rows 4-byte aligned) removes keys as well;
-// each tile's mask bytes are loaded at the end of the previous tile's softmax phase.
+// each tile's mask bytes are loaded in the previous tile's matrix-core phase and set the
+// initial value of its score accumulators.
 // DROP = true: dropout on the probabilities (p.drop_*), the kept ones scaled in the epilogue.
 template <int D, int DV, bool MASKED, bool DROP>
 using KCfg = Cfg<D, DV, fa_four_waves(D, MASKED || DROP)>;
@@ -261,13 +262,13 @@ void fa_fwd_bf16_kernel(FaParams p)
         const int n = __builtin_amdgcn_readfirstlane((int)bytes);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
     };
-    // explicit mask: this lane's row, loaded a step ahead as two 16-byte pieces: lane
-    // (lq, hf) reads the 32 bytes of 32-key block hf of the tile (word j: keys 4j .. 4j + 3
-    // of the block).  The softmax needs, in word 4b + g, the bytes of keys
-    // 32b + 8g + 4hf .. + 3 (byte e: key + e), so lane hf keeps words 2g + hf of both
-    // blocks: one lane-pair exchange per g trades block 0's odd words (held by the hf = 0
-    // lanes) for block 1's even words (held by the hf = 1 lanes).  Two wide loads touch a
-    // quarter of the cache lines that eight 4-byte loads do.
+    // explicit mask: this lane's row, loaded a step before its Q K^T products as two
+    // 16-byte pieces: lane (lq, hf) reads the 32 bytes of 32-key block hf of the tile (word
+    // j: keys 4j .. 4j + 3 of the block).  The scores of the lane need, in word 4b + g, the
+    // bytes of keys 32b + 8g + 4hf .. + 3 (byte e: key + e), so lane hf keeps words 2g + hf
+    // of both blocks: one lane-pair exchange per g trades block 0's odd words (held by the
+    // hf = 0 lanes) for block 1's even words (held by the hf = 1 lanes).  Two wide loads
+    // touch a quarter of the cache lines that eight 4-byte loads do.
     u32x4 mraw[2] = {u32x4{}, u32x4{}};
     __amdgpu_buffer_rsrc_t rmask;
     uint32_t moff = 0;
@@ -280,7 +281,7 @@ void fa_fwd_bf16_kernel(FaParams p)
         for (int k = 0; k < 2; ++k)
             mraw[k] = __builtin_amdgcn_raw_buffer_load_b128(rmask, moff + t * BN + 16 * k, 0, 0);
     };
-    // the words of the softmax order (byte e of word 4b + g: key 32b + 8g + 4hf + e)
+    // the words in score order (byte e of word 4b + g: key 32b + 8g + 4hf + e)
     auto mask_words = [&](unsigned (&mw)[8]) {
         #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -344,18 +345,37 @@ void fa_fwd_bf16_kernel(FaParams p)
     // ---- S^T = K Q^T for tile t (NKB blocks of 32 keys x 32 queries)
     auto qk = [&](int t, f32x16 (&s)[NKB]) {
         const __bf16* kb = Ks + (t & (NBUF - 1)) * C::KBUF + lq * C::KS + 8 * hf;
-        constexpr int NF = C::KK * NKB;   // fragments (= MFMAs), fragment f: kk = f / NKB, b = f % NKB
+        constexpr int NF = C::KK * NKB;   // fragments (= MFMAs)
+        // fragment f: block b and k-step kk.  The plain instance alternates the blocks; the
+        // mask tensor instance takes block 0's MFMAs first, so that block 1's initial values
+        // are formed while they run
+        auto fb = [](int f) { return MASKED ? f / C::KK : f % NKB; };
+        auto fk = [](int f) { return MASKED ? f % C::KK : f / NKB; };
         X8 a[NF];
         #pragma unroll
-        for (int b = 0; b < NKB; ++b) s[b] = f32x16{};
-        #pragma unroll
         for (int f = 0; f < LDSD && f < NF; ++f)
-            a[f] = *(const X8*)(kb + 32 * (f % NKB) * C::KS + 16 * (f / NKB));
+            a[f] = *(const X8*)(kb + 32 * fb(f) * C::KS + 16 * fk(f));
+        if constexpr (MASKED) {
+            // the mask tensor enters as the scores' initial value: -inf for a removed key
+            // (-inf plus the finite dot product stays -inf), 0 otherwise; the byte tests run
+            // beside this wave's own MFMAs instead of in the softmax phase.  Element i of
+            // block b is byte i % 4 of word 4b + i / 4
+            unsigned mw[8];
+            mask_words(mw);
+            #pragma unroll
+            for (int b = 0; b < NKB; ++b)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[b][i] = (mw[4 * b + (i >> 2)] >> (8 * (i & 3)) & 0xffu) != 0u ? -INFINITY : 0.f;
+        } else {
+            #pragma unroll
+            for (int b = 0; b < NKB; ++b) s[b] = f32x16{};
+        }
         #pragma unroll
         for (int f = 0; f < NF; ++f) {
             if (f + LDSD < NF)
-                a[f + LDSD] = *(const X8*)(kb + 32 * ((f + LDSD) % NKB) * C::KS + 16 * ((f + LDSD) / NKB));
-            s[f % NKB] = Elem<T>::mfma(a[f], qf[f / NKB], s[f % NKB]);
+                a[f + LDSD] = *(const X8*)(kb + 32 * fb(f + LDSD) * C::KS + 16 * fk(f + LDSD));
+            s[fb(f)] = Elem<T>::mfma(a[f], qf[fk(f)], s[fb(f)]);
         }
 #if FA_SCHED
         // keep LDSD reads in flight ahead of the MFMAs that consume them
@@ -434,16 +454,6 @@ void fa_fwd_bf16_kernel(FaParams p)
     // ---- online softmax of tile t; leaves bf16 probabilities in pp
     auto softmax = [&](int t, f32x16 (&s)[NKB], X8 (&pp)[2 * NKB]) {
         const int jb = t * BN + 4 * hf;   // key of element i of block b: jb + 32b + 8(i/4) + i%4
-        if constexpr (MASKED) {
-            // element i of block b: byte i % 4 of word 4b + i / 4 (one byte-select compare each)
-            unsigned mw[8];
-            mask_words(mw);
-            #pragma unroll
-            for (int b = 0; b < NKB; ++b)
-                #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if ((mw[4 * b + (i >> 2)] >> (8 * (i & 3)) & 0xffu) != 0u) s[b][i] = -INFINITY;
-        }
         if (t < full_lo || t >= full_hi) {
             #pragma unroll
             for (int b = 0; b < NKB; ++b)
@@ -561,6 +571,9 @@ void fa_fwd_bf16_kernel(FaParams p)
         __builtin_amdgcn_s_setprio(3);
         load_tile(t + PF, ld);
         if (wave_active(t)) qk(t, sa);
+        // the mask bytes of the next tile, which its Q K^T products start from a step later
+        if constexpr (MASKED)
+            if (t + 1 < T1) load_mask(t + 1);
         if (t - 1 >= T0 && wave_active(t - 1)) pv(t - 1, pp);
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
@@ -570,9 +583,6 @@ void fa_fwd_bf16_kernel(FaParams p)
         if constexpr (PF == 3) store_tile(t + 2, sto);
         if (wave_active(t)) softmax(t, sa, pp);
         if constexpr (PF != 3) store_tile(t + 2, sto);
-        // the mask words of the next tile, used by the next softmax (a step from now)
-        if constexpr (MASKED)
-            if (t + 1 < T1) load_mask(t + 1);
         __syncthreads();
     };
 
