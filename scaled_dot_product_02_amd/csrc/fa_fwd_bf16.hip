@@ -690,10 +690,18 @@ void fa_fwd_bf16_kernel(FaParams p)
                 if (__any(m_ref_n != m_ref)) {
                     const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_ref_n);
                     l_run *= alpha;
+                    // the output accumulators live in the matrix core's registers (AGPRs);
+                    // the pins keep their copies to vector registers and back inside this
+                    // rare branch (unpinned, the compiler hoisted the copies out of it, into
+                    // every step)
+                    #pragma unroll
+                    for (int r = 0; r < C::RT; ++r) asm volatile("" : "+a"(o[r]));
                     #pragma unroll
                     for (int r = 0; r < C::RT; ++r)
                         #pragma unroll
                         for (int i = 0; i < 16; ++i) o[r][i] *= alpha;
+                    #pragma unroll
+                    for (int r = 0; r < C::RT; ++r) asm volatile("" : "+a"(o[r]));
                 }
                 m_ref = m_ref_n;
                 m_true = m_true_n;
