@@ -1,7 +1,7 @@
 // Attention forward, bf16 / fp16 inputs, masks whose visible keys start at key 0 (causal
 // either way round, with or without a per-sequence prefix, no mask, or a band with no lower
-// bound): the persistent form of the tiled MFMA kernel, for packed (TND) and dense forwards
-// with GQA.
+// bound), with or without dropout: the persistent form of the tiled MFMA kernel, for packed
+// (TND) and dense forwards with GQA.
 //
 // What it computes is what the tiled kernel computes (out = softmax(scale * Q K^T) V per
 // sequence and query head with the per-row softmax max and sum; Paddle "sparse_attention"
@@ -88,15 +88,27 @@ struct PRec {
 };
 static_assert(sizeof(PRec) == 64, "one LDS record per item");
 
+// With dropout the record also carries the item's first row (sequence-local) and the third
+// Philox counter word of its first head, h0 + 256 b: 80 bytes.
+template <bool DROP> struct PRecT : PRec {};
+template <> struct PRecT<true> : PRec {
+    int32_t r0;
+    uint32_t hb0;
+    int32_t pad[2];
+};
+static_assert(sizeof(PRecT<true>) == 80, "dropout record");
+
 // LDS of a workgroup beside the K / V ring: the item records (the packed batch's
 // sequence tables, needed only while the records are built, share the ring's space).
-template <int D>
+template <int D, bool DROP>
 constexpr int persist_max_items()
 {
-    return (160 * 1024 - PNBUF * (PCfg<D>::KBUF + PCfg<D>::VBUF) * 2 - 64) / (int)sizeof(PRec);
+    return (160 * 1024 - PNBUF * (PCfg<D>::KBUF + PCfg<D>::VBUF) * 2 - 64) / (int)sizeof(PRecT<DROP>);
 }
 
-template <int D, typename T, int HPI, bool VARLEN>
+// DROP: dropout on the probabilities (the tiled kernel's Philox4x32-10 counters and byte
+// test, so both kernels drop the same entries), the kept ones scaled in the epilogue.
+template <int D, typename T, int HPI, bool VARLEN, bool DROP>
 __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
 {
     using C = PCfg<D>;
@@ -112,9 +124,9 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     typedef __attribute__((address_space(1))) float GF;
     constexpr int R = 256 / HPI;     // query rows per item
     constexpr int WPH = 8 / HPI;     // waves per head
-    constexpr int MAXI = persist_max_items<D>();
+    constexpr int MAXI = persist_max_items<D, DROP>();
     __shared__ __attribute__((aligned(16))) __bf16 ring[PNBUF * (C::KBUF + C::VBUF)];
-    __shared__ PRec s_rec[MAXI];
+    __shared__ PRecT<DROP> s_rec[MAXI];
     __shared__ int s_nitems, s_nsteps;
     __bf16* Ks = ring;
     __bf16* Vs = ring + PNBUF * C::KBUF;
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                 if (live && pos < MAXI) {
                     const int h0 = it.g * HPI;
                     const int kvh = h0 / p.group;
-                    PRec& rc = s_rec[pos];
+                    PRecT<DROP>& rc = s_rec[pos];
                     rc.kaddr = (int64_t)p.k + ((int64_t)it.b * p.k_sb + it.kv0 * p.k_ss + (int64_t)kvh * p.k_sh) * 2;
                     rc.vaddr = (int64_t)p.v + ((int64_t)it.b * p.v_sb + it.kv0 * p.v_ss + (int64_t)kvh * p.v_sh) * 2;
                     rc.qaddr = (int64_t)p.q + ((int64_t)it.b * p.q_sb + (it.q0 + it.r0) * p.q_ss + (int64_t)h0 * p.q_sh) * 2;
@@ -283,6 +295,10 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                     rc.T0 = it.T0;
                     rc.T1 = it.T1;
                     rc.pfx = it.pfx;
+                    if constexpr (DROP) {
+                        rc.r0 = it.r0;
+                        rc.hb0 = (uint32_t)h0 + 256u * (uint32_t)it.b;
+                    }
                 }
                 int st = live && pos < MAXI ? it.T1 - it.T0 : 0;
                 #pragma unroll
@@ -415,6 +431,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     int w_hi = 0;        // tiles [0, w_hi) hold a visible key of this wave's rows
     int full_hi = 0;     // tiles [0, full_hi) are visible in full from every row of the wave
     int jhi = -1;        // keys [0, jhi] are visible from this lane's row
+    uint32_t d_row = 0, d_hb = 0;   // dropout counter words of this lane's row and head
 
     // bounds of item k for this wave (causal: item row i sees keys 0 .. max(diag + i, pfx - 1))
     auto item_bounds = [&](int k) {
@@ -424,6 +441,10 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         const int pfx = rec32(s_rec[k].pfx);
         c_T0 = rec32(s_rec[k].T0);
         c_T1 = rec32(s_rec[k].T1);
+        if constexpr (DROP) {
+            d_row = (uint32_t)(rec32(s_rec[k].r0) + wrow + lq);
+            d_hb = (uint32_t)rec32((int32_t)s_rec[k].hb0) + (uint32_t)hgi;
+        }
         const int re = min(wrow + 32, rows);   // this wave's item rows [wrow, re)
         w_hi = full_hi = 0;
         jhi = -1;
@@ -558,10 +579,47 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
                     rq[i & 3] += e;
             }
         l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
-        #pragma unroll
-        for (int j = 0; j < 2 * PNKB; ++j)
+        if constexpr (DROP) {
+            // slot e of MFMA j holds key 16j + 8(e/4) + 4hf + e%4 of the tile, the 16 keys of
+            // Philox block 4t + j; slot e takes byte e%4 of word 2(e/4) + hf.  Lanes l and
+            // l + 32 hold the same query row: each computes the blocks j = hf + 2k and hands
+            // the partner the two words it needs
+            uint32_t W[2][4];
             #pragma unroll
-            for (int e = 0; e < 8; ++e) pp[j][e] = (T)s[j >> 1][8 * (j & 1) + e];
+            for (int k = 0; k < 2; ++k) {
+                W[k][0] = (uint32_t)(t * (PBN / 16) + hf + 2 * k);
+                W[k][1] = d_row;
+                W[k][2] = d_hb;
+                W[k][3] = p.drop_offset;
+                philox4x32_10(W[k], p.seed_lo, p.seed_hi);
+            }
+            uint32_t got[4];   // the partner's words hf and 2 + hf of its blocks
+            #pragma unroll
+            for (int k = 0; k < 2; ++k)
+                #pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t x = hf ? W[k][2 * w] : W[k][2 * w + 1];
+                    auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                    got[2 * k + w] = hf ? r[0] : r[1];
+                }
+            #pragma unroll
+            for (int j = 0; j < 2 * PNKB; ++j) {
+                const int k = j >> 1;
+                const bool own = (j & 1) == hf;
+                const uint32_t wa = own ? (hf ? W[k][1] : W[k][0]) : got[2 * k];
+                const uint32_t wb = own ? (hf ? W[k][3] : W[k][2]) : got[2 * k + 1];
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t byte = ((e < 4 ? wa : wb) >> (8 * (e & 3))) & 0xffu;
+                    pp[j][e] = byte >= p.drop_thr ? (T)s[j >> 1][8 * (j & 1) + e] : (T)0.f;
+                }
+            }
+        } else {
+            #pragma unroll
+            for (int j = 0; j < 2 * PNKB; ++j)
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) pp[j][e] = (T)s[j >> 1][8 * (j & 1) + e];
+        }
     };
 
     // ---- epilogue of item k: O / l rounded to the storage type, the statistics in
@@ -572,7 +630,7 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
         const float lt = pair_sum(l_run);
         const int qi = wrow + lq;
         const bool any = lt > 0.f;
-        const float wc = any ? 1.f / lt : 0.f;
+        const float wc = any ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;
         // Lane (lq, hf) holds dims 8 g + 4 hf .. + 3 of its row in group g of each 32-dim
         // block.  One exchange with the lane 32 apart (lanes 32-63 of the first operand
         // trade with lanes 0-31 of the second) per pair of groups leaves lane (lq, 0) with
@@ -694,14 +752,20 @@ __global__ __launch_bounds__(PT, 1) void fa_fwd_persist_kernel(FaParams p)
     epilogue(n_items - 1);
 }
 
+template <int D, typename T, int HPI, bool DROP>
+hipError_t launch_hpi_d(const FaParams& p, hipStream_t stream)
+{
+    if (p.cu_q)
+        hipLaunchKernelGGL((fa_fwd_persist_kernel<D, T, HPI, true, DROP>), dim3(p.n_slots), dim3(PT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_persist_kernel<D, T, HPI, false, DROP>), dim3(p.n_slots), dim3(PT), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int D, typename T, int HPI>
 hipError_t launch_hpi(const FaParams& p, hipStream_t stream)
 {
-    if (p.cu_q)
-        hipLaunchKernelGGL((fa_fwd_persist_kernel<D, T, HPI, true>), dim3(p.n_slots), dim3(PT), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fa_fwd_persist_kernel<D, T, HPI, false>), dim3(p.n_slots), dim3(PT), 0, stream, p);
-    return hipGetLastError();
+    return p.drop_thr ? launch_hpi_d<D, T, HPI, true>(p, stream) : launch_hpi_d<D, T, HPI, false>(p, stream);
 }
 
 template <int D, typename T>
@@ -725,9 +789,10 @@ int fa_persist_heads_per_item(int group)
     return h;
 }
 
-int fa_persist_max_items(int D)
+int fa_persist_max_items(int D, bool drop)
 {
-    return D == 64 ? persist_max_items<64>() : persist_max_items<128>();
+    if (drop) return D == 64 ? persist_max_items<64, true>() : persist_max_items<128, true>();
+    return D == 64 ? persist_max_items<64, false>() : persist_max_items<128, false>();
 }
 
 hipError_t launch_fa_fwd_persist(const FaParams& p, int D, bool f16, hipStream_t stream)

@@ -103,9 +103,9 @@ constexpr int kSparseRowBlock = 64;
 // Longest packed batch (sequences) of the persistent kernel, whose workgroups sort the
 // sequence lengths in LDS.
 constexpr int kPersistMaxSeq = 512;
-// the most work items one workgroup of the persistent kernel may own at head dim D (its
-// item records live in LDS)
-int fa_persist_max_items(int D);
+// the most work items one workgroup of the persistent kernel may own at head dim D, with
+// or without dropout (its item records live in LDS; dropout makes them larger)
+int fa_persist_max_items(int D, bool drop);
 
 // Row tile heights, used by the C-ABI layer to size the grids.
 constexpr int kBf16TileM = 256;

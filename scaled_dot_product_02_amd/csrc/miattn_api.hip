@@ -157,13 +157,13 @@ bool persist_enabled()
 }
 
 // Whether a forward that the tiled kernel would serve runs on the persistent one: causal
-// (either alignment, with or without a prefix) without a mask tensor, dropout or prior,
+// (either alignment, with or without a prefix or dropout) without a mask tensor or prior,
 // head dim 64 or 128 with V of the same head dim, packed batches of at most
 // kPersistMaxSeq sequences.
 bool use_persistent(const FaParams& p, int64_t D, int64_t Tq, int n_wg)
 {
     if (D != 64 && D != 128) return false;
-    if (p.Dv != D || p.prev_out || p.amask || p.drop_thr) return false;
+    if (p.Dv != D || p.prev_out || p.amask) return false;
     // every row's visible keys start at key 0 (no mask, causal with or without a prefix,
     // or a band with no lower bound): the kernel moves the causal diagonal by the band's
     // upper bound and extends each row's keys to the prefix
@@ -175,7 +175,7 @@ bool use_persistent(const FaParams& p, int64_t D, int64_t Tq, int n_wg)
     const int64_t rows = 256 / hpi;
     const int64_t tiles = p.cu_q ? (Tq + rows - 1) / rows + p.B : p.B * ((p.Sq + rows - 1) / rows);
     const int64_t items = tiles * (p.Nq / hpi);
-    if (n_wg < 1 || items >= (int64_t(1) << 30) || (items + n_wg - 1) / n_wg > fa_persist_max_items((int)D))
+    if (n_wg < 1 || items >= (int64_t(1) << 30) || (items + n_wg - 1) / n_wg > fa_persist_max_items((int)D, p.drop_thr != 0))
         return false;
     return persist_enabled();
 }

@@ -135,8 +135,8 @@ def test_attn_fwd_validation(mi):
 
 def test_attn_fwd_route_persistent(mi, monkeypatch):
     """bf16 / fp16 forwards at head dim 64 or 128 whose visible keys start at key 0 (causal,
-    no mask, a band without a lower bound; with or without a prefix), without a mask tensor,
-    dropout or prior,
+    no mask, a band without a lower bound; with or without a prefix or dropout), without a
+    mask tensor or prior,
     run on the persistent kernel while every workgroup's items fit its LDS list;
     MIATTN_PERSIST=0 sends them to the tiled kernel."""
     r = mi.attn_fwd_route
@@ -150,7 +150,7 @@ def test_attn_fwd_route_persistent(mi, monkeypatch):
     # a band with a lower bound (pre = next = 0 here) keeps the tiled kernel
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "band") == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 64, "bf16", "BNSD", "causal") == "tiled"
-    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", dropout_p=0.1) == "tiled"
+    assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", dropout_p=0.1) == "persistent"
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal", update=True) == "tiled"
     assert r(2, 32, 8, 4096, 4096, 128, 128, "f32", "BNSD", "causal") == "general"
     # at most 191 items per workgroup at head dim 128 (256 workgroups): 256 heads of one
