@@ -157,6 +157,11 @@ def test_attn_fwd_route_persistent(mi, monkeypatch):
     # kv head each (256-row items) x 191 query tiles fit, 192 do not
     assert r(1, 256, 256, 191 * 256, 191 * 256, 128, 128, "bf16", "BNSD", "causal") == "persistent"
     assert r(1, 256, 256, 192 * 256, 192 * 256, 128, 128, "bf16", "BNSD", "causal") == "tiled"
+    # with dropout the item records are 80 bytes: 152 items fit, 153 do not
+    assert r(1, 256, 256, 152 * 256, 152 * 256, 128, 128, "bf16", "BNSD", "causal",
+             dropout_p=0.1) == "persistent"
+    assert r(1, 256, 256, 153 * 256, 153 * 256, 128, 128, "bf16", "BNSD", "causal",
+             dropout_p=0.1) == "tiled"
     monkeypatch.setenv("MIATTN_PERSIST", "0")
     assert r(2, 32, 8, 4096, 4096, 128, 128, "bf16", "BNSD", "causal") == "tiled"
 
