@@ -124,7 +124,11 @@ __global__ __launch_bounds__(NT, 1) void fa_fwd_wide_kernel(FaParams p, int D, i
     // 16-bit types stage each wave's V slice in LDS ([key][dv], row stride VSS) from 16-byte
     // loads and read it back transposed; fp32 reads V^T fragments from global memory
     constexpr bool TR = sizeof(T) == 2;
-    constexpr int VSS = DVS + 8;
+    // row pitch of the slice: a ds_read_b64_tr_b16 gathers four key rows and two 16-dim
+    // halves for 32 lanes, which fall in disjoint bank ranges when the pitch is 32 or 96
+    // modulo 128 elements; slices of 32 or 96 dims meet that unpadded, 64-dim ones (two
+    // buffers, no room for a 96 pitch) keep a pitch of 72
+    constexpr int VSS = (DVS % 128 == 32 || DVS % 128 == 96) ? DVS : DVS + 8;
     constexpr int VCH = DVS / 8;                 // 16-byte chunks per key of a wave's slice
     constexpr int VU = TR ? BN * VCH / 64 : 1;   // chunks per lane per tile (= 2 VB)
     // V buffers: two (the next tile's slice loaded and stored during this one) for VB = 2;
