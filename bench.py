@@ -305,7 +305,7 @@ def main():
     if not args.no_secondary:
         sec = {}
         # the two small dense workloads (fp32 [1, 1, 128, 64] on the fp32 matrix-core path,
-        # bf16 [8, 8, 128, 64] on the tiled kernel): far too small to fill the chip, so the
+        # bf16 [8, 8, 128, 64] on the persistent kernel): far too small to fill the chip, so the
         # time per launch is launch latency; also timed as a captured graph of 100 launches
         for wname, dt_, peak in (("dense_f32_b1n1s128d64", "f32", PEAK_F32_TFLOPS),
                                  ("dense_bf16_b8n8s128d64", "bf16", PEAK_BF16_TFLOPS)):
